@@ -1,0 +1,217 @@
+"""Thin ctypes binding of libbase_layer.so (include/base_layer.h).
+
+Argument marshalling only: torch tensors give device memory and streams,
+every step of the computation runs in the library's HIP kernels. The library
+is loaded on first use; if it is missing, calls raise (there is no fallback).
+Functions carry the C names; outputs not passed in are allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbase_layer.so")
+
+BASE_OK, BASE_ERR_INVALID_ARG, BASE_ERR_INDIVISIBLE = 0, -1, -2
+BASE_ERR_UNSUPPORTED, BASE_ERR_HIP, BASE_ERR_NOT_CONVERGED = -3, -4, -5
+BASE_ERR_NONFINITE, BASE_ERR_UNBALANCED = -6, -8
+BASE_F32, BASE_BF16 = 0, 1
+BASE_ACT_RELU, BASE_ACT_GELU = 0, 1
+BASE_ROUTE_BALANCED, BASE_ROUTE_GREEDY, BASE_ROUTE_GIVEN = 0, 1, 2
+BASE_OP_AFFINITY, BASE_OP_AUCTION, BASE_OP_GREEDY, BASE_OP_LAYER = 0, 1, 2, 3
+EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
+            "base_assign_auction", "base_route_greedy", "base_layer_forward",
+            "base_set_phase_events")
+STATS_BYTES = 8 + 16 * 8 * 2
+
+
+class AuctionCfg(ctypes.Structure):
+    _fields_ = [("eps_start", ctypes.c_double), ("eps_end", ctypes.c_double),
+                ("eps_factor", ctypes.c_double), ("max_bids", ctypes.c_int64)]
+
+
+class BaseError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m balanced_token_expert_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.base_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+    lib.base_workspace_bytes.restype = ctypes.c_size_t
+    lib.base_strerror.argtypes = [i32]
+    lib.base_strerror.restype = ctypes.c_char_p
+    lib.base_affinity.argtypes = [P, P, P, i64, i64, i64, i32, P]
+    lib.base_assign_auction.argtypes = [P, i64, i64, AuctionCfg, P, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+    lib.base_route_greedy.argtypes = [P, i64, i64, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.base_layer_forward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, i32,
+                                       AuctionCfg, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.base_set_phase_events.argtypes = [P, i32]
+    for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
+              "base_set_phase_events"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().base_strerror(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BASE_BF16
+    if t.dtype == torch.float32:
+        return BASE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(rc: int, where: str):
+    if rc != BASE_OK:
+        raise BaseError(rc, where)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def base_workspace_bytes(op: int, T: int, E: int, D: int = 0, F: int = 0,
+                         dtype: int = BASE_BF16) -> int:
+    return int(load().base_workspace_bytes(op, T, E, D, F, dtype))
+
+
+def workspace(op, T, E, D=0, F=0, dtype=BASE_BF16, device="cuda"):
+    n = base_workspace_bytes(op, T, E, D, F, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class AuctionStats:
+    status: int
+    phases: int
+    bids: list
+    rounds: list
+
+
+def read_stats(buf: torch.Tensor) -> AuctionStats:
+    raw = buf.cpu()
+    head = raw[:8].view(torch.int32).tolist()
+    tail = raw[8:STATS_BYTES].view(torch.int64).tolist()
+    ph = head[1]
+    n = min(ph, 16)
+    return AuctionStats(head[0], ph, tail[:16][:n], tail[16:32][:n])
+
+
+def new_stats(device="cuda") -> torch.Tensor:
+    return torch.zeros(STATS_BYTES, dtype=torch.uint8, device=device)
+
+
+def cfg(eps_start=1.0, eps_end=1e-4, eps_factor=10.0, max_bids=0) -> AuctionCfg:
+    return AuctionCfg(float(eps_start), float(eps_end), float(eps_factor), int(max_bids))
+
+
+def base_affinity(h: torch.Tensor, w: torch.Tensor, scores=None, stream=None):
+    _dev(h, w, scores)
+    T, D = h.shape
+    E = w.shape[0]
+    if scores is None:
+        scores = torch.empty((T, E), dtype=torch.float32, device=h.device)
+    rc = load().base_affinity(_ptr(h), _ptr(w), _ptr(scores), T, E, D, _dt(h), _stream(stream))
+    _check(rc, "base_affinity")
+    return scores
+
+
+def base_assign_auction(scores: torch.Tensor, c: AuctionCfg, assign=None, perm=None,
+                        offsets=None, prices=None, stats=None, ws=None, stream=None):
+    _dev(scores)
+    T, E = scores.shape
+    dev = scores.device
+    assign = torch.empty(T, dtype=torch.int32, device=dev) if assign is None else assign
+    perm = torch.empty(T, dtype=torch.int32, device=dev) if perm is None else perm
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    prices = torch.empty(E, dtype=torch.float64, device=dev) if prices is None else prices
+    stats = new_stats(dev) if stats is None else stats
+    ws = workspace(BASE_OP_AUCTION, T, E, device=dev) if ws is None else ws
+    rc = load().base_assign_auction(_ptr(scores), T, E, c, _ptr(assign), _ptr(perm),
+                                    _ptr(offsets), _ptr(prices), _ptr(stats), _ptr(ws),
+                                    ws.numel(), _stream(stream))
+    _check(rc, "base_assign_auction")
+    return {"assign": assign, "perm": perm, "offsets": offsets, "prices": prices,
+            "stats": stats}
+
+
+def base_route_greedy(scores: torch.Tensor, assign=None, counts=None, perm=None,
+                      offsets=None, ws=None, stream=None, with_perm=True):
+    _dev(scores)
+    T, E = scores.shape
+    dev = scores.device
+    assign = torch.empty(T, dtype=torch.int32, device=dev) if assign is None else assign
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    if with_perm:
+        perm = torch.empty(T, dtype=torch.int32, device=dev) if perm is None else perm
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    ws = workspace(BASE_OP_GREEDY, T, E, device=dev) if ws is None else ws
+    rc = load().base_route_greedy(_ptr(scores), T, E, _ptr(assign), _ptr(counts), _ptr(perm),
+                                  _ptr(offsets), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "base_route_greedy")
+    return {"assign": assign, "counts": counts, "perm": perm, "offsets": offsets}
+
+
+def base_layer_forward(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = None, assign=None,
+                       scores=None, perm=None, out=None, stats=None, ws=None, stream=None,
+                       want_scores=True):
+    _dev(h, w, W1, W2, assign, scores, perm, out)
+    T, D = h.shape
+    E = w.shape[0]
+    F = W1.shape[1]
+    dev = h.device
+    dt = _dt(h)
+    c = cfg() if c is None else c
+    if assign is None:
+        if mode == BASE_ROUTE_GIVEN:
+            raise ValueError("GIVEN routing needs an assignment")
+        assign = torch.empty(T, dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((T, E), dtype=torch.float32, device=dev)
+    perm = torch.empty(T, dtype=torch.int32, device=dev) if perm is None else perm
+    out = torch.empty_like(h) if out is None else out
+    stats = new_stats(dev) if stats is None else stats
+    ws = workspace(BASE_OP_LAYER, T, E, D, F, dt, device=dev) if ws is None else ws
+    rc = load().base_layer_forward(_ptr(h), _ptr(w), _ptr(W1), _ptr(W2), T, E, D, F, dt, act,
+                                   mode, c, _ptr(assign), _ptr(scores), _ptr(perm), _ptr(out),
+                                   _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "base_layer_forward")
+    return {"out": out, "assign": assign, "scores": scores, "perm": perm, "stats": stats}
+
+
+def base_set_phase_events(events, n: int):
+    """events: a ctypes array of hipEvent_t handles (or None to stop)."""
+    _check(load().base_set_phase_events(events, int(n)), "base_set_phase_events")

@@ -1,0 +1,227 @@
+// C ABI of libbase_layer.so: argument checks, workspace layout and the launch
+// sequence of each entry point (see include/base_layer.h for the contract).
+#include "../../include/base_layer.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "internal.h"
+
+using namespace base;
+
+namespace {
+
+constexpr int64_t kMaxT = int64_t(1) << 24;  // int32 token ids and offsets
+constexpr int64_t kMaxE = 1024;              // auction keeps E prices per lane group
+constexpr int kMaxPhases = 64;
+
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout shared by base_workspace_bytes and the entry points.
+struct Layout {
+    size_t scan = 0, stats = 0, prices = 0, scores = 0, perm = 0, offsets = 0, hidden = 0,
+           auction = 0, permws = 0, assign = 0, total = 0;
+};
+
+Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
+    (void)D;
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t& slot, size_t bytes) {
+        slot = off;
+        off += al(bytes);
+    };
+    if (op == BASE_OP_AFFINITY) {
+        L.total = 0;
+        return L;
+    }
+    take(L.scan, sizeof(ScoreScan));
+    take(L.stats, sizeof(AucStatsDev));
+    if (op == BASE_OP_GREEDY) {
+        take(L.perm, (size_t)T * 4);
+        take(L.offsets, (size_t)(E + 1) * 4);
+        take(L.permws, perm_ws_bytes(T, E));
+        L.total = off;
+        return L;
+    }
+    take(L.prices, (size_t)E * 8);
+    take(L.offsets, (size_t)(E + 1) * 4);
+    if (op == BASE_OP_LAYER) {
+        take(L.scores, (size_t)T * E * 4);
+        take(L.perm, (size_t)T * 4);
+        take(L.hidden, (size_t)T * F * (dt == BASE_BF16 ? 2 : 4));
+    }
+    // the auction's own scratch, followed by the grouping's
+    take(L.auction, auction_ws_bytes(T, E) + perm_ws_bytes(T, E));
+    L.permws = L.auction + auction_ws_bytes(T, E);
+    L.total = off;
+    return L;
+}
+
+int cfg_phases(const base_auction_cfg& c) {
+    if (!(c.eps_end > 0) || !(c.eps_start >= c.eps_end) || !isfinite(c.eps_start) ||
+        !(c.eps_factor > 1) || !isfinite(c.eps_factor))
+        return -1;
+    int n = 1;
+    double eps = c.eps_start;
+    while (eps > c.eps_end) {
+        eps /= c.eps_factor;
+        if (eps < c.eps_end) eps = c.eps_end;
+        if (++n > kMaxPhases) return -1;
+    }
+    return n;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+thread_local hipEvent_t g_events[6];
+thread_local int g_nevents = 0;
+
+void mark(int i, hipStream_t st) {
+    if (i < g_nevents && g_events[i]) hipEventRecord(g_events[i], st);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? BASE_OK : BASE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* base_strerror(int code) {
+    switch (code) {
+        case BASE_OK: return "ok";
+        case BASE_ERR_INVALID_ARG: return "invalid argument";
+        case BASE_ERR_INDIVISIBLE: return "T is not a multiple of E";
+        case BASE_ERR_UNSUPPORTED: return "unsupported by this build";
+        case BASE_ERR_HIP: return "HIP launch failed";
+        case BASE_ERR_NOT_CONVERGED: return "auction stopped at its bid cap";
+        case BASE_ERR_NONFINITE: return "no finite affinity";
+        case BASE_ERR_UNBALANCED: return "given assignment is not balanced";
+        default: return "unknown error";
+    }
+}
+
+int base_set_phase_events(void** events, int n) {
+    if (n < 0 || n > 6) return BASE_ERR_INVALID_ARG;
+    if (!events) n = 0;
+    for (int i = 0; i < 6; ++i) g_events[i] = (events && i < n) ? (hipEvent_t)events[i] : nullptr;
+    g_nevents = n;
+    return BASE_OK;
+}
+
+size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dtype) {
+    if (T <= 0 || E <= 0 || op < 0 || op > BASE_OP_LAYER) return 0;
+    if (op == BASE_OP_LAYER && F <= 0) return 0;
+    return layout(op, T, E, D, F, dtype).total;
+}
+
+int base_affinity(const void* h, const void* w, float* scores, int64_t T, int64_t E, int64_t D,
+                  int dt, base_stream_t stream) {
+    if (!h || !w || !scores || T <= 0 || E <= 0 || D <= 0) return BASE_ERR_INVALID_ARG;
+    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
+    if (T > kMaxT) return BASE_ERR_UNSUPPORTED;
+    if (dt == BASE_BF16 && (D % 8 != 0 || misaligned(h) || misaligned(w)))
+        return BASE_ERR_UNSUPPORTED;
+    return hip_rc(launch_affinity(h, w, scores, T, E, D, dt, nullptr, (hipStream_t)stream));
+}
+
+int base_assign_auction(const float* scores, int64_t T, int64_t E, base_auction_cfg cfg,
+                        int32_t* assign, int32_t* perm, int32_t* offsets, double* prices,
+                        base_auction_stats* stats, void* ws, size_t ws_bytes,
+                        base_stream_t stream) {
+    if (!scores || !assign || !perm || !offsets || !prices) return BASE_ERR_INVALID_ARG;
+    if (T <= 0 || E <= 0 || E > T) return BASE_ERR_INVALID_ARG;
+    if (T % E) return BASE_ERR_INDIVISIBLE;
+    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
+    if (cfg_phases(cfg) < 0) return BASE_ERR_INVALID_ARG;
+    const Layout L = layout(BASE_OP_AUCTION, T, E, 0, 0, 0);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    ScoreScan* scan = (ScoreScan*)(W + L.scan);
+    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
+    hipError_t e = launch_scan_init(scan, st);
+    if (e == hipSuccess) e = launch_scan_scores(scores, T * E, scan, st);
+    if (e == hipSuccess)
+        e = launch_auction(scores, T, E, cfg.eps_start, cfg.eps_end, cfg.eps_factor, cfg.max_bids,
+                           scan, assign, perm, offsets, prices, sd, W + L.auction, st);
+    return hip_rc(e);
+}
+
+int base_route_greedy(const float* scores, int64_t T, int64_t E, int32_t* assign, int32_t* counts,
+                      int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                      base_stream_t stream) {
+    if (!scores || !assign || T <= 0 || E <= 0) return BASE_ERR_INVALID_ARG;
+    if ((perm == nullptr) != (offsets == nullptr)) return BASE_ERR_INVALID_ARG;
+    if (T > kMaxT || E > kMaxT) return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(BASE_OP_GREEDY, T, E, 0, 0, 0);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    ScoreScan* scan = (ScoreScan*)(W + L.scan);
+    hipError_t e = launch_scan_init(scan, st);
+    if (e == hipSuccess) e = launch_scan_scores(scores, T * E, scan, st);
+    if (e == hipSuccess) e = launch_greedy(scores, T, E, scan, assign, counts, st);
+    if (e == hipSuccess && (counts || perm)) {
+        int32_t* p = perm ? perm : (int32_t*)(W + L.perm);
+        int32_t* o = offsets ? offsets : (int32_t*)(W + L.offsets);
+        e = launch_perm(assign, T, E, p, o, counts, 0, nullptr, W + L.permws, st);
+    }
+    return hip_rc(e);
+}
+
+int base_layer_forward(const void* h, const void* w, const void* W1, const void* W2, int64_t T,
+                       int64_t E, int64_t D, int64_t F, int dt, int act, int mode,
+                       base_auction_cfg cfg, int32_t* assign, float* scores, int32_t* perm,
+                       void* out, base_auction_stats* stats, void* ws, size_t ws_bytes,
+                       base_stream_t stream) {
+    if (!h || !w || !W1 || !W2 || !assign || !out) return BASE_ERR_INVALID_ARG;
+    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
+    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
+    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
+    if (mode != BASE_ROUTE_BALANCED && mode != BASE_ROUTE_GREEDY && mode != BASE_ROUTE_GIVEN)
+        return BASE_ERR_INVALID_ARG;
+    if (mode == BASE_ROUTE_BALANCED && cfg_phases(cfg) < 0) return BASE_ERR_INVALID_ARG;
+    if (T % E) return BASE_ERR_INDIVISIBLE;
+    if (mode == BASE_ROUTE_GREEDY) return BASE_ERR_UNSUPPORTED;
+    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
+    if (dt == BASE_BF16 && (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) ||
+                            misaligned(W1) || misaligned(W2) || misaligned(out)))
+        return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(BASE_OP_LAYER, T, E, D, F, dt);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    const int64_t k = T / E;
+    ScoreScan* scan = (ScoreScan*)(W + L.scan);
+    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
+    float* s = scores ? scores : (float*)(W + L.scores);
+    int32_t* pm = perm ? perm : (int32_t*)(W + L.perm);
+    int32_t* offs = (int32_t*)(W + L.offsets);
+    double* prices = (double*)(W + L.prices);
+    void* H = W + L.hidden;
+
+    mark(0, st);
+    hipError_t e = launch_scan_init(scan, st);
+    if (e == hipSuccess) e = launch_affinity(h, w, s, T, E, D, dt, scan, st);
+    mark(1, st);
+    if (e == hipSuccess) {
+        if (mode == BASE_ROUTE_BALANCED) {
+            e = launch_auction(s, T, E, cfg.eps_start, cfg.eps_end, cfg.eps_factor, cfg.max_bids,
+                               scan, assign, pm, offs, prices, sd, W + L.auction, st);
+        } else {
+            e = launch_stats_reset(sd, st);
+            if (e == hipSuccess)
+                e = launch_perm(assign, T, E, pm, offs, nullptr, k, &sd->status, W + L.permws, st);
+        }
+    }
+    mark(2, st);
+    if (e == hipSuccess) e = launch_ffn1(h, pm, W1, H, E, k, D, F, dt, act, st);
+    mark(3, st);
+    if (e == hipSuccess) e = launch_ffn2(H, pm, W2, s, h, out, E, k, D, F, dt, st);
+    mark(4, st);
+    mark(5, st);
+    return hip_rc(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,587 @@
+// Balanced assignment of "BASE Layers" eq. 2 (sec. 3.2.1) by a token-side
+// auction with eps-scaling, on gfx950.
+//
+// Problem: maximise sum_t s[t][a_t] with exactly k = T/E tokens per expert.
+// Each expert owns k slots; a token t facing prices pi_e computes its values
+// v_e = s[t][e] - pi_e, its best expert b1 (lowest id on ties), the best value
+// v1 and the best value over the other experts v2, and bids
+// beta = pi_b1 + (v1 - v2) + eps for a slot of b1. pi_e is the expert's floor
+// p_e while it has a free slot, else the lowest bid it holds; a bid into a
+// full expert evicts that lowest holder (equal bids: the higher token id
+// goes), who must bid again. When no token is left unassigned every expert is
+// full and p_e := its lowest held bid. Phases run with eps_start,
+// eps_start/f, ..., eps_end, keeping prices and clearing the assignment.
+// Every held token satisfies s[t][e] - p_e >= max_e' (s[t][e'] - p_e') - eps,
+// so the result is within T*eps_end of the optimum (and is the optimum when
+// eps_end is below the optimality gap over T). The paper's own listing
+// (appendix fig. 9) has experts bidding for tokens; this is the same
+// primal-dual idea from the token side, which needs only per-token
+// max/second-max reductions and per-expert prices.
+//
+// GPU structure per phase:
+//   bulk rounds (all CUs): every unassigned token bids against the round's
+//     prices at once (one wave per token, wave-level max/second-max); then one
+//     workgroup per expert keeps the k best of its holders and new bidders
+//     (bitonic sort in LDS) and returns the rest to the bidder list.
+//   tail (one persistent workgroup, 16 waves): once few tokens are left, each
+//     wave follows a displacement chain -- bid, take the expert's lock in LDS,
+//     evict its lowest holder, continue with the evicted token -- with prices,
+//     counts and the current lowest holder of every expert in LDS, and the
+//     evicted token's score row fetched together with the rescan of the
+//     expert's slots.
+// Prices and bids are fp64: exactness needs eps below gap/T, far below fp32
+// resolution at prices of order one.
+#include <float.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace base {
+
+constexpr int kBulkRounds = 6;       // multi-CU rounds per phase (at most)
+constexpr int kTailMax = 1024;       // bidders left when the tail takes over
+constexpr int kResolveCap = 4096;    // candidates sorted at once per expert
+constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
+constexpr int kTailThreads = 1024;
+constexpr int32_t kErrNotConverged = -5;
+constexpr int32_t kErrNonfinite = -6;
+
+struct AucCtl {
+    int32_t cur;          // bidder list in use (0/1)
+    int32_t bulk_done;    // the tail owns the rest of this phase
+    int32_t identity;     // the bidder list is 0..T-1 (round 0)
+    int32_t done_blocks;  // resolve blocks finished (last one flips cur)
+    int32_t nbid[2];
+    int32_t abort;        // a device error is set: skip all work
+    int32_t pad;
+    unsigned long long bids_total;
+    unsigned long long bids_phase;
+    long long rounds_phase;
+};
+
+struct AucWs {
+    AucCtl* ctl;
+    double* floor_;    // E   price floors p_e
+    double* pi;        // E   prices for the next bulk round
+    int32_t* cnt;      // E   holders per expert
+    int32_t* minslot;  // E   slot of the lowest holder (when full)
+    int32_t* mintok;   // E
+    int32_t* list0;    // T
+    int32_t* list1;    // T
+    int32_t* bexp;     // T   bid of token t: expert
+    double* bval;      // T   bid of token t: amount
+    int32_t* stok;     // E*k slot tokens
+    double* sbid;      // E*k slot bids
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static AucWs carve(void* ws, int64_t T, int64_t E) {
+    char* p = (char*)ws;
+    AucWs w;
+    w.ctl = (AucCtl*)p; p += align256(sizeof(AucCtl));
+    w.floor_ = (double*)p; p += align256(E * 8);
+    w.pi = (double*)p; p += align256(E * 8);
+    w.cnt = (int32_t*)p; p += align256(E * 4);
+    w.minslot = (int32_t*)p; p += align256(E * 4);
+    w.mintok = (int32_t*)p; p += align256(E * 4);
+    w.list0 = (int32_t*)p; p += align256(T * 4);
+    w.list1 = (int32_t*)p; p += align256(T * 4);
+    w.bexp = (int32_t*)p; p += align256(T * 4);
+    w.bval = (double*)p; p += align256(T * 8);
+    w.stok = (int32_t*)p; p += align256(T * 4);
+    w.sbid = (double*)p; p += align256(T * 8);
+    return w;
+}
+
+size_t auction_ws_bytes(int64_t T, int64_t E) {
+    return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + 3 * align256(E * 4) +
+           4 * align256(T * 4) + 2 * align256(T * 8) + align256(T * 4) + 256;
+}
+
+// ---------------------------------------------------------------- helpers
+
+struct Sani {
+    bool fix;
+    float repl;
+};
+
+BASE_DEV Sani read_sani(const ScoreScan* scan) {
+    Sani s;
+    s.fix = scan->nonfinite != 0;
+    s.repl = scan->min_key == 0xffffffffu ? 0.0f : f32_unkey(scan->min_key);
+    return s;
+}
+
+template <int NCH>
+BASE_DEV void load_row(const float* s, int64_t t, int64_t E, int lane, Sani sn, float (&v)[NCH]) {
+    const float* row = s + t * E;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t e = lane + 64 * c;
+        float x = (e < E) ? row[e] : 0.0f;
+        if (sn.fix && !is_finite_f32(x)) x = sn.repl;
+        v[c] = x;
+    }
+}
+
+// Best expert (lowest id on ties), best value and the best value over the
+// other experts, of s[t][e] - pi[e], reduced over the wave.
+// pb returns the price of b1 exactly as used for v1 (prices in LDS may be
+// raised by other waves meanwhile; the bid must use one consistent value).
+template <int NCH, typename PiT>
+BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& b1, double& v1,
+                       double& v2, double& pb) {
+    double val[NCH], pv[NCH];
+    double best = -DBL_MAX;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        pv[c] = 0.0;
+        if (e < E) {
+            pv[c] = pi[e];
+            val[c] = (double)v[c] - pv[c];
+            if (bi == 0x7fffffff || val[c] > best) { best = val[c]; bi = e; }
+        } else {
+            val[c] = -DBL_MAX;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const double ob = shfl_xor_f64(best, o);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || ob > best || (ob == best && oi < bi))) {
+            best = ob;
+            bi = oi;
+        }
+    }
+    double sec = -DBL_MAX;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        if (e < E && e != bi && val[c] > sec) sec = val[c];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sec = fmax(sec, shfl_xor_f64(sec, o));
+    if (E == 1) sec = best;
+    double mine = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (c == (bi >> 6)) mine = pv[c];
+    pb = shfl_f64(mine, bi & 63);
+    b1 = bi;
+    v1 = best;
+    v2 = sec;
+}
+
+// a is evicted before b: lower bid, or equal bid and higher token id
+BASE_DEV bool evict_first(double ba, int ta, double bb, int tb) {
+    return ba < bb || (ba == bb && ta > tb);
+}
+
+// ---------------------------------------------------------------- phase control
+
+__global__ void auc_init_kernel(AucWs w, int64_t E, const ScoreScan* scan, int64_t n,
+                                AucStatsDev* st, int32_t* assign, int64_t T) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < E) w.floor_[i] = 0.0;
+    if (i < T) assign[i] = 0;
+    if (i == 0) {
+        st->status = (scan->min_key == 0xffffffffu && n > 0) ? kErrNonfinite : 0;
+        st->phases = 0;
+        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; }
+        w.ctl->bids_total = 0;
+        w.ctl->abort = st->status != 0;
+    }
+}
+
+__global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucStatsDev* st) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < E) {
+        w.cnt[i] = 0;
+        w.pi[i] = w.floor_[i];
+    }
+    if (i == 0) {
+        AucCtl* c = w.ctl;
+        c->cur = 0;
+        c->bulk_done = 0;
+        c->identity = 1;
+        c->done_blocks = 0;
+        c->nbid[0] = (int32_t)T;
+        c->nbid[1] = 0;
+        c->abort = st->status != 0;
+        c->bids_phase = 0;
+        c->rounds_phase = 0;
+    }
+}
+
+// ---------------------------------------------------------------- bulk rounds
+
+template <int NCH>
+__global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64_t T, int64_t E,
+                                                           AucWs w, const ScoreScan* scan,
+                                                           int round, double eps) {
+    AucCtl* ctl = w.ctl;
+    if (ctl->abort || ctl->bulk_done) return;
+    const int cur = ctl->cur;
+    const int64_t nb = ctl->nbid[cur];
+    if (round > 0 && nb <= kTailMax) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) ctl->bulk_done = 1;
+        return;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) ctl->nbid[cur ^ 1] = 0;
+    const bool ident = ctl->identity;
+    const int32_t* list = cur ? w.list1 : w.list0;
+    const Sani sn = read_sani(scan);
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    int64_t mine = 0;
+    for (int64_t j = wave; j < nb; j += nw) {
+        const int64_t t = ident ? j : list[j];
+        float v[NCH];
+        load_row<NCH>(s, t, E, lane, sn, v);
+        int b1;
+        double v1, v2, pb;
+        best_two<NCH>(v, w.pi, E, lane, b1, v1, v2, pb);
+        if (lane == 0) {
+            w.bexp[t] = b1;
+            w.bval[t] = pb + (v1 - v2) + eps;
+        }
+        ++mine;
+    }
+    if (lane == 0 && mine) atomicAdd(&ctl->bids_phase, (unsigned long long)mine);
+}
+
+// One block per expert: keep the k best of (current holders + this round's
+// bidders for this expert), return the others to the next bidder list.
+__global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
+                                                               AucWs w) {
+    __shared__ double cb[kResolveCap];
+    __shared__ int32_t ct[kResolveCap];
+    __shared__ int32_t ncand;
+    AucCtl* ctl = w.ctl;
+    if (ctl->abort || ctl->bulk_done) return;
+    const int cur = ctl->cur;
+    const int64_t nb = ctl->nbid[cur];
+    const bool ident = ctl->identity;
+    const int32_t* list = cur ? w.list1 : w.list0;
+    int32_t* outl = cur ? w.list0 : w.list1;
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    int32_t* stok = w.stok + (int64_t)e * k;
+    double* sbid = w.sbid + (int64_t)e * k;
+
+    // sort cb/ct[0..n) best first: bid descending, then token ascending
+    auto sort_cands = [&](int n) {
+        int P = 1;
+        while (P < n) P <<= 1;
+        for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = 0x7fffffff; }
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < P / 2; i += blockDim.x) {
+                    const int lo = (i / stride) * stride * 2 + (i % stride);
+                    const int hi = lo + stride;
+                    const bool best_first = ((lo & size) == 0);
+                    const double b0 = cb[lo], b1 = cb[hi];
+                    const int t0 = ct[lo], t1 = ct[hi];
+                    const bool hi_better = b1 > b0 || (b1 == b0 && t1 < t0);
+                    if (hi_better == best_first) {
+                        cb[lo] = b1; cb[hi] = b0;
+                        ct[lo] = t1; ct[hi] = t0;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    };
+    // sort, send entries [k, n) to the next bidder list, keep min(n, k)
+    auto keep_best = [&](int n) {
+        sort_cands(n);
+        for (int i0 = (int)k; i0 < n; i0 += blockDim.x) {
+            const int i = i0 + tid;
+            const bool r = i < n;
+            const unsigned long long m = __ballot(r);
+            int base = 0;
+            if (lane == 0 && m) base = atomicAdd(&ctl->nbid[cur ^ 1], (int)__popcll(m));
+            base = __shfl(base, 0, 64);
+            if (r) {
+                const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+                outl[base + __popcll(m & below)] = ct[i];
+            }
+        }
+        __syncthreads();
+        if (tid == 0) ncand = (int)min<int64_t>(n, k);
+        __syncthreads();
+    };
+
+    const int c0 = w.cnt[e];
+    for (int i = tid; i < c0; i += blockDim.x) { cb[i] = sbid[i]; ct[i] = stok[i]; }
+    if (tid == 0) ncand = c0;
+    __syncthreads();
+    bool changed = false;
+    for (int64_t j0 = 0; j0 < nb; j0 += blockDim.x) {
+        const int64_t j = j0 + tid;
+        if (j < nb) {
+            const int64_t t = ident ? j : list[j];
+            if (w.bexp[t] == e) {
+                const int pos = atomicAdd(&ncand, 1);
+                cb[pos] = w.bval[t];
+                ct[pos] = (int32_t)t;
+            }
+        }
+        __syncthreads();
+        const int n = ncand;
+        changed = changed || n != c0;
+        if (n > kResolveCap - (int)blockDim.x) keep_best(n);
+    }
+    if (changed) {
+        int n = ncand;
+        if (n >= k) {
+            keep_best(n);
+            n = (int)k;
+        }
+        for (int i = tid; i < n; i += blockDim.x) { sbid[i] = cb[i]; stok[i] = ct[i]; }
+        if (tid == 0) {
+            w.cnt[e] = n;
+            if (n == k) {  // sorted: the lowest holder is last
+                w.pi[e] = cb[k - 1];
+                w.minslot[e] = (int)k - 1;
+                w.mintok[e] = ct[k - 1];
+            } else {
+                w.pi[e] = w.floor_[e];
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const int done = atomicAdd(&ctl->done_blocks, 1);
+        if (done == (int)gridDim.x - 1) {
+            ctl->done_blocks = 0;
+            ctl->identity = 0;
+            ctl->cur = cur ^ 1;
+            ctl->rounds_phase += 1;
+            __threadfence();
+        }
+    }
+}
+
+// ---------------------------------------------------------------- tail
+
+template <int NCH>
+__global__ __launch_bounds__(kTailThreads) void auc_tail_kernel(const float* s, int64_t T, int64_t E,
+                                                                int64_t k, AucWs w,
+                                                                const ScoreScan* scan, double eps,
+                                                                int phase, int64_t max_bids,
+                                                                AucStatsDev* st) {
+    extern __shared__ char smem[];
+    double* pi = (double*)smem;                 // E
+    double* flo = pi + E;                       // E
+    int32_t* cnt = (int32_t*)(flo + E);         // E
+    int32_t* minslot = cnt + E;                 // E
+    int32_t* mintok = minslot + E;              // E
+    int32_t* lock = mintok + E;                 // E
+    __shared__ int32_t next;
+    __shared__ int32_t stop;
+    __shared__ unsigned long long nbids;
+
+    AucCtl* ctl = w.ctl;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool aborted = ctl->abort;
+    const int cur = ctl->cur;
+    const int64_t nb = aborted ? 0 : ctl->nbid[cur];
+    const bool ident = ctl->identity;
+    const int32_t* list = cur ? w.list1 : w.list0;
+    for (int64_t e = tid; e < E; e += blockDim.x) {
+        pi[e] = w.pi[e];
+        flo[e] = w.floor_[e];
+        cnt[e] = w.cnt[e];
+        minslot[e] = w.minslot[e];
+        mintok[e] = w.mintok[e];
+        lock[e] = 0;
+    }
+    if (tid == 0) {
+        next = 0;
+        const unsigned long long before = ctl->bids_total + ctl->bids_phase;
+        stop = (max_bids > 0 && before >= (unsigned long long)max_bids && nb > 0) ? 1 : 0;
+        nbids = 0;
+    }
+    __syncthreads();
+    const Sani sn = read_sani(scan);
+    const unsigned long long cap =
+        max_bids > 0 ? (unsigned long long)max_bids - min<unsigned long long>(
+                           (unsigned long long)max_bids, ctl->bids_total + ctl->bids_phase)
+                     : ~0ull;
+
+    for (;;) {
+        int j = 0;
+        if (lane == 0) j = atomicAdd(&next, 1);
+        j = __shfl(j, 0, 64);
+        if (j >= nb) break;
+        int64_t t = ident ? j : list[j];
+        float v[NCH];
+        load_row<NCH>(s, t, E, lane, sn, v);
+        while (t >= 0) {
+            if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+            int b1;
+            double v1, v2, pib;
+            for (;;) {
+                best_two<NCH>(v, pi, E, lane, b1, v1, v2, pib);
+                int ok = 0;
+                if (lane == 0) {
+                    int expect = 0;
+                    while (!__hip_atomic_compare_exchange_strong(&lock[b1], &expect, 1, __ATOMIC_ACQUIRE,
+                                                                 __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_WORKGROUP)) {
+                        expect = 0;
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    ok = (pi[b1] == pib);
+                    if (!ok)
+                        __hip_atomic_store(&lock[b1], 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                ok = __shfl(ok, 0, 64);
+                if (ok) break;
+            }
+            // lane 0 holds lock[b1]; commit the bid
+            const double beta = pib + (v1 - v2) + eps;
+            int32_t* stok = w.stok + (int64_t)b1 * k;
+            double* sbid = w.sbid + (int64_t)b1 * k;
+            int c = 0, slot = 0, victim = -1;
+            if (lane == 0) {
+                c = cnt[b1];
+                if (c < k) {
+                    slot = c;
+                    cnt[b1] = c + 1;
+                } else {
+                    slot = minslot[b1];
+                    victim = mintok[b1];
+                }
+                stok[slot] = (int32_t)t;
+                sbid[slot] = beta;
+            }
+            c = __shfl(c, 0, 64);
+            slot = __shfl(slot, 0, 64);
+            victim = __shfl(victim, 0, 64);
+            if (victim >= 0) load_row<NCH>(s, victim, E, lane, sn, v);  // overlaps the rescan
+            if (c + 1 >= k) {
+                // expert full: find its lowest holder (the new bid substituted)
+                double bm = DBL_MAX;
+                int tm = 0x7fffffff, sm = -1;
+                for (int64_t i = lane; i < k; i += 64) {
+                    double b;
+                    int tk;
+                    if (i == slot) { b = beta; tk = (int)t; }
+                    else { b = sbid[i]; tk = stok[i]; }
+                    if (sm < 0 || evict_first(b, tk, bm, tm)) { bm = b; tm = tk; sm = (int)i; }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const double ob = shfl_xor_f64(bm, o);
+                    const int ot = __shfl_xor(tm, o, 64);
+                    const int os = __shfl_xor(sm, o, 64);
+                    if (os >= 0 && (sm < 0 || evict_first(ob, ot, bm, tm))) { bm = ob; tm = ot; sm = os; }
+                }
+                if (lane == 0) {
+                    pi[b1] = bm;
+                    minslot[b1] = sm;
+                    mintok[b1] = tm;
+                }
+            }
+            if (lane == 0) {
+                __threadfence_block();
+                __hip_atomic_store(&lock[b1], 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const unsigned long long nbd = atomicAdd(&nbids, 1ull) + 1;
+                if (nbd >= cap) stop = 1;
+            }
+            t = victim;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned long long pb = ctl->bids_phase + nbids;
+        ctl->bids_total += pb;
+        if (phase < 16) {
+            st->bids[phase] = (long long)pb;
+            st->rounds[phase] = ctl->rounds_phase;
+        }
+        st->phases = phase + 1;
+        if (stop && !aborted) st->status = kErrNotConverged;
+    }
+    // every expert is full: its price floor becomes its lowest held bid
+    for (int64_t e = tid; e < E; e += blockDim.x) {
+        w.floor_[e] = (cnt[e] == k) ? pi[e] : flo[e];
+        w.cnt[e] = cnt[e];
+    }
+}
+
+// ---------------------------------------------------------------- finalize
+
+__global__ void auc_finalize_kernel(AucWs w, int64_t E, int64_t k, int32_t* assign, double* prices) {
+    const int e = blockIdx.x;
+    const int64_t n = min<int64_t>(w.cnt[e], k);
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int32_t t = w.stok[(int64_t)e * k + i];
+        assign[t] = e;
+    }
+    if (threadIdx.x == 0) prices[e] = w.floor_[e];
+}
+
+// ---------------------------------------------------------------- launcher
+
+template <int NCH>
+static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_start,
+                              double eps_end, double eps_factor, int64_t max_bids,
+                              const ScoreScan* scan, int32_t* assign, double* prices,
+                              AucStatsDev* st, AucWs w, hipStream_t stream) {
+    const int64_t k = T / E;
+    const unsigned g1 = (unsigned)(((T > E ? T : E) + 255) / 256);
+    hipLaunchKernelGGL(auc_init_kernel, dim3(g1), dim3(256), 0, stream, w, E, scan, T * E, st, assign, T);
+    const int rounds = (k <= kBulkKMax) ? kBulkRounds : 0;
+    int64_t bid_blocks = (T + 15) / 16;
+    if (bid_blocks > 2048) bid_blocks = 2048;
+    const size_t tail_lds = (size_t)E * (8 + 8 + 4 * 4);
+    double eps = eps_start;
+    for (int phase = 0;; ++phase) {
+        hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
+                           stream, w, T, E, st);
+        for (int r = 0; r < rounds; ++r) {
+            hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3((unsigned)bid_blocks), dim3(256), 0,
+                               stream, s, T, E, w, scan, r, eps);
+            hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
+                               E, k, w);
+        }
+        hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(kTailThreads), tail_lds, stream, s, T,
+                           E, k, w, scan, eps, phase, max_bids, st);
+        if (eps <= eps_end) break;
+        eps = eps / eps_factor;
+        if (eps < eps_end) eps = eps_end;
+    }
+    hipLaunchKernelGGL(auc_finalize_kernel, dim3((unsigned)E), dim3(256), 0, stream, w, E, k, assign,
+                       prices);
+    return hipGetLastError();
+}
+
+hipError_t launch_auction(const float* s, int64_t T, int64_t E, double eps_start, double eps_end,
+                          double eps_factor, int64_t max_bids, const ScoreScan* scan,
+                          int32_t* assign, int32_t* perm, int32_t* offsets, double* prices,
+                          AucStatsDev* stats, void* ws, hipStream_t stream) {
+    AucWs w = carve(ws, T, E);
+    hipError_t err;
+    const int64_t nch = (E + 63) / 64;
+    if (nch <= 1) err = run_auction<1>(s, T, E, eps_start, eps_end, eps_factor, max_bids, scan, assign, prices, stats, w, stream);
+    else if (nch <= 2) err = run_auction<2>(s, T, E, eps_start, eps_end, eps_factor, max_bids, scan, assign, prices, stats, w, stream);
+    else if (nch <= 4) err = run_auction<4>(s, T, E, eps_start, eps_end, eps_factor, max_bids, scan, assign, prices, stats, w, stream);
+    else if (nch <= 8) err = run_auction<8>(s, T, E, eps_start, eps_end, eps_factor, max_bids, scan, assign, prices, stats, w, stream);
+    else err = run_auction<16>(s, T, E, eps_start, eps_end, eps_factor, max_bids, scan, assign, prices, stats, w, stream);
+    if (err != hipSuccess) return err;
+    // expert grouping (ascending token id within each expert); the perm
+    // workspace follows the auction's
+    return launch_perm(assign, T, E, perm, offsets, nullptr, 0, nullptr,
+                       (char*)ws + auction_ws_bytes(T, E), stream);
+}
+
+}  // namespace base

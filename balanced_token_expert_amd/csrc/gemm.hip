@@ -1,0 +1,356 @@
+// Dense products of the BASE layer on gfx950.
+//
+// Three products share one "NT" kernel shape, C[m][n] = sum_k A[m][k] B[n][k]
+// with K contiguous in both operands:
+//   affinity  s = h w^T                       ("BASE Layers" sec. 3.1, fig. 2)
+//   FFN1      H_e = act(X_e W1_e^T), X_e[i] = h[perm[e*k+i]]   (gather fused
+//             into the A-tile loads: fig. 2's expert sort costs no pass)
+//   FFN2      Y_e = H_e W2_e^T with the epilogue of eq. 1:
+//             out[t] = sigmoid(s[t][e]) * Y_e[i] + h[t], t = perm[e*k+i]
+//             (fig. 2's inverse sort fused into the stores)
+//
+// bf16 path: 64-wide waves issue v_mfma_f32_32x32x16_bf16 on tiles staged
+// through LDS (double-buffered, one barrier per 64-deep K step); fp32
+// accumulation. The block -> tile map keeps the tiles that share a weight
+// tile on one XCD (consecutive logical tiles land on the same L2).
+// fp32 path: a plain LDS-tiled FMA kernel (exact fp32 products).
+#include "common.h"
+#include "internal.h"
+
+namespace base {
+
+enum { KIND_AFF = 0, KIND_FFN1 = 1, KIND_FFN2 = 2 };
+
+struct GemmParams {
+    const void* A;          // bf16 bits or fp32, rows of length K
+    const void* B;          // N x K per group
+    int64_t M, N, K;        // M = rows per group
+    int64_t groups;
+    const int32_t* perm;    // FFN1: A row map; FFN2: output row map
+    int64_t b_gstride;      // elements between consecutive groups' B
+    float* s_out;           // AFF: M x N fp32
+    ScoreScan* scan;        // AFF: min finite key / non-finite count
+    void* H;                // FFN1 output, (groups*M) x N
+    int act;                // 0 relu, 1 gelu
+    const float* s_in;      // FFN2: gate scores, rows of length E
+    int64_t E;
+    const void* h;          // FFN2: residual rows (length N)
+    void* out;              // FFN2: output rows (length N)
+};
+
+// Physical block id -> logical tile id such that each XCD (blocks are dealt
+// round-robin to the 8 XCDs) receives a contiguous run of logical tiles.
+BASE_DEV int64_t xcd_logical(int64_t pid, int64_t nblk) {
+    int64_t x = pid & 7, slot = pid >> 3;
+    int64_t per = nblk >> 3, rem = nblk & 7;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+
+BASE_DEV float apply_act(float v, int act) { return act ? gelu_erf(v) : fmaxf(v, 0.0f); }
+
+// ---------------------------------------------------------------- bf16 MFMA
+
+template <int Kind, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
+    constexpr int BK = 64, LDK = BK + 8;
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int CA = BM * (BK / 8) / NT;   // 16-byte A chunks per thread
+    constexpr int CB = BN * (BK / 8) / NT;
+    static_assert(TM >= 1 && TN >= 1 && CA >= 1 && CB >= 1, "tile shape");
+    static_assert((BM * (BK / 8)) % NT == 0 && (BN * (BK / 8)) % NT == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+    const int64_t lid = xcd_logical(blockIdx.x, gridDim.x);
+    const int64_t g = lid / (ntm * ntn);
+    if (g >= p.groups) return;
+    const int64_t rr = lid % (ntm * ntn);
+    const int64_t tn = rr / ntm, tm = rr % ntm;  // M tiles fastest: they share B
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
+
+    // rows this thread stages (fixed over the K loop)
+    const uint16_t* arow[CA];
+    const uint16_t* brow[CB];
+    int akc[CA], bkc[CB], ar[CA], br[CB];
+#pragma unroll
+    for (int j = 0; j < CA; ++j) {
+        int c = tid + j * NT;
+        ar[j] = c >> 3;
+        akc[j] = (c & 7) * 8;
+        int64_t m = m0 + ar[j];
+        arow[j] = nullptr;
+        if (m < p.M) {
+            int64_t src;
+            if (Kind == KIND_FFN1) src = p.perm[g * p.M + m];
+            else if (Kind == KIND_FFN2) src = g * p.M + m;
+            else src = m;
+            arow[j] = A + src * p.K;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        int c = tid + j * NT;
+        br[j] = c >> 3;
+        bkc[j] = (c & 7) * 8;
+        int64_t n = n0 + br[j];
+        brow[j] = (n < p.N) ? B + n * p.K : nullptr;
+    }
+
+    uint4 ra[CA], rb[CB];
+    auto load_regs = [&](int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < CA; ++j) {
+            int64_t kk = k0 + akc[j];
+            ra[j] = (arow[j] && kk < p.K) ? *(const uint4*)(arow[j] + kk) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            int64_t kk = k0 + bkc[j];
+            rb[j] = (brow[j] && kk < p.K) ? *(const uint4*)(brow[j] + kk) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < CA; ++j) *(uint4*)&As[buf][ar[j] * LDK + akc[j]] = ra[j];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) *(uint4*)&Bs[buf][br[j] * LDK + bkc[j]] = rb[j];
+    };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = (p.K + BK - 1) / BK;
+    load_regs(0);
+    store_lds(0);
+    __syncthreads();
+    const int frow = lane & 31, fk = (lane >> 5) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_regs((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *(const bf16x8_t*)&As[buf][(wm * WTM + i * 32 + frow) * LDK + kk * 16 + fk];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *(const bf16x8_t*)&Bs[buf][(wn * WTN + j * 32 + frow) * LDK + kk * 16 + fk];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store_lds(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue. acc[i][j][r] is C[row][col] with
+    //   row = wm*WTM + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = wn*WTN + j*32 + lane%32
+    uint32_t kmin = 0xffffffffu;
+    int nonfin = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (m >= p.M) continue;
+            int64_t t = 0;
+            float gate = 0.0f;
+            if (Kind == KIND_FFN2) {
+                t = p.perm[g * p.M + m];
+                gate = sigmoid_f32(p.s_in[t * p.E + g]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+                if (n >= p.N) continue;
+                const float v = acc[i][j][r];
+                if (Kind == KIND_AFF) {
+                    p.s_out[m * p.N + n] = v;
+                    if (is_finite_f32(v)) kmin = min(kmin, f32_key(v));
+                    else ++nonfin;
+                } else if (Kind == KIND_FFN1) {
+                    ((uint16_t*)p.H)[(g * p.M + m) * p.N + n] = f32_to_bf16(apply_act(v, p.act));
+                } else {
+                    const float res = bf16_to_f32(((const uint16_t*)p.h)[t * p.N + n]);
+                    ((uint16_t*)p.out)[t * p.N + n] = f32_to_bf16(gate * v + res);
+                }
+            }
+        }
+    }
+    if (Kind == KIND_AFF) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+            nonfin += __shfl_xor(nonfin, o, 64);
+        }
+        if (lane == 0 && p.scan) {
+            if (kmin != 0xffffffffu) atomicMin(&p.scan->min_key, kmin);
+            if (nonfin) atomicAdd(&p.scan->nonfinite, (uint32_t)nonfin);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 FMA
+
+template <int Kind>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[BK][BN + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+    const int64_t lid = blockIdx.x;
+    const int64_t g = lid / (ntm * ntn);
+    if (g >= p.groups) return;
+    const int64_t rr = lid % (ntm * ntn);
+    const int64_t tn = rr / ntm, tm = rr % ntm;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const float* A = (const float*)p.A;
+    const float* B = (const float*)p.B + g * p.b_gstride;
+
+    // staging: 64 rows x 16 k per tile, 4 elements per thread
+    const int lr = tid >> 2, lk = (tid & 3) * 4;
+    const float* arow = nullptr;
+    {
+        int64_t m = m0 + lr;
+        if (m < p.M) {
+            int64_t src = (Kind == KIND_FFN1) ? p.perm[g * p.M + m]
+                        : (Kind == KIND_FFN2) ? g * p.M + m : m;
+            arow = A + src * p.K;
+        }
+    }
+    const float* brow = (n0 + lr < p.N) ? B + (n0 + lr) * p.K : nullptr;
+
+    float acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int64_t kk = k0 + lk + q;
+            As[lk + q][lr] = (arow && kk < p.K) ? arow[kk] : 0.0f;
+            Bs[lk + q][lr] = (brow && kk < p.K) ? brow[kk] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    uint32_t kmin = 0xffffffffu;
+    int nonfin = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty * 4 + i;
+        if (m >= p.M) continue;
+        int64_t t = 0;
+        float gate = 0.0f;
+        if (Kind == KIND_FFN2) {
+            t = p.perm[g * p.M + m];
+            gate = sigmoid_f32(p.s_in[t * p.E + g]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx * 4 + j;
+            if (n >= p.N) continue;
+            const float v = acc[i][j];
+            if (Kind == KIND_AFF) {
+                p.s_out[m * p.N + n] = v;
+                if (is_finite_f32(v)) kmin = min(kmin, f32_key(v));
+                else ++nonfin;
+            } else if (Kind == KIND_FFN1) {
+                ((float*)p.H)[(g * p.M + m) * p.N + n] = apply_act(v, p.act);
+            } else {
+                ((float*)p.out)[t * p.N + n] = gate * v + ((const float*)p.h)[t * p.N + n];
+            }
+        }
+    }
+    if (Kind == KIND_AFF) {
+        const int lane = tid & 63;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+            nonfin += __shfl_xor(nonfin, o, 64);
+        }
+        if (lane == 0 && p.scan) {
+            if (kmin != 0xffffffffu) atomicMin(&p.scan->min_key, kmin);
+            if (nonfin) atomicAdd(&p.scan->nonfinite, (uint32_t)nonfin);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int Kind, int BM, int BN, int WM, int WN>
+static hipError_t run_bf16(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.groups;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_kernel<Kind, BM, BN, WM, WN>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int Kind>
+static hipError_t run_f32(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64) * p.groups;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_f32_kernel<Kind>, dim3((unsigned)tiles), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_affinity(const void* h, const void* w, float* s, int64_t T, int64_t E,
+                           int64_t D, int dt, ScoreScan* scan, hipStream_t st) {
+    GemmParams p = {};
+    p.A = h; p.B = w; p.M = T; p.N = E; p.K = D; p.groups = 1;
+    p.s_out = s; p.scan = scan;
+    if (dt == 0) return run_f32<KIND_AFF>(p, st);
+    if (E <= 64) return run_bf16<KIND_AFF, 128, 64, 2, 2>(p, st);
+    return run_bf16<KIND_AFF, 128, 128, 2, 2>(p, st);
+}
+
+hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1, void* H, int64_t E,
+                       int64_t k, int64_t D, int64_t F, int dt, int act, hipStream_t st) {
+    GemmParams p = {};
+    p.A = h; p.B = W1; p.M = k; p.N = F; p.K = D; p.groups = E;
+    p.perm = perm; p.b_gstride = F * D; p.H = H; p.act = act;
+    if (dt == 0) return run_f32<KIND_FFN1>(p, st);
+    return run_bf16<KIND_FFN1, 128, 128, 2, 2>(p, st);
+}
+
+hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const float* s,
+                       const void* h, void* out, int64_t E, int64_t k, int64_t D, int64_t F,
+                       int dt, hipStream_t st) {
+    GemmParams p = {};
+    p.A = H; p.B = W2; p.M = k; p.N = D; p.K = F; p.groups = E;
+    p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
+    if (dt == 0) return run_f32<KIND_FFN2>(p, st);
+    return run_bf16<KIND_FFN2, 128, 128, 2, 2>(p, st);
+}
+
+}  // namespace base

@@ -1,0 +1,264 @@
+// Score sanitizing scan, greedy routing and the stable expert grouping.
+//
+//  scan      one pass over s: smallest finite score and the number of NaN/inf
+//            scores. The released BASE code replaces non-finite affinities by
+//            the smallest finite one before solving; consumers apply that
+//            replacement on the fly from this summary.
+//  greedy    test-time routing of "BASE Layers" sec. 3.2.2: a_t = argmax_e
+//            s[t][e], lowest expert id among equal scores. One wave per row.
+//  perm      fig. 2's sort_by_expert: token ids grouped by expert, ascending
+//            within each group (a stable counting sort): per-chunk histograms,
+//            a scan, then ranks from bit-sliced wave ballots.
+#include "common.h"
+#include "internal.h"
+
+namespace base {
+
+constexpr int32_t kStatusUnbalanced = -8;
+
+__global__ void scan_init_kernel(ScoreScan* scan) {
+    if (threadIdx.x == 0) {
+        scan->min_key = 0xffffffffu;
+        scan->nonfinite = 0;
+    }
+}
+
+__global__ __launch_bounds__(256) void scan_scores_kernel(const float* s, int64_t n, ScoreScan* scan) {
+    uint32_t kmin = 0xffffffffu;
+    uint32_t bad = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 v = ((const float4*)s)[i];
+        float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (is_finite_f32(a[q])) kmin = min(kmin, f32_key(a[q]));
+            else ++bad;
+        }
+    }
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float a = s[i];
+        if (is_finite_f32(a)) kmin = min(kmin, f32_key(a));
+        else ++bad;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+        bad += (uint32_t)__shfl_xor((int)bad, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        if (kmin != 0xffffffffu) atomicMin(&scan->min_key, kmin);
+        if (bad) atomicAdd(&scan->nonfinite, bad);
+    }
+}
+
+__global__ void stats_reset_kernel(AucStatsDev* st) {
+    if (threadIdx.x == 0) {
+        st->status = 0;
+        st->phases = 0;
+        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; }
+    }
+}
+
+hipError_t launch_stats_reset(AucStatsDev* st, hipStream_t s) {
+    hipLaunchKernelGGL(stats_reset_kernel, dim3(1), dim3(64), 0, s, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_init(ScoreScan* scan, hipStream_t st) {
+    hipLaunchKernelGGL(scan_init_kernel, dim3(1), dim3(64), 0, st, scan);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_scores(const float* s, int64_t n, ScoreScan* scan, hipStream_t st) {
+    int64_t blocks = (n / 4 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(scan_scores_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, n, scan);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- greedy
+
+__global__ __launch_bounds__(256) void greedy_kernel(const float* s, int64_t T, int64_t E,
+                                                     const ScoreScan* scan, int32_t* assign) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const bool fix = scan->nonfinite != 0;
+    const float repl = scan->min_key == 0xffffffffu ? 0.0f : f32_unkey(scan->min_key);
+    for (int64_t t = wave; t < T; t += nwaves) {
+        const float* row = s + t * E;
+        float best = 0.0f;
+        int bi = 0x7fffffff;
+        for (int64_t e = lane; e < E; e += 64) {
+            float v = row[e];
+            if (fix && !is_finite_f32(v)) v = repl;
+            if (bi == 0x7fffffff || v > best) { best = v; bi = (int)e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            float ov = __shfl_xor(best, o, 64);
+            int oi = __shfl_xor(bi, o, 64);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > best || (ov == best && oi < bi))) {
+                best = ov;
+                bi = oi;
+            }
+        }
+        if (lane == 0) assign[t] = bi;
+    }
+}
+
+hipError_t launch_greedy(const float* s, int64_t T, int64_t E, const ScoreScan* scan,
+                         int32_t* assign, int32_t* /*counts*/, hipStream_t st) {
+    int64_t blocks = (T + 3) / 4;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, T, E, scan, assign);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- perm
+
+constexpr int kPermChunk = 4096;  // tokens per block
+constexpr int kPermThreads = 256;
+
+size_t perm_ws_bytes(int64_t T, int64_t E) {
+    int64_t nb = (T + kPermChunk - 1) / kPermChunk;
+    return (size_t)(2 * nb * E + E) * sizeof(int32_t) + 256;
+}
+
+BASE_DEV int clamp_id(int32_t a, int64_t E) { return (a < 0 || a >= E) ? 0 : a; }
+
+// block b: counts of its chunk per expert -> cnt[b*E + e]
+__global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(const int32_t* assign, int64_t T,
+                                                                 int64_t E, int32_t* cnt,
+                                                                 int32_t* status) {
+    extern __shared__ int32_t hist[];
+    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kPermChunk;
+    const int64_t t1 = min(T, t0 + kPermChunk);
+    bool bad = false;
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+        int32_t a = assign[t];
+        if (a < 0 || a >= E) bad = true;
+        atomicAdd(&hist[clamp_id(a, E)], 1);
+    }
+    if (bad && status) *status = kStatusUnbalanced;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) cnt[blockIdx.x * E + e] = hist[e];
+}
+
+// one block: base[b*E+e] = offsets[e] + sum_{b'<b} cnt[b'*E+e]; offsets, counts
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* cnt, int64_t nb, int64_t E,
+                                                         int64_t T, int32_t* base, int32_t* offsets,
+                                                         int32_t* counts, int64_t want_k,
+                                                         int32_t* status, int32_t* tot) {
+    __shared__ int32_t part[1024];
+    // per-expert totals (and the running per-block prefix kept in base)
+    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t run = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            base[b * E + e] = run;
+            run += cnt[b * E + e];
+        }
+        tot[e] = run;
+        if (counts) counts[e] = run;
+        if (want_k > 0 && run != want_k && status) *status = kStatusUnbalanced;
+    }
+    __syncthreads();
+    // exclusive scan of tot over e: each thread sums a contiguous slice
+    const int64_t per = (E + blockDim.x - 1) / blockDim.x;
+    const int64_t e0 = threadIdx.x * per, e1 = min(E, e0 + per);
+    int32_t sum = 0;
+    for (int64_t e = e0; e < e1; ++e) sum += tot[e];
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t run = 0;
+        for (unsigned i = 0; i < blockDim.x; ++i) {
+            int32_t v = part[i];
+            part[i] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    int32_t run = part[threadIdx.x];
+    for (int64_t e = e0; e < e1; ++e) {
+        int32_t v = tot[e];
+        tot[e] = run;  // now the exclusive offset
+        if (offsets) offsets[e] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0 && offsets) offsets[E] = (int32_t)T;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
+        const int32_t off = tot[e];
+        for (int64_t b = 0; b < nb; ++b) base[b * E + e] += off;
+    }
+}
+
+// block b: stable placement of its chunk. Tokens are taken 256 at a time in
+// order; within a wave, equal-expert lanes are found with one ballot per bit
+// of the expert id, and the rank of a lane is the number of equal lanes below
+// it. Waves of a batch are ordered through per-wave counts in LDS.
+__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(const int32_t* assign, int64_t T,
+                                                                    int64_t E, const int32_t* base,
+                                                                    int32_t* perm) {
+    extern __shared__ int32_t sm[];
+    int32_t* running = sm;            // E
+    int32_t* wcnt = sm + E;           // 4 * E
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) running[e] = base[blockIdx.x * E + e];
+    int nbits = 0;
+    while ((1ll << nbits) < E) ++nbits;
+    const int64_t t0 = (int64_t)blockIdx.x * kPermChunk;
+    const int64_t t1 = min(T, t0 + kPermChunk);
+    for (int64_t tb = t0; tb < t1; tb += kPermThreads) {
+        for (int64_t i = threadIdx.x; i < 4 * E; i += blockDim.x) wcnt[i] = 0;
+        __syncthreads();
+        const int64_t t = tb + threadIdx.x;
+        const bool valid = t < t1;
+        const int e = valid ? clamp_id(assign[t], E) : 0;
+        unsigned long long same = __ballot(valid);
+        for (int j = 0; j < nbits; ++j) {
+            const bool bit = (e >> j) & 1;
+            const unsigned long long b = __ballot(valid && bit);
+            same &= bit ? b : ~b;
+        }
+        if (!valid) same = 0;
+        const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank = __popcll(same & below);
+        const bool last = valid && ((same >> lane) == 1ull);  // highest equal lane
+        if (last) wcnt[wave * E + e] = rank + 1;
+        __syncthreads();
+        if (valid) {
+            int pos = running[e] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+            perm[pos] = (int32_t)t;
+        }
+        __syncthreads();
+        for (int64_t x = threadIdx.x; x < E; x += blockDim.x)
+            running[x] += wcnt[x] + wcnt[E + x] + wcnt[2 * E + x] + wcnt[3 * E + x];
+        __syncthreads();
+    }
+}
+
+hipError_t launch_perm(const int32_t* assign, int64_t T, int64_t E, int32_t* perm,
+                       int32_t* offsets, int32_t* counts, int64_t want_k, int32_t* status,
+                       void* ws, hipStream_t st) {
+    const int64_t nb = (T + kPermChunk - 1) / kPermChunk;
+    int32_t* cnt = (int32_t*)ws;
+    int32_t* base = cnt + nb * E;
+    int32_t* tot = base + nb * E;
+    hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nb), dim3(kPermThreads), E * sizeof(int32_t),
+                       st, assign, T, E, cnt, status);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, nb, E, T, base, offsets,
+                       counts, want_k, status, tot);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)nb), dim3(kPermThreads),
+                       5 * E * sizeof(int32_t), st, assign, T, E, base, perm);
+    return hipGetLastError();
+}
+
+}  // namespace base

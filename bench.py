@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the BASE-layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch: affinities, the
+balanced assignment (auction, eps 1.0 -> 1e-4, factor 10), the expert
+grouping, both expert products with the fused gate/residual/scatter
+(``base_layer_forward``, BALANCED) plus greedy test-time routing of the same
+scores (``base_route_greedy``), on the large workload: T=65536 tokens
+(32 x 2048), E=128 experts, D=2048, FFN 2048->8192->2048 GELU, bf16 (about
+8.6 GB of expert weights). Inputs are seeded synthetic data, resident in HBM
+before timing starts.
+
+Also reported: the auction solve time on the mixture workload (T=16384,
+E=128, D=1024, eps 1.0 -> 1e-4), the per-phase kernel times (HIP events
+recorded by the library on its stream), the roofline of the dominant kernel,
+and the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PHASES = ("affinity", "route", "ffn1", "ffn2")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles for the library's phase markers."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev[i] = h
+
+    def block(self, i):
+        """Address of handles [i, i+6) (a hipEvent_t array for the library)."""
+        return ctypes.addressof(self.ev) + i * ctypes.sizeof(ctypes.c_void_p)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+
+def gen_inputs(wl, threads=16):
+    from balanced_token_expert_amd import workloads as W
+    t0 = time.time()
+    w = W.gen_centroids(wl)
+    with ThreadPoolExecutor(threads) as ex:
+        blocks = list(ex.map(lambda c: W.gen_tokens(wl, rows=slice(c, min(wl.T, c + 4096)),
+                                                    centroids=w), range(0, wl.T, 4096)))
+        h = np.concatenate(blocks)
+        W1 = W2 = None
+        if wl.F is not None:
+            W1 = list(ex.map(lambda e: W.gen_w1(wl, e), range(wl.E)))
+            W2 = list(ex.map(lambda e: W.gen_w2(wl, e), range(wl.E)))
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s")
+    return h, w, W1, W2
+
+
+def to_dev(x, dtype="bf16"):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def stack_dev(parts, dtype="bf16"):
+    import torch
+    E = len(parts)
+    out = torch.empty((E,) + parts[0].shape,
+                      dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    for e, p in enumerate(parts):
+        out[e].copy_(to_dev(p, dtype))
+    return out
+
+
+def cpu_baseline(wl, h, w, W1, W2, sample_experts=8):
+    """The oracle as it stands, on a bounded sample: affinities, CPU auction
+    and greedy routing over all T tokens; the fp64 layer forward for the
+    tokens of `sample_experts` experts. Scaled to tokens/s of the full step."""
+    import oracle
+    from balanced_token_expert_amd import workloads as W
+    t0 = time.perf_counter()
+    s = oracle.affinity(W.as_f64(h, wl.dtype), W.as_f64(w, wl.dtype))
+    t_aff = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = oracle.auction(s, wl.eps_start, wl.eps_end, wl.eps_factor)
+    t_auc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.greedy_route(s)
+    t_gr = time.perf_counter() - t0
+    a = r["assign"]
+    ex = list(range(sample_experts))
+    n_tok = int(np.isin(a, ex).sum())
+    t0 = time.perf_counter()
+    oracle.layer_forward(W.as_f64(h, wl.dtype), W.as_f64(w, wl.dtype),
+                         lambda e: W.as_f64(W1[e], wl.dtype), lambda e: W.as_f64(W2[e], wl.dtype),
+                         a, wl.act, experts=ex, s=s)
+    t_ffn = time.perf_counter() - t0
+    per_tok = (t_aff + t_auc + t_gr) / wl.T + t_ffn / max(n_tok, 1)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(1.0 / per_tok, 1), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"{wl.name}: fp64 affinity, CPU auction (1 thread) and greedy over all "
+                       f"{wl.T} tokens ({t_aff:.2f}s, {t_auc:.2f}s, {t_gr:.2f}s); fp64 expert "
+                       f"FFN + eq. 1 for the {n_tok} tokens of experts 0..{sample_experts - 1} "
+                       f"({t_ffn:.2f}s); per-token costs summed"),
+            "auction_s": round(t_auc, 3)}
+
+
+def auction_solve(reps=10):
+    """Auction solve ms on the mixture workload (device-resident fp32 scores)."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    import oracle
+    wl = W.workload(2)
+    h, w, _, _ = gen_inputs(wl)
+    hd, wd = to_dev(h), to_dev(w)
+    s = api.base_affinity(hd, wd)
+    T, E = wl.T, wl.E
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=100 * T * 5)
+    bufs = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+                perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                prices=torch.empty(E, dtype=torch.float64, device="cuda"),
+                stats=api.new_stats(), ws=api.workspace(api.BASE_OP_AUCTION, T, E))
+    for _ in range(2):
+        api.base_assign_auction(s, c, **bufs)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        api.base_assign_auction(s, c, **bufs)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    st = api.read_stats(bufs["stats"])
+    s32 = s.cpu().numpy().astype(np.float64)
+    asg = bufs["assign"].cpu().numpy()
+    p = bufs["prices"].cpu().numpy()
+    k = T // E
+    gap = oracle.dual_value(s32, p, k) - oracle.objective(s32, asg)
+    balanced = bool((np.bincount(asg, minlength=E) == k).all())
+    t0 = time.perf_counter()
+    oracle.auction(s32, wl.eps_start, wl.eps_end, wl.eps_factor)
+    t_cpu = time.perf_counter() - t0
+    return {"value": round(float(np.median(times)), 4), "unit": "ms", "workload": wl.name,
+            "eps": f"{wl.eps_start}->{wl.eps_end} x1/{wl.eps_factor}", "reps": reps,
+            "min_ms": round(float(np.min(times)), 4), "status": st.status,
+            "bids_per_phase": st.bids, "bulk_rounds_per_phase": st.rounds,
+            "balanced": balanced, "dual_gap": gap, "dual_gap_bound": T * wl.eps_end,
+            "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=5, help=argparse.SUPPRESS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-auction", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (every expert resident on one "
+              "MI355X, no collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+
+    api.load()
+    torch.cuda.init()
+    wl = W.workload(args.workload)
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    h, w, W1, W2 = gen_inputs(wl)
+    hd, wd = to_dev(h, wl.dtype), to_dev(w, wl.dtype)
+    W1d, W2d = stack_dev(W1, wl.dtype), stack_dev(W2, wl.dtype)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs on device: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=100 * T * 5)
+    lay = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+               scores=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+               perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+               out=torch.empty_like(hd), stats=api.new_stats(),
+               ws=api.workspace(api.BASE_OP_LAYER, T, E, D, F,
+                                api.BASE_BF16 if wl.dtype == "bf16" else api.BASE_F32))
+    gr = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+              counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+              ws=api.workspace(api.BASE_OP_GREEDY, T, E))
+
+    nsteps = args.warmup + args.steps
+    ev = HipEvents(6 * nsteps)
+    gr_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(nsteps)]
+
+    def step(i):
+        api.base_set_phase_events(ev.block(6 * i), 6)
+        api.base_layer_forward(hd, wd, W1d, W2d, act, api.BASE_ROUTE_BALANCED, c, **lay)
+        gr_ev[i][0].record()
+        api.base_route_greedy(lay["scores"], **gr)
+        gr_ev[i][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    wall0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    api.base_set_phase_events(None, 0)
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-phase kernel times over the timed steps
+    ph = {p: [] for p in PHASES}
+    ph["greedy"] = []
+    for i in range(args.warmup, nsteps):
+        b = 6 * i
+        for j, p in enumerate(PHASES):
+            ph[p].append(ev.ms(b + j, b + j + 1))
+        ph["greedy"].append(gr_ev[i][0].elapsed_time(gr_ev[i][1]))
+    avg = {p: float(np.mean(v)) for p, v in ph.items()}
+    st = api.read_stats(lay["stats"])
+    a = lay["assign"].cpu().numpy()
+    balanced = bool((np.bincount(a, minlength=E) == T // E).all())
+    gcount = gr["counts"].cpu().numpy()
+
+    # roofline of the dominant kernel (one launch per phase for the products)
+    flops_ffn = 2.0 * T * D * F
+    kern = max(("ffn1", "ffn2"), key=lambda p: avg[p])
+    achieved = flops_ffn / (avg[kern] * 1e-3) / 1e12
+    roof = {"kernel": f"{kern} (expert GEMM {'1' if kern == 'ffn1' else '2'}, "
+                      f"{E} experts x [{T // E}x{D if kern == 'ffn1' else F}]"
+                      f"x[{D if kern == 'ffn1' else F}x{F if kern == 'ffn1' else D}])",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "algorithmic_flops": flops_ffn,
+            "avg_launch_ms": round(avg[kern], 4)}
+
+    res = {"metric": "BASE layer fwd tokens/s at 1 GPU + auction solve ms (T=16k, E=128)",
+           "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded numpy PCG64, shapes of the paper's setting)",
+           "config": {"workload": wl.name, "T": T, "E": E, "D": D, "F": F, "act": wl.act,
+                      "route": "balanced auction eps 1.0->1e-4 (factor 10) + greedy on the "
+                               "same scores", "parallelism": "single GPU, all experts resident"},
+           "phase_ms": {p: round(v, 4) for p, v in avg.items()},
+           "auction": {"status": st.status, "bids_per_phase": st.bids,
+                       "bulk_rounds_per_phase": st.rounds, "balanced": balanced},
+           "greedy_load": {"max_over_mean": round(float(gcount.max() / (T / E)), 3),
+                           "max_share": round(float(gcount.max() / T), 5),
+                           "uniform_share": round(1.0 / E, 5)},
+           "roofline": roof, "wall_s_timed": round(wall, 3)}
+    if not args.no_auction:
+        res["auction_solve_ms"] = auction_solve()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, h, w, W1, W2)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

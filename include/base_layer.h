@@ -1,0 +1,225 @@
+/*
+ * base_layer.h -- C ABI of the MI355X (gfx950) BASE-layer forward library
+ * (libbase_layer.so).
+ *
+ * The operation is the forward pass of a BASE layer -- Lewis, Bhosale,
+ * Dettmers, Goyal, Zettlemoyer, "BASE Layers: Simplifying Training of Large,
+ * Sparse Models" (arXiv 2103.16716):
+ *   - token-expert affinities s[t][e] = h_t . w_e (sec. 3.1; fig. 2 scores the
+ *     tokens against the expert centroids);
+ *   - the balanced assignment of eq. 2 (sec. 3.2.1): maximise sum_t s[t][a_t]
+ *     subject to every expert receiving exactly k = T/E tokens, solved by an
+ *     auction (sec. 3.2.1; the paper's own listing, fig. 9, is prior art --
+ *     here tokens bid for expert slots, see base_assign_auction);
+ *   - greedy test-time routing, a_t = argmax_e s[t][e] (sec. 3.2.2);
+ *   - grouping the tokens by expert (fig. 2's expert sort), running each
+ *     expert's position-wise FFN, and the output of eq. 1 (sec. 3.1):
+ *       y_t = sigmoid(h_t . w_{a_t}) * f_{a_t}(h_t) + h_t,
+ *     returned in the original token order (fig. 2 undoes the sort).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `stats` results and host structs passed by
+ *     value is a DEVICE pointer (HIP global memory) owned by the caller. The
+ *     library allocates nothing and keeps no pointer after the enqueued work
+ *     completes.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *     call returns without synchronising. Outputs are valid after the stream
+ *     reaches the enqueued work.
+ *   - Matrices are row-major and dense. Shapes: h T x D, w E x D, scores
+ *     T x E (fig. 2's orientation), W1 E x F x D and W2 E x D x F (each
+ *     expert's matrices in the [out, in] layout, so the reduction dimension
+ *     is contiguous for both products).
+ *   - Return value: BASE_OK (0) or a negative BASE_ERR_* code found on the
+ *     host before anything is enqueued (nothing is enqueued then), or
+ *     BASE_ERR_HIP if a launch failed. Conditions that only the device can
+ *     see are written to stats->status (see base_auction_stats).
+ *   - Calls that share a workspace must not overlap; use distinct workspaces
+ *     (or one stream) for concurrent calls.
+ */
+#ifndef BASE_LAYER_H_
+#define BASE_LAYER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *base_stream_t; /* a hipStream_t */
+
+typedef enum {
+    BASE_OK = 0,
+    BASE_ERR_INVALID_ARG = -1,   /* null pointer, size <= 0, E > T, bad enum,
+                                    eps schedule not eps_start >= eps_end > 0,
+                                    workspace too small */
+    BASE_ERR_INDIVISIBLE = -2,   /* T % E != 0 (eq. 2 needs T/E per expert;
+                                    the paper leaves this case open) */
+    BASE_ERR_UNSUPPORTED = -3,   /* a valid request this build does not serve */
+    BASE_ERR_HIP = -4,           /* a HIP launch or query failed */
+    BASE_ERR_NOT_CONVERGED = -5, /* device: the auction hit cfg.max_bids */
+    BASE_ERR_NONFINITE = -6,     /* device: no finite affinity at all */
+    BASE_ERR_UNBALANCED = -8     /* device: a given assignment is not balanced
+                                    or holds an expert id outside [0, E) */
+} base_status;
+
+typedef enum { BASE_F32 = 0, BASE_BF16 = 1 } base_dtype;
+
+/* Expert activation: ReLU (the paper's feed-forward blocks, sec. 4.1) or
+ * GELU in its exact erf form, x/2 * (1 + erf(x / sqrt 2)). */
+typedef enum { BASE_ACT_RELU = 0, BASE_ACT_GELU = 1 } base_act;
+
+/* How base_layer_forward routes tokens: the balanced assignment used in
+ * training (sec. 3.2.1), greedy argmax as at test time (sec. 3.2.2), or an
+ * assignment the caller gives (must be balanced). */
+typedef enum {
+    BASE_ROUTE_BALANCED = 0,
+    BASE_ROUTE_GREEDY = 1,
+    BASE_ROUTE_GIVEN = 2
+} base_route;
+
+/* Auction settings. The paper's listing leaves its epsilon undefined; this
+ * library takes Bertsekas-style eps-scaling: phases with eps = eps_start,
+ * max(eps/eps_factor, eps_end), ..., eps_end (eps_start == eps_end: a single
+ * phase). The result is within T * eps_end of the optimum of eq. 2, and is
+ * the optimum itself when eps_end < gap / T, gap being the distance from the
+ * optimum to the second-best balanced assignment. max_bids <= 0 means no cap;
+ * otherwise the auction stops once that many bids have been made and reports
+ * BASE_ERR_NOT_CONVERGED (a safety valve, not part of the method). */
+typedef struct {
+    double eps_start;
+    double eps_end;
+    double eps_factor; /* > 1; 10 is the usual choice */
+    int64_t max_bids;
+} base_auction_cfg;
+
+/* Written by the device (a DEVICE pointer); read it after the stream has
+ * reached the call. status is BASE_OK or BASE_ERR_NOT_CONVERGED /
+ * BASE_ERR_NONFINITE / BASE_ERR_UNBALANCED. bids[p] counts the bids of eps
+ * phase p (p < 16); rounds[p] counts that phase's parallel bidding rounds
+ * (all unassigned tokens bidding at once) before the remaining displacement
+ * chains were finished one bid at a time per chain. */
+typedef struct {
+    int32_t status;
+    int32_t phases;
+    int64_t bids[16];
+    int64_t rounds[16];
+} base_auction_stats;
+
+/* Workspace queries: the bytes of device scratch memory each entry point
+ * needs for the given sizes. The caller allocates it (any alignment the HIP
+ * allocator gives); its contents need not be initialised and are garbage on
+ * return. */
+typedef enum {
+    BASE_OP_AFFINITY = 0,
+    BASE_OP_AUCTION = 1,
+    BASE_OP_GREEDY = 2,
+    BASE_OP_LAYER = 3
+} base_op;
+
+size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F,
+                            int dtype);
+
+/* Text for a base_status code (static storage; never NULL). */
+const char *base_strerror(int code);
+
+/*
+ * base_affinity -- s[t][e] = sum_d h[t][d] * w[e][d]  (sec. 3.1, fig. 2).
+ *   h: T x D, w: E x D, both of dtype dt (bf16 or fp32);
+ *   scores: T x E fp32 output. Products and sums in fp32 (bf16 inputs are
+ *   widened exactly); the summation order is the kernel's.
+ * Errors: BASE_ERR_INVALID_ARG for null pointers or non-positive sizes.
+ * No workspace. Non-finite results are stored as computed.
+ */
+int base_affinity(const void *h, const void *w, float *scores, int64_t T,
+                  int64_t E, int64_t D, int dt, base_stream_t stream);
+
+/*
+ * base_assign_auction -- balanced assignment of eq. 2 (sec. 3.2.1) by a
+ * token-side auction with eps-scaling.
+ *   scores: T x E fp32 (read only). NaN and +-inf are read as the smallest
+ *     finite score of the matrix, as the released code does before solving;
+ *     if no score is finite, stats->status = BASE_ERR_NONFINITE.
+ *   assign[T] (out, int32): the expert of each token; every expert gets
+ *     exactly k = T/E tokens.
+ *   perm[T] (out, int32): token ids grouped by expert, ascending within
+ *     each expert: perm[e*k .. e*k+k-1] are expert e's tokens.
+ *   offsets[E+1] (out, int32): offsets[e] = e*k.
+ *   prices[E] (out, fp64): final expert prices p_e (the lowest bid each
+ *     expert holds). They certify the result: with
+ *     D(p) = sum_t max_e (s[t][e] - p_e) + k sum_e p_e (>= optimum),
+ *     sum_t s[t][a_t] >= D(p) - T * eps_end.
+ *   stats (device pointer, may be NULL): see base_auction_stats.
+ *   ws / ws_bytes: scratch of base_workspace_bytes(BASE_OP_AUCTION, ...).
+ * Errors (host): INVALID_ARG, INDIVISIBLE (T % E), UNSUPPORTED if
+ *   T > 2^24 or E > 1024.
+ */
+int base_assign_auction(const float *scores, int64_t T, int64_t E,
+                        base_auction_cfg cfg, int32_t *assign, int32_t *perm,
+                        int32_t *offsets, double *prices,
+                        base_auction_stats *stats, void *ws, size_t ws_bytes,
+                        base_stream_t stream);
+
+/*
+ * base_route_greedy -- test-time routing (sec. 3.2.2): a_t = the expert with
+ * the highest score, the lowest expert id among equal scores (scores
+ * sanitised as in base_assign_auction; all non-finite -> every token to
+ * expert 0 and stats-free status is not reported).
+ *   assign[T], counts[E] (tokens per expert), perm[T] (grouped by expert,
+ *   ascending token id within a group), offsets[E+1] (prefix sums of
+ *   counts). Any of counts/perm/offsets may be NULL to skip it (perm and
+ *   offsets go together).
+ *   ws: scratch of base_workspace_bytes(BASE_OP_GREEDY, ...).
+ * T % E need not be 0.
+ */
+int base_route_greedy(const float *scores, int64_t T, int64_t E,
+                      int32_t *assign, int32_t *counts, int32_t *perm,
+                      int32_t *offsets, void *ws, size_t ws_bytes,
+                      base_stream_t stream);
+
+/*
+ * base_layer_forward -- the whole BASE layer forward (fig. 2 without the
+ * cross-worker shuffle and all-to-alls: one device holds every expert):
+ * affinities, routing, expert grouping, y = sigmoid(s[t][a_t]) * f(h_t) + h_t
+ * (eq. 1) with f_e(x) = W2_e act(W1_e x) (no bias), output in token order.
+ *   h: T x D, w: E x D, W1: E x F x D, W2: E x D x F, out: T x D, all dtype
+ *     dt. For bf16, products accumulate in fp32 and the hidden activation
+ *     act(W1 x) is stored as bf16 between the two products; for fp32 all
+ *     arithmetic is fp32. The gate uses the fp32 affinity of the chosen
+ *     expert.
+ *   mode: BASE_ROUTE_BALANCED (auction, cfg used) or BASE_ROUTE_GIVEN
+ *     (assign is an input; a token with an id outside [0,E) or an expert
+ *     without exactly k tokens sets stats->status = BASE_ERR_UNBALANCED and
+ *     out is left unspecified) or BASE_ROUTE_GREEDY (ragged expert groups:
+ *     returns BASE_ERR_UNSUPPORTED in this build; base_route_greedy gives
+ *     the routing).
+ *   assign[T]: output (BALANCED) or input (GIVEN).
+ *   scores: T x E fp32 output, or NULL (then kept in the workspace).
+ *   perm: T int32 output of the expert grouping, or NULL.
+ *   stats: device pointer or NULL; prices are written to the workspace.
+ *   ws: scratch of base_workspace_bytes(BASE_OP_LAYER, T, E, D, F, dt).
+ * Errors: as base_assign_auction; INDIVISIBLE also for GIVEN mode.
+ */
+int base_layer_forward(const void *h, const void *w, const void *W1,
+                       const void *W2, int64_t T, int64_t E, int64_t D,
+                       int64_t F, int dt, int act, int mode,
+                       base_auction_cfg cfg, int32_t *assign, float *scores,
+                       int32_t *perm, void *out, base_auction_stats *stats,
+                       void *ws, size_t ws_bytes, base_stream_t stream);
+
+/*
+ * base_set_phase_events -- optional tracing. When `events` is non-NULL, every
+ * later base_layer_forward call on this host thread records n (<= 6) HIP
+ * events (hipEvent_t, created by the caller) on its stream: [0] before the
+ * affinity product, [1] after it, [2] after routing and grouping, [3] after
+ * the first expert product, [4] after the second (the end), [5] = [4]. The
+ * caller reads durations with hipEventElapsedTime. NULL turns tracing off.
+ * Returns BASE_ERR_INVALID_ARG if n is outside [0, 6].
+ */
+int base_set_phase_events(void **events, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASE_LAYER_H_ */

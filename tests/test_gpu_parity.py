@@ -1,0 +1,312 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Criteria: affinities within Higham's fp32 dot-product bound of the exact fp64
+value (bit-exact on inputs whose products and sums are exact in fp32);
+greedy routing and the expert grouping bit-exact given the same scores;
+auction assignments exactly balanced, eps-complementary-slack w.r.t. the
+returned prices, within T*eps_end of the exact optimum, and equal to the
+unique optimum when eps_end < gap/T; layer outputs within 1e-5 (fp32) /
+2e-2 (bf16) relative error of the oracle given the same assignment, and
+equal to h bit-exactly when W2 = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from balanced_token_expert_amd import api
+from balanced_token_expert_amd import workloads as W
+from tests.gpu_util import dev_to_f64, f64, higham_bound, inputs, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# shapes spanning several tiles with ragged tails (M, N and K not multiples
+# of the 128x128x64 tiles)
+SMALL = [
+    dict(T=640, E=10, D=136, F=200, dtype="bf16", act="gelu", kind="iid"),
+    dict(T=640, E=10, D=72, F=96, dtype="f32", act="relu", kind="iid"),
+    dict(T=1536, E=24, D=256, F=320, dtype="bf16", act="relu", kind="mixture"),
+    dict(T=2048, E=16, D=128, F=264, dtype="bf16", act="gelu", kind="skew"),
+]
+
+
+def _wl(c, wid=900):
+    return W.custom(c["T"], c["E"], c["D"], F=c["F"], dtype=c["dtype"], act=c["act"],
+                    kind=c["kind"], wid=wid)
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ affinity
+
+@pytest.mark.parametrize("c", SMALL + [dict(T=512, E=8, D=64, F=256, dtype="f32", act="relu",
+                                             kind="iid")])
+def test_affinity_within_fp32_dot_bound(c):
+    wl = _wl(c, wid=901)
+    host, dev = inputs(wl, experts=False)
+    s = api.base_affinity(dev["h"], dev["w"])
+    _sync()
+    h64, w64 = f64(host["h"], wl.dtype), f64(host["w"], wl.dtype)
+    ref = oracle.affinity(h64, w64)
+    err = np.abs(s.cpu().numpy().astype(np.float64) - ref)
+    bound = higham_bound(h64, w64)
+    assert (err <= bound).all(), f"max err/bound {(err / bound).max()}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_affinity_bit_exact_on_small_integers(dtype):
+    # integer entries in [-4, 4]: every product and partial sum is an integer
+    # below 2^24, exact in fp32 whatever the summation order
+    rng = np.random.default_rng(5)
+    T, E, D = 300, 40, 200
+    hi = rng.integers(-4, 5, size=(T, D)).astype(np.float32)
+    wi = rng.integers(-4, 5, size=(E, D)).astype(np.float32)
+    conv = W.f32_to_bf16_bits if dtype == "bf16" else (lambda x: x)
+    s = api.base_affinity(to_dev(conv(hi), dtype), to_dev(conv(wi), dtype))
+    _sync()
+    ref = oracle.affinity(hi.astype(np.float64), wi.astype(np.float64))
+    np.testing.assert_array_equal(s.cpu().numpy().astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------ greedy + perm
+
+@pytest.mark.parametrize("T,E", [(640, 10), (4096, 128), (1000, 7), (333, 1)])
+def test_greedy_and_perm_bit_exact(T, E):
+    rng = np.random.default_rng(T + E)
+    # coarse values so that ties occur (lowest expert id must win)
+    s = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+    sd = to_dev(s, "f32")
+    r = api.base_route_greedy(sd)
+    _sync()
+    a, cnt = oracle.greedy_route(s)
+    perm, off = oracle.canonical_perm(a, E)
+    assert (r["assign"].cpu().numpy() == a).all()
+    assert (r["counts"].cpu().numpy() == cnt).all()
+    assert (r["perm"].cpu().numpy() == perm).all()
+    assert (r["offsets"].cpu().numpy() == off).all()
+
+
+def test_greedy_sanitizes_nonfinite():
+    s = np.array([[np.nan, -5.0, -7.0], [np.inf, 1.0, 2.0], [-np.inf, -np.inf, -9.0],
+                  [3.0, np.nan, 3.0]], dtype=np.float32)
+    r = api.base_route_greedy(to_dev(s, "f32"))
+    _sync()
+    a, cnt = oracle.greedy_route(s)
+    assert r["assign"].cpu().numpy().tolist() == a.tolist()
+    assert r["counts"].cpu().numpy().tolist() == cnt.tolist()
+
+
+# ------------------------------------------------------------------ auction
+
+def _check_auction(s32: np.ndarray, res, eps_end: float, exact=None):
+    T, E = s32.shape
+    k = T // E
+    s = s32.astype(np.float64)
+    a = res["assign"].cpu().numpy()
+    p = res["prices"].cpu().numpy()
+    st = api.read_stats(res["stats"])
+    assert st.status == 0, st
+    cnt = np.bincount(a, minlength=E)
+    assert (cnt == k).all(), "unbalanced"
+    perm, off = oracle.canonical_perm(a, E)
+    assert (res["perm"].cpu().numpy() == perm).all()
+    assert (res["offsets"].cpu().numpy() == off).all()
+    viol = oracle.eps_cs_violation(s, a, p)
+    assert viol <= eps_end * (1 + 1e-9) + 1e-12, viol
+    P = oracle.objective(s, a)
+    Dv = oracle.dual_value(s, p, k)
+    assert P >= Dv - T * eps_end - 1e-7 * max(1.0, abs(P))
+    if exact is not None:
+        opt = oracle.objective(s, exact)
+        assert P >= opt - T * eps_end - 1e-9 * max(1.0, abs(opt))
+        assert P <= opt + 1e-9 * max(1.0, abs(opt))
+    return a, st
+
+
+@pytest.mark.parametrize("c", SMALL)
+@pytest.mark.parametrize("eps", [(1.0, 1e-4), (1e-2, 1e-2)])
+def test_auction_certificates_small(c, eps):
+    wl = _wl(c, wid=902)
+    host, dev = inputs(wl, experts=False)
+    s = api.base_affinity(dev["h"], dev["w"])
+    res = api.base_assign_auction(s, api.cfg(eps[0], eps[1], 10.0, max_bids=50_000_000))
+    _sync()
+    s32 = s.cpu().numpy()
+    exact = oracle.hungarian(s32.astype(np.float64)) if wl.T <= 1024 else \
+        oracle.cycle_cancel(s32.astype(np.float64),
+                            oracle.auction(s32.astype(np.float64), 1.0, 1e-5)["assign"])[0]
+    _check_auction(s32, res, eps[1], exact)
+
+
+@pytest.mark.parametrize("T,E,seed", [(512, 8, 0), (768, 12, 1), (1024, 4, 2), (600, 2, 3),
+                                      (256, 1, 4), (64, 64, 5)])
+def test_auction_bit_exact_below_gap(T, E, seed):
+    rng = np.random.default_rng(1000 + seed)
+    s32 = rng.standard_normal((T, E)).astype(np.float32)
+    s = s32.astype(np.float64)
+    opt_a = oracle.hungarian(s)
+    gap = oracle.min_cycle_gap(s, opt_a)
+    assert gap > 0
+    eps_end = min(1e-4, gap / (2 * T)) if np.isfinite(gap) else 1e-4
+    res = api.base_assign_auction(to_dev(s32, "f32"),
+                                  api.cfg(1.0, eps_end, 10.0, max_bids=50_000_000))
+    _sync()
+    a, _ = _check_auction(s32, res, eps_end, opt_a)
+    assert (a == opt_a).all()
+
+
+def test_auction_tail_only_large_k():
+    # k = 4096 > the bulk rounds' limit: the persistent tail does all bidding
+    rng = np.random.default_rng(7)
+    s32 = rng.standard_normal((8192, 2)).astype(np.float32)
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1.0, 1e-3, 10.0, 50_000_000))
+    _sync()
+    s = s32.astype(np.float64)
+    top = np.argsort(-(s[:, 0] - s[:, 1]), kind="stable")[:4096]
+    want = np.ones(8192, np.int32)
+    want[top] = 0
+    _check_auction(s32, res, 1e-3, want)
+
+
+def test_auction_rank1_closed_form():
+    # s = x_t * y_e, distinct x and y: the unique optimum is assortative
+    T, E = 2048, 16
+    k = T // E
+    rng = np.random.default_rng(11)
+    x = rng.permutation(np.linspace(-3, 3, T)).astype(np.float32)
+    y = rng.permutation(np.linspace(-1, 2, E)).astype(np.float32)
+    s32 = np.outer(x, y).astype(np.float32)
+    want = np.empty(T, np.int32)
+    by_x, by_y = np.argsort(-x), np.argsort(-y)
+    for j in range(E):
+        want[by_x[j * k:(j + 1) * k]] = by_y[j]
+    s = s32.astype(np.float64)
+    gap = oracle.min_cycle_gap(s, want)
+    assert gap > 0
+    eps_end = min(1e-4, gap / (2 * T))
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1.0, eps_end, 10.0, 50_000_000))
+    _sync()
+    a, _ = _check_auction(s32, res, eps_end, want)
+    assert (a == want).all()
+
+
+def test_auction_nonfinite_scores_sanitized():
+    rng = np.random.default_rng(12)
+    s32 = rng.standard_normal((256, 8)).astype(np.float32)
+    s32[rng.random((256, 8)) < 0.05] = np.nan
+    s32[3, :] = np.inf
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1.0, 1e-4, 10.0, 50_000_000))
+    _sync()
+    clean = oracle.sanitize(s32.astype(np.float64)).astype(np.float32)
+    _check_auction(clean, res, 1e-4, oracle.hungarian(clean.astype(np.float64)))
+
+
+def test_auction_all_nonfinite_reports_status():
+    s32 = np.full((64, 4), np.nan, dtype=np.float32)
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1.0, 1e-4, 10.0, 1_000_000))
+    _sync()
+    assert api.read_stats(res["stats"]).status == api.BASE_ERR_NONFINITE
+
+
+def test_auction_bid_cap_reports_not_converged():
+    rng = np.random.default_rng(13)
+    s32 = rng.standard_normal((4096, 64)).astype(np.float32)
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1e-3, 1e-3, 10.0, max_bids=1))
+    _sync()
+    assert api.read_stats(res["stats"]).status == api.BASE_ERR_NOT_CONVERGED
+    perm = res["perm"].cpu().numpy()
+    assert ((perm >= 0) & (perm < 4096)).all()
+
+
+# ------------------------------------------------------------------ layer
+
+def _layer_ref(wl, host, a, s32, experts=None):
+    h64, w64 = f64(host["h"], wl.dtype), f64(host["w"], wl.dtype)
+    W1 = lambda e: f64(host["W1"][e], wl.dtype)
+    W2 = lambda e: f64(host["W2"][e], wl.dtype)
+    return oracle.layer_forward(h64, w64, W1, W2, a, wl.act, experts=experts,
+                                s=s32.astype(np.float64))
+
+
+@pytest.mark.parametrize("c", SMALL)
+def test_layer_given_assignment_parity(c):
+    wl = _wl(c, wid=903)
+    host, dev = inputs(wl)
+    rng = np.random.default_rng(3)
+    a = rng.permutation(np.repeat(np.arange(wl.E), wl.k)).astype(np.int32)
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    r = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], dev["W2"], act,
+                               api.BASE_ROUTE_GIVEN, assign=torch.from_numpy(a).cuda())
+    _sync()
+    assert api.read_stats(r["stats"]).status == 0
+    s32 = r["scores"].cpu().numpy()
+    ref = _layer_ref(wl, host, a, s32)
+    y = dev_to_f64(r["out"])
+    tol = 1e-5 if wl.dtype == "f32" else 2e-2
+    assert rel_err(y, ref) <= tol, rel_err(y, ref)
+    perm, _ = oracle.canonical_perm(a, wl.E)
+    assert (r["perm"].cpu().numpy() == perm).all()
+
+
+@pytest.mark.parametrize("c", SMALL)
+def test_layer_balanced_parity(c):
+    wl = _wl(c, wid=904)
+    host, dev = inputs(wl)
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    r = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], dev["W2"], act,
+                               api.BASE_ROUTE_BALANCED, api.cfg(1.0, 1e-4, 10.0, 50_000_000))
+    _sync()
+    st = api.read_stats(r["stats"])
+    assert st.status == 0
+    a = r["assign"].cpu().numpy()
+    assert (np.bincount(a, minlength=wl.E) == wl.k).all()
+    s32 = r["scores"].cpu().numpy()
+    ref = _layer_ref(wl, host, a, s32)
+    tol = 1e-5 if wl.dtype == "f32" else 2e-2
+    assert rel_err(dev_to_f64(r["out"]), ref) <= tol
+
+
+@pytest.mark.parametrize("c", SMALL[:2])
+def test_layer_zero_w2_returns_h_exactly(c):
+    wl = _wl(c, wid=905)
+    host, dev = inputs(wl)
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    r = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], torch.zeros_like(dev["W2"]), act,
+                               api.BASE_ROUTE_BALANCED, api.cfg(1.0, 1e-3, 10.0, 50_000_000))
+    _sync()
+    assert torch.equal(r["out"], dev["h"])
+
+
+def test_layer_given_unbalanced_reports_status():
+    wl = _wl(SMALL[0], wid=906)
+    host, dev = inputs(wl)
+    a = np.zeros(wl.T, np.int32)
+    r = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_GELU,
+                               api.BASE_ROUTE_GIVEN, assign=torch.from_numpy(a).cuda())
+    _sync()
+    assert api.read_stats(r["stats"]).status == api.BASE_ERR_UNBALANCED
+
+
+# ------------------------------------------------------------------ host-side errors
+
+def test_host_errors():
+    s = torch.zeros((10, 3), device="cuda")
+    with pytest.raises(api.BaseError) as ei:
+        api.base_assign_auction(s, api.cfg())
+    assert ei.value.code == api.BASE_ERR_INDIVISIBLE
+    s = torch.zeros((12, 3), device="cuda")
+    with pytest.raises(api.BaseError) as ei:
+        api.base_assign_auction(s, api.cfg(1e-4, 1.0))
+    assert ei.value.code == api.BASE_ERR_INVALID_ARG
+    with pytest.raises(api.BaseError) as ei:
+        api.base_assign_auction(s, api.cfg(), ws=torch.empty(8, dtype=torch.uint8, device="cuda"))
+    assert ei.value.code == api.BASE_ERR_INVALID_ARG
+    h = torch.zeros((12, 8), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3, 8), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((3, 16, 8), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((3, 8, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(api.BaseError) as ei:
+        api.base_layer_forward(h, w, W1, W2, 1, api.BASE_ROUTE_GREEDY)
+    assert ei.value.code == api.BASE_ERR_UNSUPPORTED
