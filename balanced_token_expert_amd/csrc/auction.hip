@@ -25,10 +25,10 @@
 //     (bitonic sort in LDS) and returns the rest to the bidder list.
 //   tail (one persistent workgroup, 16 waves): once few tokens are left, each
 //     wave follows a displacement chain -- bid, take the expert's lock in LDS,
-//     evict its lowest holder, continue with the evicted token -- with prices,
-//     counts and the current lowest holder of every expert in LDS, and the
-//     evicted token's score row fetched together with the rescan of the
-//     expert's slots.
+//     evict its lowest holder, continue with the evicted token. Prices, counts
+//     and, per expert, a sorted list of its L lowest holders live in LDS, so
+//     an eviction and the new price need no memory round trip; the list is
+//     rebuilt from the expert's slots in global memory only when it runs dry.
 // Prices and bids are fp64: exactness needs eps below gap/T, far below fp32
 // resolution at prices of order one.
 #include <float.h>
@@ -45,6 +45,10 @@ constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
 constexpr int kTailThreads = 1024;
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
+constexpr int32_t kNoTok = 0x7fffffff;
+
+// lowest-holder list length per expert (LDS budget of the tail)
+static int low_len(int64_t E) { return E <= 256 ? 16 : (E <= 512 ? 8 : 4); }
 
 struct AucCtl {
     int32_t cur;          // bidder list in use (0/1)
@@ -64,27 +68,36 @@ struct AucWs {
     double* floor_;    // E   price floors p_e
     double* pi;        // E   prices for the next bulk round
     int32_t* cnt;      // E   holders per expert
-    int32_t* minslot;  // E   slot of the lowest holder (when full)
-    int32_t* mintok;   // E
+    int32_t* nlow;     // E   entries in the lowest-holder list
+    int32_t* comp;     // E   1 if the list holds every holder
+    double* lowb;      // E*L lowest holders, eviction order: bid
+    int32_t* lowt;     // E*L                                 token
+    int32_t* lows;     // E*L                                 slot
     int32_t* list0;    // T
     int32_t* list1;    // T
     int32_t* bexp;     // T   bid of token t: expert
     double* bval;      // T   bid of token t: amount
     int32_t* stok;     // E*k slot tokens
     double* sbid;      // E*k slot bids
+    int L;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 static AucWs carve(void* ws, int64_t T, int64_t E) {
     char* p = (char*)ws;
+    const int L = low_len(E);
     AucWs w;
+    w.L = L;
     w.ctl = (AucCtl*)p; p += align256(sizeof(AucCtl));
     w.floor_ = (double*)p; p += align256(E * 8);
     w.pi = (double*)p; p += align256(E * 8);
     w.cnt = (int32_t*)p; p += align256(E * 4);
-    w.minslot = (int32_t*)p; p += align256(E * 4);
-    w.mintok = (int32_t*)p; p += align256(E * 4);
+    w.nlow = (int32_t*)p; p += align256(E * 4);
+    w.comp = (int32_t*)p; p += align256(E * 4);
+    w.lowb = (double*)p; p += align256(E * L * 8);
+    w.lowt = (int32_t*)p; p += align256(E * L * 4);
+    w.lows = (int32_t*)p; p += align256(E * L * 4);
     w.list0 = (int32_t*)p; p += align256(T * 4);
     w.list1 = (int32_t*)p; p += align256(T * 4);
     w.bexp = (int32_t*)p; p += align256(T * 4);
@@ -95,8 +108,10 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
 }
 
 size_t auction_ws_bytes(int64_t T, int64_t E) {
+    const int L = low_len(E);
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + 3 * align256(E * 4) +
-           4 * align256(T * 4) + 2 * align256(T * 8) + align256(T * 4) + 256;
+           align256(E * L * 8) + 2 * align256(E * L * 4) + 4 * align256(T * 4) +
+           2 * align256(T * 8) + 256;
 }
 
 // ---------------------------------------------------------------- helpers
@@ -126,15 +141,15 @@ BASE_DEV void load_row(const float* s, int64_t t, int64_t E, int lane, Sani sn, 
 }
 
 // Best expert (lowest id on ties), best value and the best value over the
-// other experts, of s[t][e] - pi[e], reduced over the wave.
-// pb returns the price of b1 exactly as used for v1 (prices in LDS may be
-// raised by other waves meanwhile; the bid must use one consistent value).
+// other experts, of s[t][e] - pi[e], reduced over the wave. pb returns the
+// price of b1 exactly as used for v1 (prices in LDS may be raised by other
+// waves meanwhile; the bid must use one consistent value).
 template <int NCH, typename PiT>
 BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& b1, double& v1,
                        double& v2, double& pb) {
     double val[NCH], pv[NCH];
     double best = -DBL_MAX;
-    int bi = 0x7fffffff;
+    int bi = kNoTok;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = lane + 64 * c;
@@ -142,34 +157,25 @@ BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& 
         if (e < E) {
             pv[c] = pi[e];
             val[c] = (double)v[c] - pv[c];
-            if (bi == 0x7fffffff || val[c] > best) { best = val[c]; bi = e; }
+            if (bi == kNoTok || val[c] > best) { best = val[c]; bi = e; }
         } else {
             val[c] = -DBL_MAX;
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const double ob = shfl_xor_f64(best, o);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ob > best || (ob == best && oi < bi))) {
-            best = ob;
-            bi = oi;
-        }
-    }
+    wave_argmax_f64(best, bi);  // uniform from here on
     double sec = -DBL_MAX;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = lane + 64 * c;
         if (e < E && e != bi && val[c] > sec) sec = val[c];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sec = fmax(sec, shfl_xor_f64(sec, o));
+    sec = wave_max_f64(sec);
     if (E == 1) sec = best;
     double mine = 0.0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
         if (c == (bi >> 6)) mine = pv[c];
-    pb = shfl_f64(mine, bi & 63);
+    pb = readlane_f64(mine, bi & 63);
     b1 = bi;
     v1 = best;
     v2 = sec;
@@ -200,6 +206,8 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < E) {
         w.cnt[i] = 0;
+        w.nlow[i] = 0;
+        w.comp[i] = 1;
         w.pi[i] = w.floor_[i];
     }
     if (i == 0) {
@@ -255,7 +263,8 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
 }
 
 // One block per expert: keep the k best of (current holders + this round's
-// bidders for this expert), return the others to the next bidder list.
+// bidders for this expert), return the others to the next bidder list, and
+// publish the expert's price and its L lowest holders.
 __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
                                                                AucWs w) {
     __shared__ double cb[kResolveCap];
@@ -270,6 +279,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     int32_t* outl = cur ? w.list0 : w.list1;
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
+    const int L = w.L;
     int32_t* stok = w.stok + (int64_t)e * k;
     double* sbid = w.sbid + (int64_t)e * k;
 
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     auto sort_cands = [&](int n) {
         int P = 1;
         while (P < n) P <<= 1;
-        for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = 0x7fffffff; }
+        for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
         __syncthreads();
         for (int size = 2; size <= P; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -338,21 +348,22 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         if (n > kResolveCap - (int)blockDim.x) keep_best(n);
     }
     if (changed) {
-        int n = ncand;
-        if (n >= k) {
-            keep_best(n);
-            n = (int)k;
+        const int n = ncand;
+        keep_best(n);  // sorted best first; at most k kept
+        const int m = (int)min<int64_t>(n, k);
+        for (int i = tid; i < m; i += blockDim.x) { sbid[i] = cb[i]; stok[i] = ct[i]; }
+        // lowest holders in eviction order: slot m-1, m-2, ...
+        const int nl = min(m, L);
+        for (int i = tid; i < nl; i += blockDim.x) {
+            w.lowb[(int64_t)e * L + i] = cb[m - 1 - i];
+            w.lowt[(int64_t)e * L + i] = ct[m - 1 - i];
+            w.lows[(int64_t)e * L + i] = m - 1 - i;
         }
-        for (int i = tid; i < n; i += blockDim.x) { sbid[i] = cb[i]; stok[i] = ct[i]; }
         if (tid == 0) {
-            w.cnt[e] = n;
-            if (n == k) {  // sorted: the lowest holder is last
-                w.pi[e] = cb[k - 1];
-                w.minslot[e] = (int)k - 1;
-                w.mintok[e] = ct[k - 1];
-            } else {
-                w.pi[e] = w.floor_[e];
-            }
+            w.cnt[e] = m;
+            w.nlow[e] = nl;
+            w.comp[e] = (m <= L) ? 1 : 0;
+            w.pi[e] = (m == k) ? cb[k - 1] : w.floor_[e];
         }
     }
     __syncthreads();
@@ -369,154 +380,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     }
 }
 
-// ---------------------------------------------------------------- tail
-
-template <int NCH>
-__global__ __launch_bounds__(kTailThreads) void auc_tail_kernel(const float* s, int64_t T, int64_t E,
-                                                                int64_t k, AucWs w,
-                                                                const ScoreScan* scan, double eps,
-                                                                int phase, int64_t max_bids,
-                                                                AucStatsDev* st) {
-    extern __shared__ char smem[];
-    double* pi = (double*)smem;                 // E
-    double* flo = pi + E;                       // E
-    int32_t* cnt = (int32_t*)(flo + E);         // E
-    int32_t* minslot = cnt + E;                 // E
-    int32_t* mintok = minslot + E;              // E
-    int32_t* lock = mintok + E;                 // E
-    __shared__ int32_t next;
-    __shared__ int32_t stop;
-    __shared__ unsigned long long nbids;
-
-    AucCtl* ctl = w.ctl;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const bool aborted = ctl->abort;
-    const int cur = ctl->cur;
-    const int64_t nb = aborted ? 0 : ctl->nbid[cur];
-    const bool ident = ctl->identity;
-    const int32_t* list = cur ? w.list1 : w.list0;
-    for (int64_t e = tid; e < E; e += blockDim.x) {
-        pi[e] = w.pi[e];
-        flo[e] = w.floor_[e];
-        cnt[e] = w.cnt[e];
-        minslot[e] = w.minslot[e];
-        mintok[e] = w.mintok[e];
-        lock[e] = 0;
-    }
-    if (tid == 0) {
-        next = 0;
-        const unsigned long long before = ctl->bids_total + ctl->bids_phase;
-        stop = (max_bids > 0 && before >= (unsigned long long)max_bids && nb > 0) ? 1 : 0;
-        nbids = 0;
-    }
-    __syncthreads();
-    const Sani sn = read_sani(scan);
-    const unsigned long long cap =
-        max_bids > 0 ? (unsigned long long)max_bids - min<unsigned long long>(
-                           (unsigned long long)max_bids, ctl->bids_total + ctl->bids_phase)
-                     : ~0ull;
-
-    for (;;) {
-        int j = 0;
-        if (lane == 0) j = atomicAdd(&next, 1);
-        j = __shfl(j, 0, 64);
-        if (j >= nb) break;
-        int64_t t = ident ? j : list[j];
-        float v[NCH];
-        load_row<NCH>(s, t, E, lane, sn, v);
-        while (t >= 0) {
-            if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
-            int b1;
-            double v1, v2, pib;
-            for (;;) {
-                best_two<NCH>(v, pi, E, lane, b1, v1, v2, pib);
-                int ok = 0;
-                if (lane == 0) {
-                    int expect = 0;
-                    while (!__hip_atomic_compare_exchange_strong(&lock[b1], &expect, 1, __ATOMIC_ACQUIRE,
-                                                                 __ATOMIC_RELAXED,
-                                                                 __HIP_MEMORY_SCOPE_WORKGROUP)) {
-                        expect = 0;
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                    ok = (pi[b1] == pib);
-                    if (!ok)
-                        __hip_atomic_store(&lock[b1], 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-                ok = __shfl(ok, 0, 64);
-                if (ok) break;
-            }
-            // lane 0 holds lock[b1]; commit the bid
-            const double beta = pib + (v1 - v2) + eps;
-            int32_t* stok = w.stok + (int64_t)b1 * k;
-            double* sbid = w.sbid + (int64_t)b1 * k;
-            int c = 0, slot = 0, victim = -1;
-            if (lane == 0) {
-                c = cnt[b1];
-                if (c < k) {
-                    slot = c;
-                    cnt[b1] = c + 1;
-                } else {
-                    slot = minslot[b1];
-                    victim = mintok[b1];
-                }
-                stok[slot] = (int32_t)t;
-                sbid[slot] = beta;
-            }
-            c = __shfl(c, 0, 64);
-            slot = __shfl(slot, 0, 64);
-            victim = __shfl(victim, 0, 64);
-            if (victim >= 0) load_row<NCH>(s, victim, E, lane, sn, v);  // overlaps the rescan
-            if (c + 1 >= k) {
-                // expert full: find its lowest holder (the new bid substituted)
-                double bm = DBL_MAX;
-                int tm = 0x7fffffff, sm = -1;
-                for (int64_t i = lane; i < k; i += 64) {
-                    double b;
-                    int tk;
-                    if (i == slot) { b = beta; tk = (int)t; }
-                    else { b = sbid[i]; tk = stok[i]; }
-                    if (sm < 0 || evict_first(b, tk, bm, tm)) { bm = b; tm = tk; sm = (int)i; }
-                }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const double ob = shfl_xor_f64(bm, o);
-                    const int ot = __shfl_xor(tm, o, 64);
-                    const int os = __shfl_xor(sm, o, 64);
-                    if (os >= 0 && (sm < 0 || evict_first(ob, ot, bm, tm))) { bm = ob; tm = ot; sm = os; }
-                }
-                if (lane == 0) {
-                    pi[b1] = bm;
-                    minslot[b1] = sm;
-                    mintok[b1] = tm;
-                }
-            }
-            if (lane == 0) {
-                __threadfence_block();
-                __hip_atomic_store(&lock[b1], 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-                const unsigned long long nbd = atomicAdd(&nbids, 1ull) + 1;
-                if (nbd >= cap) stop = 1;
-            }
-            t = victim;
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned long long pb = ctl->bids_phase + nbids;
-        ctl->bids_total += pb;
-        if (phase < 16) {
-            st->bids[phase] = (long long)pb;
-            st->rounds[phase] = ctl->rounds_phase;
-        }
-        st->phases = phase + 1;
-        if (stop && !aborted) st->status = kErrNotConverged;
-    }
-    // every expert is full: its price floor becomes its lowest held bid
-    for (int64_t e = tid; e < E; e += blockDim.x) {
-        w.floor_[e] = (cnt[e] == k) ? pi[e] : flo[e];
-        w.cnt[e] = cnt[e];
-    }
-}
+#include "auction_tail.h"
 
 // ---------------------------------------------------------------- finalize
 
@@ -533,6 +397,14 @@ __global__ void auc_finalize_kernel(AucWs w, int64_t E, int64_t k, int32_t* assi
 // ---------------------------------------------------------------- launcher
 
 template <int NCH>
+static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
+                        const ScoreScan* scan, double eps, int phase, int64_t max_bids,
+                        AucStatsDev* st, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(kTailThreads), lds, stream, s, T, E, k, w,
+                       scan, eps, phase, max_bids, st);
+}
+
+template <int NCH>
 static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_start,
                               double eps_end, double eps_factor, int64_t max_bids,
                               const ScoreScan* scan, int32_t* assign, double* prices,
@@ -543,7 +415,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     const int rounds = (k <= kBulkKMax) ? kBulkRounds : 0;
     int64_t bid_blocks = (T + 15) / 16;
     if (bid_blocks > 2048) bid_blocks = 2048;
-    const size_t tail_lds = (size_t)E * (8 + 8 + 4 * 4);
+    const size_t tail_lds = tail_lds_bytes(E, w.L);
     double eps = eps_start;
     for (int phase = 0;; ++phase) {
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
@@ -554,8 +426,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
                                E, k, w);
         }
-        hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(kTailThreads), tail_lds, stream, s, T,
-                           E, k, w, scan, eps, phase, max_bids, st);
+        launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, tail_lds, stream);
         if (eps <= eps_end) break;
         eps = eps / eps_factor;
         if (eps < eps_end) eps = eps_end;

@@ -78,6 +78,63 @@ BASE_DEV double wave_min_f64(double v) {
     return v;
 }
 
+// ---- DPP cross-lane moves (a few cycles, no LDS crossbar). Lanes whose
+// source is outside the row keep their own value.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16
+constexpr int kDppShl1 = 0x101;       // lane i <- i+1 within a row of 16
+constexpr int kDppShr1 = 0x111;       // lane i <- i-1 within a row of 16
+constexpr int kDppRowBcast0 = 0x150;  // every lane <- lane 0 of its row of 16
+
+template <int CTRL>
+BASE_DEV int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+BASE_DEV double dpp_f64(double v) {
+    long long x = __double_as_longlong(v);
+    int lo = dpp_i32<CTRL>((int)(x & 0xffffffff));
+    int hi = dpp_i32<CTRL>((int)(x >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+BASE_DEV int readlane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+BASE_DEV double readlane_f64(double v, int l) {
+    long long x = __double_as_longlong(v);
+    int lo = __builtin_amdgcn_readlane((int)(x & 0xffffffff), l);
+    int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+BASE_DEV int first_lane_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// (value, index) pairs: a replaces b if larger, or equal with a lower index.
+BASE_DEV void argmax_merge(double& v, int& i, double ov, int oi) {
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+// Wave-wide argmax (lowest index among equal maxima); result is uniform.
+BASE_DEV void wave_argmax_f64(double& v, int& i) {
+    argmax_merge(v, i, dpp_f64<kDppXor1>(v), dpp_i32<kDppXor1>(i));
+    argmax_merge(v, i, dpp_f64<kDppXor2>(v), dpp_i32<kDppXor2>(i));
+    argmax_merge(v, i, dpp_f64<kDppHalfMirror>(v), dpp_i32<kDppHalfMirror>(i));
+    argmax_merge(v, i, dpp_f64<kDppMirror>(v), dpp_i32<kDppMirror>(i));
+    double bv = readlane_f64(v, 0);
+    int bi = readlane_i32(i, 0);
+    argmax_merge(bv, bi, readlane_f64(v, 16), readlane_i32(i, 16));
+    argmax_merge(bv, bi, readlane_f64(v, 32), readlane_i32(i, 32));
+    argmax_merge(bv, bi, readlane_f64(v, 48), readlane_i32(i, 48));
+    v = bv;
+    i = bi;
+}
+BASE_DEV double wave_max_f64(double v) {
+    v = fmax(v, dpp_f64<kDppXor1>(v));
+    v = fmax(v, dpp_f64<kDppXor2>(v));
+    v = fmax(v, dpp_f64<kDppHalfMirror>(v));
+    v = fmax(v, dpp_f64<kDppMirror>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
+                fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 // Exact GELU x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), fp32.
 BASE_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 

@@ -141,7 +141,7 @@ def test_auction_certificates_small(c, eps):
 
 
 @pytest.mark.parametrize("T,E,seed", [(512, 8, 0), (768, 12, 1), (1024, 4, 2), (600, 2, 3),
-                                      (256, 1, 4), (64, 64, 5)])
+                                      (256, 1, 4), (64, 64, 5), (1600, 200, 6), (1200, 300, 7)])
 def test_auction_bit_exact_below_gap(T, E, seed):
     rng = np.random.default_rng(1000 + seed)
     s32 = rng.standard_normal((T, E)).astype(np.float32)
