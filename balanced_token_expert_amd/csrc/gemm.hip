@@ -9,10 +9,12 @@
 //             out[t] = sigmoid(s[t][e]) * Y_e[i] + h[t], t = perm[e*k+i]
 //             (fig. 2's inverse sort fused into the stores)
 //
-// bf16 path: 64-wide waves issue v_mfma_f32_32x32x16_bf16 on tiles staged
-// through LDS (double-buffered, one barrier per 64-deep K step); fp32
-// accumulation. The block -> tile map keeps the tiles that share a weight
-// tile on one XCD (consecutive logical tiles land on the same L2).
+// bf16 path: 64-wide waves issue v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation. The expert products use 256 x 256 tiles fed through a
+// 4-stage LDS pipeline of direct global->LDS loads (gemm_dma.h); the affinity
+// uses a register-staged, double-buffered 128-row tile. The block -> tile map
+// keeps the tiles that share a weight tile on one XCD (consecutive logical
+// tiles land on the same L2).
 // fp32 path: a plain LDS-tiled FMA kernel (exact fp32 products).
 #include "common.h"
 #include "internal.h"
@@ -47,6 +49,10 @@ BASE_DEV int64_t xcd_logical(int64_t pid, int64_t nblk) {
 }
 
 BASE_DEV float apply_act(float v, int act) { return act ? gelu_erf(v) : fmaxf(v, 0.0f); }
+
+template <int Kind, int TM, int TN>
+BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g, int64_t mw,
+                         int64_t nw, int lane);
 
 // ---------------------------------------------------------------- bf16 MFMA
 
@@ -160,15 +166,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
         __syncthreads();
     }
 
-    // ---- epilogue. acc[i][j][r] is C[row][col] with
-    //   row = wm*WTM + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = wn*WTN + j*32 + lane%32
+    store_tile<Kind, TM, TN>(p, acc, g, m0 + wm * WTM, n0 + wn * WTN, lane);
+}
+
+#include "gemm_dma.h"
+
+// ---- epilogue of one wave's TM x TN block of 32x32 MFMA tiles, whose first
+// output row and column are mw and nw. acc[i][j][r] is C[row][col] with
+//   row = mw + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = nw + j*32 + lane%32
+template <int Kind, int TM, int TN>
+BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g, int64_t mw,
+                         int64_t nw, int lane) {
     uint32_t kmin = 0xffffffffu;
     int nonfin = 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int64_t m = mw + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             if (m >= p.M) continue;
             int64_t t = 0;
             float gate = 0.0f;
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+                const int64_t n = nw + j * 32 + (lane & 31);
                 if (n >= p.N) continue;
                 const float v = acc[i][j][r];
                 if (Kind == KIND_AFF) {
@@ -315,6 +330,16 @@ static hipError_t run_bf16(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int Kind, int BN, int WM, int WN>
+static hipError_t run_dma(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN) * p.groups;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<Kind, BN, WM, WN>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, st, p);
+    return hipGetLastError();
+}
+
 template <int Kind>
 static hipError_t run_f32(const GemmParams& p, hipStream_t st) {
     const int64_t tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64) * p.groups;
@@ -340,7 +365,7 @@ hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1, void*
     p.A = h; p.B = W1; p.M = k; p.N = F; p.K = D; p.groups = E;
     p.perm = perm; p.b_gstride = F * D; p.H = H; p.act = act;
     if (dt == 0) return run_f32<KIND_FFN1>(p, st);
-    return run_bf16<KIND_FFN1, 128, 128, 2, 2>(p, st);
+    return run_dma<KIND_FFN1, 256, 4, 2>(p, st);
 }
 
 hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const float* s,
@@ -350,7 +375,9 @@ hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const
     p.A = H; p.B = W2; p.M = k; p.N = D; p.K = F; p.groups = E;
     p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
     if (dt == 0) return run_f32<KIND_FFN2>(p, st);
-    return run_bf16<KIND_FFN2, 128, 128, 2, 2>(p, st);
+    // 256-wide tiles unless that leaves under two workgroups per CU
+    if (((D + 255) / 256) * ((k + 255) / 256) * E >= 512) return run_dma<KIND_FFN2, 256, 4, 2>(p, st);
+    return run_dma<KIND_FFN2, 128, 4, 2>(p, st);
 }
 
 }  // namespace base
