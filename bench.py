@@ -182,6 +182,25 @@ def auction_solve(reps=10):
             "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1}
 
 
+def copy_probe(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per
+    launch): the reference point that scales the HBM byte counters of a
+    profiler run (FETCH_SIZE / WRITE_SIZE) to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_bytes_each_way": nbytes, "ms": round(ms, 4),
+                      "GB/s_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +209,7 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-auction", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (every expert resident on one "
@@ -200,6 +220,9 @@ def main():
     from balanced_token_expert_amd import api
     from balanced_token_expert_amd import workloads as W
 
+    if args.copy_probe:
+        copy_probe()
+        return
     api.load()
     torch.cuda.init()
     wl = W.workload(args.workload)
