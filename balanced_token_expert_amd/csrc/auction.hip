@@ -23,12 +23,13 @@
 //     prices at once (one wave per token, wave-level max/second-max); then one
 //     workgroup per expert keeps the k best of its holders and new bidders
 //     (bitonic sort in LDS) and returns the rest to the bidder list.
-//   tail (one persistent workgroup, 16 waves): once few tokens are left, each
-//     wave follows a displacement chain -- bid, take the expert's lock in LDS,
-//     evict its lowest holder, continue with the evicted token. Prices, counts
-//     and, per expert, a sorted list of its L lowest holders live in LDS, so
-//     an eviction and the new price need no memory round trip; the list is
-//     rebuilt from the expert's slots in global memory only when it runs dry.
+//   tail (one persistent workgroup): once few tokens are left, each wave
+//     follows a displacement chain -- bid, take the expert's lock in LDS,
+//     evict its lowest holder, continue with the evicted token. Prices,
+//     counts and, per expert, a sorted list of its L lowest holders live in
+//     LDS, so a step needs one score-row load (often from an LDS cache) plus
+//     LDS work; the list is rebuilt from the expert's slots in global memory
+//     only when it runs dry.
 // Prices and bids are fp64: exactness needs eps below gap/T, far below fp32
 // resolution at prices of order one.
 #include <float.h>
@@ -38,11 +39,10 @@
 
 namespace base {
 
-constexpr int kBulkRounds = 6;       // multi-CU rounds per phase (at most)
-constexpr int kTailMax = 1024;       // bidders left when the tail takes over
+constexpr int kBulkRounds = 32;      // multi-CU rounds per phase (at most)
+constexpr int kTailMax = 64;         // bidders left when the tail takes over
 constexpr int kResolveCap = 4096;    // candidates sorted at once per expert
 constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
-constexpr int kTailThreads = 1024;
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
 constexpr int32_t kNoTok = 0x7fffffff;
@@ -141,44 +141,56 @@ BASE_DEV void load_row(const float* s, int64_t t, int64_t E, int lane, Sani sn, 
 }
 
 // Best expert (lowest id on ties), best value and the best value over the
-// other experts, of s[t][e] - pi[e], reduced over the wave. pb returns the
-// price of b1 exactly as used for v1 (prices in LDS may be raised by other
-// waves meanwhile; the bid must use one consistent value).
+// other experts, of s[t][e] - pi[e], reduced over the wave: two wave-wide
+// maxima, the best expert found by ballots. pb returns the price of b1
+// exactly as used for v1 (prices in LDS may be raised by other waves
+// meanwhile; the bid must use one consistent value).
 template <int NCH, typename PiT>
 BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& b1, double& v1,
                        double& v2, double& pb) {
     double val[NCH], pv[NCH];
     double best = -DBL_MAX;
-    int bi = kNoTok;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = lane + 64 * c;
+        val[c] = -DBL_MAX;
         pv[c] = 0.0;
         if (e < E) {
             pv[c] = pi[e];
             val[c] = (double)v[c] - pv[c];
-            if (bi == kNoTok || val[c] > best) { best = val[c]; bi = e; }
-        } else {
-            val[c] = -DBL_MAX;
+            best = fmax(best, val[c]);
         }
     }
-    wave_argmax_f64(best, bi);  // uniform from here on
+    const double vmax = wave_max_f64(best);
+    int bi = -1;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const unsigned long long m = __ballot(lane + 64 * c < E && val[c] == vmax);
+        if (bi < 0 && m) bi = 64 * c + __builtin_ctzll(m);
+    }
     double sec = -DBL_MAX;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = lane + 64 * c;
-        if (e < E && e != bi && val[c] > sec) sec = val[c];
+        if (e < E && e != bi) sec = fmax(sec, val[c]);
     }
     sec = wave_max_f64(sec);
-    if (E == 1) sec = best;
+    if (E == 1) sec = vmax;
     double mine = 0.0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
         if (c == (bi >> 6)) mine = pv[c];
-    pb = readlane_f64(mine, bi & 63);
     b1 = bi;
-    v1 = best;
+    v1 = vmax;
     v2 = sec;
+    pb = readlane_f64(mine, bi & 63);
+}
+
+// The bid beta = pb + (v1 - v2) + eps. It is at least the next double above
+// pb, so a bid always outbids the price it was made against even where eps
+// is below the resolution of the prices (then eps is effectively larger).
+BASE_DEV double bid_amount(double pb, double v1, double v2, double eps) {
+    return fmax(pb + (v1 - v2) + eps, nextafter(pb, DBL_MAX));
 }
 
 // a is evicted before b: lower bid, or equal bid and higher token id
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
         best_two<NCH>(v, w.pi, E, lane, b1, v1, v2, pb);
         if (lane == 0) {
             w.bexp[t] = b1;
-            w.bval[t] = pb + (v1 - v2) + eps;
+            w.bval[t] = bid_amount(pb, v1, v2, eps);
         }
         ++mine;
     }
@@ -400,7 +412,7 @@ template <int NCH>
 static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
                         AucStatsDev* st, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(kTailThreads), lds, stream, s, T, E, k, w,
+    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(tail_threads(NCH)), lds, stream, s, T, E, k, w,
                        scan, eps, phase, max_bids, st);
 }
 
@@ -415,7 +427,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     const int rounds = (k <= kBulkKMax) ? kBulkRounds : 0;
     int64_t bid_blocks = (T + 15) / 16;
     if (bid_blocks > 2048) bid_blocks = 2048;
-    const size_t tail_lds = tail_lds_bytes(E, w.L);
+    const size_t tail_lds = tail_lds_bytes(E, w.L, tail_threads(NCH));
     double eps = eps_start;
     for (int phase = 0;; ++phase) {
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,

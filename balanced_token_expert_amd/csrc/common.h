@@ -87,6 +87,8 @@ constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16
 constexpr int kDppShl1 = 0x101;       // lane i <- i+1 within a row of 16
 constexpr int kDppShr1 = 0x111;       // lane i <- i-1 within a row of 16
 constexpr int kDppRowBcast0 = 0x150;  // every lane <- lane 0 of its row of 16
+constexpr int kDppBcast15 = 0x142;    // row r <- lane 15 of row r-1 (rows in the row mask)
+constexpr int kDppBcast31 = 0x143;    // rows 2, 3 <- lane 31 (rows in the row mask)
 
 template <int CTRL>
 BASE_DEV int dpp_i32(int v) {
@@ -97,6 +99,18 @@ BASE_DEV double dpp_f64(double v) {
     long long x = __double_as_longlong(v);
     int lo = dpp_i32<CTRL>((int)(x & 0xffffffff));
     int hi = dpp_i32<CTRL>((int)(x >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+// rows outside ROW_MASK keep v
+template <int CTRL, int ROW_MASK>
+BASE_DEV int dpp_rows_i32(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+BASE_DEV double dpp_rows_f64(double v) {
+    long long x = __double_as_longlong(v);
+    int lo = dpp_rows_i32<CTRL, ROW_MASK>((int)(x & 0xffffffff));
+    int hi = dpp_rows_i32<CTRL, ROW_MASK>((int)(x >> 32));
     return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 BASE_DEV int readlane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
@@ -126,13 +140,25 @@ BASE_DEV void wave_argmax_f64(double& v, int& i) {
     v = bv;
     i = bi;
 }
+// Wave-wide max: reduce within each row of 16, then carry the row maxima up
+// with row broadcasts; lane 63 ends with the maximum (returned uniform).
 BASE_DEV double wave_max_f64(double v) {
     v = fmax(v, dpp_f64<kDppXor1>(v));
     v = fmax(v, dpp_f64<kDppXor2>(v));
     v = fmax(v, dpp_f64<kDppHalfMirror>(v));
     v = fmax(v, dpp_f64<kDppMirror>(v));
-    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
-                fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+    v = fmax(v, dpp_rows_f64<kDppBcast15, 0xA>(v));
+    v = fmax(v, dpp_rows_f64<kDppBcast31, 0xC>(v));
+    return readlane_f64(v, 63);
+}
+BASE_DEV int wave_min_i32(int v) {
+    v = min(v, dpp_i32<kDppXor1>(v));
+    v = min(v, dpp_i32<kDppXor2>(v));
+    v = min(v, dpp_i32<kDppHalfMirror>(v));
+    v = min(v, dpp_i32<kDppMirror>(v));
+    v = min(v, dpp_rows_i32<kDppBcast15, 0xA>(v));
+    v = min(v, dpp_rows_i32<kDppBcast31, 0xC>(v));
+    return readlane_i32(v, 63);
 }
 
 // Exact GELU x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), fp32.
