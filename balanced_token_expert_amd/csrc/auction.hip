@@ -39,7 +39,7 @@
 
 namespace base {
 
-constexpr int kBulkRounds = 32;      // multi-CU rounds per phase (at most)
+constexpr int kBulkRounds = 16;      // multi-CU rounds per phase (at most)
 constexpr int kTailMax = 64;         // bidders left when the tail takes over
 constexpr int kResolveCap = 4096;    // candidates sorted at once per expert
 constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
@@ -276,12 +276,25 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
 
 // One block per expert: keep the k best of (current holders + this round's
 // bidders for this expert), return the others to the next bidder list, and
-// publish the expert's price and its L lowest holders.
+// publish the expert's price and its L lowest holders. The holders are kept
+// sorted best first (bid descending, then token ascending) in the expert's
+// slots across the bulk rounds of a phase, so a round sorts only its new
+// bidders and merges by rank: a holder's new position is its old one plus
+// the number of bidders better than it, a bidder's is its position among the
+// bidders plus the number of holders better than it (binary searches).
+// Bidders are gathered kResolveCap at a time; a full buffer is merged before
+// the scan goes on.
+BASE_DEV bool better(double ba, int ta, double bb, int tb) { return ba > bb || (ba == bb && ta < tb); }
+
 __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
                                                                AucWs w) {
-    __shared__ double cb[kResolveCap];
+    __shared__ double cb[kResolveCap];   // bidders
     __shared__ int32_t ct[kResolveCap];
-    __shared__ int32_t ncand;
+    __shared__ double hb[kBulkKMax];     // holders, best first
+    __shared__ int32_t ht[kBulkKMax];
+    __shared__ double ob[kBulkKMax];     // merged
+    __shared__ int32_t ot[kBulkKMax];
+    __shared__ int32_t ncand, nhold;
     AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->bulk_done) return;
     const int cur = ctl->cur;
@@ -295,8 +308,19 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     int32_t* stok = w.stok + (int64_t)e * k;
     double* sbid = w.sbid + (int64_t)e * k;
 
-    // sort cb/ct[0..n) best first: bid descending, then token ascending
-    auto sort_cands = [&](int n) {
+    // append the token of each thread with rej set to the next bidder list
+    auto reject = [&](bool rej, int tok) {
+        const unsigned long long m = __ballot(rej);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(&ctl->nbid[cur ^ 1], (int)__popcll(m));
+        base = __shfl(base, 0, 64);
+        if (rej) {
+            const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+            outl[base + __popcll(m & below)] = tok;
+        }
+    };
+    // merge the n gathered bidders into the holders
+    auto merge = [&](int n) {
         int P = 1;
         while (P < n) P <<= 1;
         for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
@@ -309,8 +333,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
                     const bool best_first = ((lo & size) == 0);
                     const double b0 = cb[lo], b1 = cb[hi];
                     const int t0 = ct[lo], t1 = ct[hi];
-                    const bool hi_better = b1 > b0 || (b1 == b0 && t1 < t0);
-                    if (hi_better == best_first) {
+                    if (better(b1, t1, b0, t0) == best_first) {
                         cb[lo] = b1; cb[hi] = b0;
                         ct[lo] = t1; ct[hi] = t0;
                     }
@@ -318,30 +341,53 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
                 __syncthreads();
             }
         }
-    };
-    // sort, send entries [k, n) to the next bidder list, keep min(n, k)
-    auto keep_best = [&](int n) {
-        sort_cands(n);
-        for (int i0 = (int)k; i0 < n; i0 += blockDim.x) {
+        const int c = nhold;
+        // holder i moves to i + (bidders better than it)
+        for (int i0 = 0; i0 < c; i0 += blockDim.x) {
             const int i = i0 + tid;
-            const bool r = i < n;
-            const unsigned long long m = __ballot(r);
-            int base = 0;
-            if (lane == 0 && m) base = atomicAdd(&ctl->nbid[cur ^ 1], (int)__popcll(m));
-            base = __shfl(base, 0, 64);
-            if (r) {
-                const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-                outl[base + __popcll(m & below)] = ct[i];
+            bool rej = false;
+            int tok = 0;
+            if (i < c) {
+                int lo = 0, hi = n;  // first bidder not better than holder i
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (better(cb[mid], ct[mid], hb[i], ht[i])) lo = mid + 1;
+                    else hi = mid;
+                }
+                const int r = i + lo;
+                if (r < k) { ob[r] = hb[i]; ot[r] = ht[i]; }
+                else { rej = true; tok = ht[i]; }
             }
+            reject(rej, tok);
+        }
+        // bidder j moves to j + (holders better than it)
+        for (int j0 = 0; j0 < n; j0 += blockDim.x) {
+            const int j = j0 + tid;
+            bool rej = false;
+            int tok = 0;
+            if (j < n) {
+                int lo = 0, hi = c;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (better(hb[mid], ht[mid], cb[j], ct[j])) lo = mid + 1;
+                    else hi = mid;
+                }
+                const int r = j + lo;
+                if (r < k) { ob[r] = cb[j]; ot[r] = ct[j]; }
+                else { rej = true; tok = ct[j]; }
+            }
+            reject(rej, tok);
         }
         __syncthreads();
-        if (tid == 0) ncand = (int)min<int64_t>(n, k);
+        const int c2 = (int)min<int64_t>(c + n, k);
+        for (int i = tid; i < c2; i += blockDim.x) { hb[i] = ob[i]; ht[i] = ot[i]; }
+        if (tid == 0) { nhold = c2; ncand = 0; }
         __syncthreads();
     };
 
     const int c0 = w.cnt[e];
-    for (int i = tid; i < c0; i += blockDim.x) { cb[i] = sbid[i]; ct[i] = stok[i]; }
-    if (tid == 0) ncand = c0;
+    for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
+    if (tid == 0) { ncand = 0; nhold = c0; }
     __syncthreads();
     bool changed = false;
     for (int64_t j0 = 0; j0 < nb; j0 += blockDim.x) {
@@ -356,26 +402,25 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         }
         __syncthreads();
         const int n = ncand;
-        changed = changed || n != c0;
-        if (n > kResolveCap - (int)blockDim.x) keep_best(n);
+        changed = changed || n > 0;
+        if (n > kResolveCap - (int)blockDim.x) merge(n);
     }
+    if (ncand > 0) merge(ncand);
     if (changed) {
-        const int n = ncand;
-        keep_best(n);  // sorted best first; at most k kept
-        const int m = (int)min<int64_t>(n, k);
-        for (int i = tid; i < m; i += blockDim.x) { sbid[i] = cb[i]; stok[i] = ct[i]; }
+        const int m = nhold;
+        for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
         // lowest holders in eviction order: slot m-1, m-2, ...
         const int nl = min(m, L);
         for (int i = tid; i < nl; i += blockDim.x) {
-            w.lowb[(int64_t)e * L + i] = cb[m - 1 - i];
-            w.lowt[(int64_t)e * L + i] = ct[m - 1 - i];
+            w.lowb[(int64_t)e * L + i] = hb[m - 1 - i];
+            w.lowt[(int64_t)e * L + i] = ht[m - 1 - i];
             w.lows[(int64_t)e * L + i] = m - 1 - i;
         }
         if (tid == 0) {
             w.cnt[e] = m;
             w.nlow[e] = nl;
             w.comp[e] = (m <= L) ? 1 : 0;
-            w.pi[e] = (m == k) ? cb[k - 1] : w.floor_[e];
+            w.pi[e] = (m == k) ? hb[k - 1] : w.floor_[e];
         }
     }
     __syncthreads();
@@ -433,7 +478,9 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
                            stream, w, T, E, st);
         for (int r = 0; r < rounds; ++r) {
-            hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3((unsigned)bid_blocks), dim3(256), 0,
+            // round 0: every token bids; later rounds: the returned few
+            const unsigned nblk = (unsigned)(r == 0 ? bid_blocks : (bid_blocks < 256 ? bid_blocks : 256));
+            hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3(nblk), dim3(256), 0,
                                stream, s, T, E, w, scan, r, eps);
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
                                E, k, w);

@@ -234,6 +234,20 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
         max_bids > 0 ? (unsigned long long)max_bids - min<unsigned long long>(
                            (unsigned long long)max_bids, ctl->bids_total + ctl->bids_phase)
                      : ~0ull;
+    // fill the row cache with every expert's lowest holder (its next victim)
+    if (cache) {
+        for (int64_t e = wave; e < E; e += kThreads / 64) {
+            if (first_lane_i32(nlow[e]) == 0) continue;
+            const int h = first_lane_i32(lowt[e * L]);
+            float r[NCH];
+            load_row<NCH>(s, h, E, lane, sn, r);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                if (lane + 64 * c < E) rowc[e * E + lane + 64 * c] = r[c];
+            if (lane == 0) rowtag[e] = h;
+        }
+        __syncthreads();
+    }
     double* xb = rbx_b + wave * 64;
     int32_t* xt = rbx_t + wave * 64;
     int32_t* xs = rbx_s + wave * 64;
@@ -257,12 +271,6 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
         int fr = -1;  // expert t was just evicted from
         while (t >= 0) {
             if (first_lane_i32(stop)) break;
-            // the slot store of the previous step has landed once this returns
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (pending >= 0) {
-                lds_count(&st_done[pending], lane);
-                pending = -1;
-            }
             // the row: from the cache when the tag names t before and after
             float v[NCH];
             bool hit = false;
@@ -280,8 +288,11 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                         if (lane == 0) rowtag[cpe] = -1;
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                        for (int c = 0; c < NCH; ++c)
-                            if (lane + 64 * c < E) rowc[cpe * E + lane + 64 * c] = cpv[c];
+                        for (int c = 0; c < NCH; ++c) {
+                            float x = cpv[c];
+                            if (sn.fix && !is_finite_f32(x)) x = sn.repl;
+                            if (lane + 64 * c < E) rowc[cpe * E + lane + 64 * c] = x;
+                        }
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                         if (lane == 0) rowtag[cpe] = cpt;
                     }
@@ -294,6 +305,13 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                 double v1, v2, pb;
                 best_two<NCH>(v, pi, E, lane, e, v1, v2, pb);
                 const double beta = bid_amount(pb, v1, v2, eps);
+                // the slot store of the previous step has landed once this
+                // returns; it is counted before this wave waits for any lock
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (pending >= 0) {
+                    lds_count(&st_done[pending], lane);
+                    pending = -1;
+                }
                 lds_lock(&lock[e], lane);
                 // ---- under the lock of e
                 const int64_t eb = (int64_t)e * L;
@@ -385,7 +403,11 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
 #pragma unroll
                         for (int cc = 0; cc < NCH; ++cc) cpv[cc] = v[cc];
                     } else {
-                        load_row<NCH>(s, head1, E, lane, sn, cpv);
+                        // raw load (sanitized when published): nothing waits for it here
+                        const float* row = s + (int64_t)head1 * E;
+#pragma unroll
+                        for (int cc = 0; cc < NCH; ++cc)
+                            cpv[cc] = (lane + 64 * cc < E) ? row[lane + 64 * cc] : 0.0f;
                     }
                 }
                 lds_unlock(&lock[e], lane);
