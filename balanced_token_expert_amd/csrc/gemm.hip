@@ -216,7 +216,9 @@ BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g
             nonfin += __shfl_xor(nonfin, o, 64);
         }
         if (lane == 0 && p.scan) {
-            if (kmin != 0xffffffffu) atomicMin(&p.scan->min_key, kmin);
+            if (kmin != 0xffffffffu &&
+                kmin < __hip_atomic_load(&p.scan->min_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                atomicMin(&p.scan->min_key, kmin);
             if (nonfin) atomicAdd(&p.scan->nonfinite, (uint32_t)nonfin);
         }
     }
@@ -312,7 +314,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
             nonfin += __shfl_xor(nonfin, o, 64);
         }
         if (lane == 0 && p.scan) {
-            if (kmin != 0xffffffffu) atomicMin(&p.scan->min_key, kmin);
+            if (kmin != 0xffffffffu &&
+                kmin < __hip_atomic_load(&p.scan->min_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                atomicMin(&p.scan->min_key, kmin);
             if (nonfin) atomicAdd(&p.scan->nonfinite, (uint32_t)nonfin);
         }
     }

@@ -24,6 +24,7 @@ __global__ void scan_init_kernel(ScoreScan* scan) {
 }
 
 __global__ __launch_bounds__(256) void scan_scores_kernel(const float* s, int64_t n, ScoreScan* scan) {
+    __shared__ uint32_t wmin[4], wbad[4];
     uint32_t kmin = 0xffffffffu;
     uint32_t bad = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -47,8 +48,15 @@ __global__ __launch_bounds__(256) void scan_scores_kernel(const float* s, int64_
         kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
         bad += (uint32_t)__shfl_xor((int)bad, o, 64);
     }
-    if ((threadIdx.x & 63) == 0) {
-        if (kmin != 0xffffffffu) atomicMin(&scan->min_key, kmin);
+    // one atomic per block, and only when it can lower the minimum (many
+    // blocks hitting one address serialise at the L2)
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { wmin[wv] = kmin; wbad[wv] = bad; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int q = 1; q < (int)(blockDim.x >> 6); ++q) { kmin = min(kmin, wmin[q]); bad += wbad[q]; }
+        if (kmin < __hip_atomic_load(&scan->min_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMin(&scan->min_key, kmin);
         if (bad) atomicAdd(&scan->nonfinite, bad);
     }
 }
@@ -74,7 +82,7 @@ hipError_t launch_scan_init(ScoreScan* scan, hipStream_t st) {
 hipError_t launch_scan_scores(const float* s, int64_t n, ScoreScan* scan, hipStream_t st) {
     int64_t blocks = (n / 4 + 255) / 256;
     if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(scan_scores_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, n, scan);
     return hipGetLastError();
 }

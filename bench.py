@@ -36,6 +36,41 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PHASES = ("affinity", "route", "ffn1", "ffn2")
 
+# HBM bytes per launch of the expert products at the large workload, from
+# two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+# scaled by what the same counters read for a 1 GiB copy (--copy-probe):
+# fetched = FETCH_SIZE * 1024 * FETCH_SCALE, written = WRITE_SIZE * 1024.
+# They describe the kernel built from the sources whose hash is recorded;
+# after any change to those sources the figure is stale and reported as null.
+TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
+                   "balanced_token_expert_amd/csrc/gemm_dma.h",
+                   "balanced_token_expert_amd/csrc/common.h")
+FETCH_SCALE = 1.99994
+WRITE_SCALE = 1.0
+MEASURED_TRAFFIC = {
+    # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "ffn1": ("large_t64k_e128_d2048", None, 2367059.5, 1048576.0),
+    "ffn2": ("large_t64k_e128_d2048", None, 2809011.4, 262162.5),
+}
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the recorded counters, or None when they
+    were taken on another workload or on different kernel sources."""
+    rec = MEASURED_TRAFFIC.get(kernel)
+    if rec is None or rec[0] != workload or rec[1] != sources_sha256():
+        return None
+    return rec[2] * 1024 * FETCH_SCALE + rec[3] * 1024 * WRITE_SCALE
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -102,7 +137,7 @@ def stack_dev(parts, dtype="bf16"):
     return out
 
 
-def cpu_baseline(wl, h, w, W1, W2, sample_experts=8):
+def cpu_baseline(wl, h, w, W1, W2, sample_experts=48):
     """The oracle as it stands, on a bounded sample: affinities, CPU auction
     and greedy routing over all T tokens; the fp64 layer forward for the
     tokens of `sample_experts` experts. Scaled to tokens/s of the full step."""
@@ -177,7 +212,7 @@ def auction_solve(reps=10):
     return {"value": round(float(np.median(times)), 4), "unit": "ms", "workload": wl.name,
             "eps": f"{wl.eps_start}->{wl.eps_end} x1/{wl.eps_factor}", "reps": reps,
             "min_ms": round(float(np.min(times)), 4), "status": st.status,
-            "bids_per_phase": st.bids, "bulk_rounds_per_phase": st.rounds,
+            "bids_per_phase": st.bids, "rounds_per_phase": st.rounds,
             "balanced": balanced, "dual_gap": gap, "dual_gap_bound": T * wl.eps_end,
             "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1}
 
@@ -291,16 +326,19 @@ def main():
     gcount = gr["counts"].cpu().numpy()
 
     # roofline of the dominant kernel (one launch per phase for the products)
+    # the dominant kernel: the longest single launch of the step (an expert
+    # product; the auction is many short latency-bound launches)
     flops_ffn = 2.0 * T * D * F
     kern = max(("ffn1", "ffn2"), key=lambda p: avg[p])
     achieved = flops_ffn / (avg[kern] * 1e-3) / 1e12
+    traffic = measured_traffic(kern, wl.name)
     roof = {"kernel": f"{kern} (expert GEMM {'1' if kern == 'ffn1' else '2'}, "
                       f"{E} experts x [{T // E}x{D if kern == 'ffn1' else F}]"
                       f"x[{D if kern == 'ffn1' else F}x{F if kern == 'ffn1' else D}])",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "algorithmic_flops": flops_ffn,
-            "avg_launch_ms": round(avg[kern], 4)}
+            "traffic": None if traffic is None else round(traffic),
+            "algorithmic_flops": flops_ffn, "avg_launch_ms": round(avg[kern], 4)}
 
     res = {"metric": "BASE layer fwd tokens/s at 1 GPU + auction solve ms (T=16k, E=128)",
            "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -312,7 +350,7 @@ def main():
                                "same scores", "parallelism": "single GPU, all experts resident"},
            "phase_ms": {p: round(v, 4) for p, v in avg.items()},
            "auction": {"status": st.status, "bids_per_phase": st.bids,
-                       "bulk_rounds_per_phase": st.rounds, "balanced": balanced},
+                       "rounds_per_phase": st.rounds, "balanced": balanced},
            "greedy_load": {"max_over_mean": round(float(gcount.max() / (T / E)), 3),
                            "max_share": round(float(gcount.max() / T), 5),
                            "uniform_share": round(1.0 / E, 5)},

@@ -96,9 +96,9 @@ typedef struct {
 /* Written by the device (a DEVICE pointer); read it after the stream has
  * reached the call. status is BASE_OK or BASE_ERR_NOT_CONVERGED /
  * BASE_ERR_NONFINITE / BASE_ERR_UNBALANCED. bids[p] counts the bids of eps
- * phase p (p < 16); rounds[p] counts that phase's parallel bidding rounds
- * (all unassigned tokens bidding at once) before the remaining displacement
- * chains were finished one bid at a time per chain. */
+ * phase p (p < 16); rounds[p] is that phase's sequential depth: its parallel
+ * bidding rounds (all unassigned tokens bidding at once) plus the number of
+ * bids in the longest displacement chain finished after them. */
 typedef struct {
     int32_t status;
     int32_t phases;
@@ -163,8 +163,8 @@ int base_assign_auction(const float *scores, int64_t T, int64_t E,
 /*
  * base_route_greedy -- test-time routing (sec. 3.2.2): a_t = the expert with
  * the highest score, the lowest expert id among equal scores (scores
- * sanitised as in base_assign_auction; all non-finite -> every token to
- * expert 0 and stats-free status is not reported).
+ * sanitised as in base_assign_auction; if no score is finite every token
+ * goes to expert 0 -- this entry point has no status output).
  *   assign[T], counts[E] (tokens per expert), perm[T] (grouped by expert,
  *   ascending token id within a group), offsets[E+1] (prefix sums of
  *   counts). Any of counts/perm/offsets may be NULL to skip it (perm and
