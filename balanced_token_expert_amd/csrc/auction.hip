@@ -141,40 +141,61 @@ BASE_DEV void load_row(const float* s, int64_t t, int64_t E, int lane, Sani sn, 
 }
 
 // Best expert (lowest id on ties), best value and the best value over the
-// other experts, of s[t][e] - pi[e], reduced over the wave: two wave-wide
-// maxima, the best expert found by ballots. pb returns the price of b1
-// exactly as used for v1 (prices in LDS may be raised by other waves
-// meanwhile; the bid must use one consistent value).
-template <int NCH, typename PiT>
-BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& b1, double& v1,
-                       double& v2, double& pb) {
-    double val[NCH], pv[NCH];
-    double best = -DBL_MAX;
+// other experts, of s[t][e] - pi[e], reduced over the wave in one pass: each
+// lane keeps its top two values and the pairs are merged by DPP (row steps,
+// then row broadcasts; lane 63 ends with the wave's pair); the best expert is
+// then found by ballots. pb returns the price of b1 exactly as used for v1
+// (prices in LDS may be raised by other waves meanwhile; the bid must use one
+// consistent value).
+BASE_DEV void top2_merge(double& m1, double& m2, double o1, double o2) {
+    const double hi = fmax(m1, o1), lo = fmin(m1, o1);
+    m2 = fmax(lo, fmax(m2, o2));
+    m1 = hi;
+}
+template <int CTRL>
+BASE_DEV void top2_step(double& m1, double& m2) {
+    top2_merge(m1, m2, dpp_f64<CTRL>(m1), dpp_f64<CTRL>(m2));
+}
+template <int CTRL, int ROWS>
+BASE_DEV void top2_rows(double& m1, double& m2) {
+    // rows outside ROWS see their own pair, which merges to itself only if
+    // it is not counted twice: keep them unchanged
+    const double o1 = dpp_rows_f64<CTRL, ROWS>(m1), o2 = dpp_rows_f64<CTRL, ROWS>(m2);
+    double n1 = m1, n2 = m2;
+    top2_merge(n1, n2, o1, o2);
+    const int row = (int)(__lane_id() >> 4);
+    if ((ROWS >> row) & 1) { m1 = n1; m2 = n2; }
+}
+
+// core of best_two: the prices of this lane's experts (lane + 64 c) are given
+template <int NCH>
+BASE_DEV void best_two_pv(const float (&v)[NCH], const double (&pv)[NCH], int64_t E, int lane,
+                          int& b1, double& v1, double& v2, double& pb) {
+    double val[NCH];
+    double m1 = -DBL_MAX, m2 = -DBL_MAX;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = lane + 64 * c;
         val[c] = -DBL_MAX;
-        pv[c] = 0.0;
         if (e < E) {
-            pv[c] = pi[e];
             val[c] = (double)v[c] - pv[c];
-            best = fmax(best, val[c]);
+            top2_merge(m1, m2, val[c], -DBL_MAX);
         }
     }
-    const double vmax = wave_max_f64(best);
+    top2_step<kDppXor1>(m1, m2);
+    top2_step<kDppXor2>(m1, m2);
+    top2_step<kDppHalfMirror>(m1, m2);
+    top2_step<kDppMirror>(m1, m2);
+    top2_rows<kDppBcast15, 0xA>(m1, m2);
+    top2_rows<kDppBcast31, 0xC>(m1, m2);
+    const double vmax = readlane_f64(m1, 63);
+    double sec = readlane_f64(m2, 63);
     int bi = -1;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const unsigned long long m = __ballot(lane + 64 * c < E && val[c] == vmax);
         if (bi < 0 && m) bi = 64 * c + __builtin_ctzll(m);
     }
-    double sec = -DBL_MAX;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int e = lane + 64 * c;
-        if (e < E && e != bi) sec = fmax(sec, val[c]);
-    }
-    sec = wave_max_f64(sec);
     if (E == 1) sec = vmax;
     double mine = 0.0;
 #pragma unroll
@@ -184,6 +205,18 @@ BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& 
     v1 = vmax;
     v2 = sec;
     pb = readlane_f64(mine, bi & 63);
+}
+
+template <int NCH, typename PiT>
+BASE_DEV void best_two(const float (&v)[NCH], PiT pi, int64_t E, int lane, int& b1, double& v1,
+                       double& v2, double& pb) {
+    double pv[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        pv[c] = (e < E) ? pi[e] : 0.0;
+    }
+    best_two_pv<NCH>(v, pv, E, lane, b1, v1, v2, pb);
 }
 
 // The bid beta = pb + (v1 - v2) + eps. It is at least the next double above
@@ -457,8 +490,8 @@ template <int NCH>
 static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
                         AucStatsDev* st, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(tail_threads(NCH)), lds, stream, s, T, E, k, w,
-                       scan, eps, phase, max_bids, st);
+    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(tail_threads(NCH)), lds, stream, s, T, E,
+                       k, w, scan, eps, phase, max_bids, st);
 }
 
 template <int NCH>

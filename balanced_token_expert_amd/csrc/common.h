@@ -78,6 +78,10 @@ BASE_DEV double wave_min_f64(double v) {
     return v;
 }
 
+// address spaces for the direct global -> LDS loads (global_load_lds)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 // ---- DPP cross-lane moves (a few cycles, no LDS crossbar). Lanes whose
 // source is outside the row keep their own value.
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]

@@ -21,9 +21,6 @@ __shared__ __attribute__((aligned(16))) char g_stage3[kDmaStageBytes];
 
 __device__ __attribute__((aligned(16))) uint4 g_zero16;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 template <int S>
 BASE_DEV char* dma_stage() {
     return S == 0 ? g_stage0 : (S == 1 ? g_stage1 : (S == 2 ? g_stage2 : g_stage3));
