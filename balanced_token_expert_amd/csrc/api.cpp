@@ -20,7 +20,7 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 // Workspace layout shared by base_workspace_bytes and the entry points.
 struct Layout {
     size_t scan = 0, stats = 0, prices = 0, scores = 0, perm = 0, offsets = 0, hidden = 0,
-           auction = 0, permws = 0, assign = 0, total = 0;
+           auction = 0, permws = 0, assign = 0, gblk = 0, total = 0;
 };
 
 Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
@@ -50,6 +50,7 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
         take(L.scores, (size_t)T * E * 4);
         take(L.perm, (size_t)T * 4);
         take(L.hidden, (size_t)T * F * (dt == BASE_BF16 ? 2 : 4));
+        take(L.gblk, (size_t)(E + 1) * 4);
     }
     // the auction's own scratch, followed by the grouping's
     take(L.auction, auction_ws_bytes(T, E) + perm_ws_bytes(T, E));
@@ -182,8 +183,7 @@ int base_layer_forward(const void* h, const void* w, const void* W1, const void*
     if (mode != BASE_ROUTE_BALANCED && mode != BASE_ROUTE_GREEDY && mode != BASE_ROUTE_GIVEN)
         return BASE_ERR_INVALID_ARG;
     if (mode == BASE_ROUTE_BALANCED && cfg_phases(cfg) < 0) return BASE_ERR_INVALID_ARG;
-    if (T % E) return BASE_ERR_INDIVISIBLE;
-    if (mode == BASE_ROUTE_GREEDY) return BASE_ERR_UNSUPPORTED;
+    if (mode != BASE_ROUTE_GREEDY && T % E) return BASE_ERR_INDIVISIBLE;
     if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
     if (dt == BASE_BF16 && (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) ||
                             misaligned(W1) || misaligned(W2) || misaligned(out)))
@@ -200,6 +200,9 @@ int base_layer_forward(const void* h, const void* w, const void* W1, const void*
     int32_t* offs = (int32_t*)(W + L.offsets);
     double* prices = (double*)(W + L.prices);
     void* H = W + L.hidden;
+    int32_t* gblk = (int32_t*)(W + L.gblk);
+    // greedy routing gives ragged expert groups (rows offs[e] .. offs[e+1]-1)
+    const int32_t* goff = (mode == BASE_ROUTE_GREEDY) ? offs : nullptr;
 
     mark(0, st);
     hipError_t e = launch_scan_init(scan, st);
@@ -209,6 +212,11 @@ int base_layer_forward(const void* h, const void* w, const void* W1, const void*
         if (mode == BASE_ROUTE_BALANCED) {
             e = launch_auction(s, T, E, cfg.eps_start, cfg.eps_end, cfg.eps_factor, cfg.max_bids,
                                scan, assign, pm, offs, prices, sd, W + L.auction, st);
+        } else if (mode == BASE_ROUTE_GREEDY) {
+            e = launch_stats_reset(sd, st);
+            if (e == hipSuccess) e = launch_greedy(s, T, E, scan, assign, nullptr, st);
+            if (e == hipSuccess)
+                e = launch_perm(assign, T, E, pm, offs, nullptr, 0, nullptr, W + L.permws, st);
         } else {
             e = launch_stats_reset(sd, st);
             if (e == hipSuccess)
@@ -216,9 +224,9 @@ int base_layer_forward(const void* h, const void* w, const void* W1, const void*
         }
     }
     mark(2, st);
-    if (e == hipSuccess) e = launch_ffn1(h, pm, W1, H, E, k, D, F, dt, act, st);
+    if (e == hipSuccess) e = launch_ffn1(h, pm, W1, H, E, k, D, F, dt, act, goff, gblk, T, st);
     mark(3, st);
-    if (e == hipSuccess) e = launch_ffn2(H, pm, W2, s, h, out, E, k, D, F, dt, st);
+    if (e == hipSuccess) e = launch_ffn2(H, pm, W2, s, h, out, E, k, D, F, dt, goff, gblk, T, st);
     mark(4, st);
     mark(5, st);
     return hip_rc(e);

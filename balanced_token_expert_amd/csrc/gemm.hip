@@ -38,7 +38,66 @@ struct GemmParams {
     int64_t E;
     const void* h;          // FFN2: residual rows (length N)
     void* out;              // FFN2: output rows (length N)
+    // ragged groups (null: every group has M rows): group g owns rows
+    // [goff[g], goff[g+1]) and the blocks [gblk[g], gblk[g+1]) of the launch
+    const int32_t* goff;
+    const int32_t* gblk;
 };
+
+// The tile a block computes: group g, tile (tm, tn), and the group's rows
+// row0 .. row0 + rows - 1 (in the grouped row order of A / H).
+struct Tile {
+    int64_t g, tm, tn, row0, rows;
+};
+template <int BM, int BN>
+BASE_DEV bool locate_tile(const GemmParams& p, int64_t lid, Tile& t) {
+    const int64_t ntn = (p.N + BN - 1) / BN;
+    if (!p.goff) {
+        const int64_t ntm = (p.M + BM - 1) / BM;
+        t.g = lid / (ntm * ntn);
+        if (t.g >= p.groups) return false;
+        const int64_t rr = lid % (ntm * ntn);
+        t.tn = rr / ntm;  // M tiles fastest: they share B
+        t.tm = rr % ntm;
+        t.row0 = t.g * p.M;
+        t.rows = p.M;
+        return true;
+    }
+    if (lid >= p.gblk[p.groups]) return false;
+    int64_t lo = 0, hi = p.groups;  // the last group whose blocks start at or before lid
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (p.gblk[mid] <= lid) lo = mid;
+        else hi = mid;
+    }
+    t.g = lo;
+    t.row0 = p.goff[lo];
+    t.rows = p.goff[lo + 1] - p.goff[lo];
+    const int64_t ntm = (t.rows + BM - 1) / BM;
+    const int64_t local = lid - p.gblk[lo];
+    t.tn = local / ntm;
+    t.tm = local % ntm;
+    return true;
+}
+
+// gblk[g] = blocks of groups 0..g-1 for BM-row tiles and ntn column tiles
+// (one workgroup of 1024 threads; groups <= 1024)
+__global__ __launch_bounds__(1024) void group_blocks_kernel(const int32_t* goff, int64_t groups,
+                                                            int64_t bm, int64_t ntn, int32_t* gblk) {
+    __shared__ int32_t sc[1024];
+    const int g = threadIdx.x;
+    const int32_t own = (g < groups) ? (int32_t)(((goff[g + 1] - goff[g]) + bm - 1) / bm * ntn) : 0;
+    sc[g] = own;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int32_t v = (g >= o) ? sc[g - o] : 0;
+        __syncthreads();
+        sc[g] += v;
+        __syncthreads();
+    }
+    if (g < groups) gblk[g + 1] = sc[g];
+    if (g == 0) gblk[0] = 0;
+}
 
 // Physical block id -> logical tile id such that each XCD (blocks are dealt
 // round-robin to the 8 XCDs) receives a contiguous run of logical tiles.
@@ -51,7 +110,7 @@ BASE_DEV int64_t xcd_logical(int64_t pid, int64_t nblk) {
 BASE_DEV float apply_act(float v, int act) { return act ? gelu_erf(v) : fmaxf(v, 0.0f); }
 
 template <int Kind, int TM, int TN>
-BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g, int64_t mw,
+BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl, int64_t mw,
                          int64_t nw, int lane);
 
 // ---------------------------------------------------------------- bf16 MFMA
@@ -72,13 +131,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
-    const int64_t lid = xcd_logical(blockIdx.x, gridDim.x);
-    const int64_t g = lid / (ntm * ntn);
-    if (g >= p.groups) return;
-    const int64_t rr = lid % (ntm * ntn);
-    const int64_t tn = rr / ntm, tm = rr % ntm;  // M tiles fastest: they share B
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    Tile tl;
+    if (!locate_tile<BM, BN>(p, xcd_logical(blockIdx.x, gridDim.x), tl)) return;
+    const int64_t g = tl.g;
+    const int64_t m0 = tl.tm * BM, n0 = tl.tn * BN;
 
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
@@ -94,10 +150,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
         akc[j] = (c & 7) * 8;
         int64_t m = m0 + ar[j];
         arow[j] = nullptr;
-        if (m < p.M) {
+        if (m < tl.rows) {
             int64_t src;
-            if (Kind == KIND_FFN1) src = p.perm[g * p.M + m];
-            else if (Kind == KIND_FFN2) src = g * p.M + m;
+            if (Kind == KIND_FFN1) src = p.perm[tl.row0 + m];
+            else if (Kind == KIND_FFN2) src = tl.row0 + m;
             else src = m;
             arow[j] = A + src * p.K;
         }
@@ -166,7 +222,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
         __syncthreads();
     }
 
-    store_tile<Kind, TM, TN>(p, acc, g, m0 + wm * WTM, n0 + wn * WTN, lane);
+    store_tile<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 #include "gemm_dma.h"
@@ -175,8 +231,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 // output row and column are mw and nw. acc[i][j][r] is C[row][col] with
 //   row = mw + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = nw + j*32 + lane%32
 template <int Kind, int TM, int TN>
-BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g, int64_t mw,
+BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl, int64_t mw,
                          int64_t nw, int lane) {
+    const int64_t g = tl.g;
     uint32_t kmin = 0xffffffffu;
     int nonfin = 0;
 #pragma unroll
@@ -184,11 +241,11 @@ BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t m = mw + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (m >= p.M) continue;
+            if (m >= tl.rows) continue;
             int64_t t = 0;
             float gate = 0.0f;
             if (Kind == KIND_FFN2) {
-                t = p.perm[g * p.M + m];
+                t = p.perm[tl.row0 + m];
                 gate = sigmoid_f32(p.s_in[t * p.E + g]);
             }
 #pragma unroll
@@ -201,7 +258,7 @@ BASE_DEV void store_tile(const GemmParams& p, f32x16_t (&acc)[TM][TN], int64_t g
                     if (is_finite_f32(v)) kmin = min(kmin, f32_key(v));
                     else ++nonfin;
                 } else if (Kind == KIND_FFN1) {
-                    ((uint16_t*)p.H)[(g * p.M + m) * p.N + n] = f32_to_bf16(apply_act(v, p.act));
+                    ((uint16_t*)p.H)[(tl.row0 + m) * p.N + n] = f32_to_bf16(apply_act(v, p.act));
                 } else {
                     const float res = bf16_to_f32(((const uint16_t*)p.h)[t * p.N + n]);
                     ((uint16_t*)p.out)[t * p.N + n] = f32_to_bf16(gate * v + res);
@@ -232,13 +289,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     __shared__ float As[BK][BM + 4];
     __shared__ float Bs[BK][BN + 4];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int64_t ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
-    const int64_t lid = blockIdx.x;
-    const int64_t g = lid / (ntm * ntn);
-    if (g >= p.groups) return;
-    const int64_t rr = lid % (ntm * ntn);
-    const int64_t tn = rr / ntm, tm = rr % ntm;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    Tile tl;
+    if (!locate_tile<BM, BN>(p, blockIdx.x, tl)) return;
+    const int64_t g = tl.g;
+    const int64_t m0 = tl.tm * BM, n0 = tl.tn * BN;
     const float* A = (const float*)p.A;
     const float* B = (const float*)p.B + g * p.b_gstride;
 
@@ -247,9 +301,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     const float* arow = nullptr;
     {
         int64_t m = m0 + lr;
-        if (m < p.M) {
-            int64_t src = (Kind == KIND_FFN1) ? p.perm[g * p.M + m]
-                        : (Kind == KIND_FFN2) ? g * p.M + m : m;
+        if (m < tl.rows) {
+            int64_t src = (Kind == KIND_FFN1) ? p.perm[tl.row0 + m]
+                        : (Kind == KIND_FFN2) ? tl.row0 + m : m;
             arow = A + src * p.K;
         }
     }
@@ -283,11 +337,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + ty * 4 + i;
-        if (m >= p.M) continue;
+        if (m >= tl.rows) continue;
         int64_t t = 0;
         float gate = 0.0f;
         if (Kind == KIND_FFN2) {
-            t = p.perm[g * p.M + m];
+            t = p.perm[tl.row0 + m];
             gate = sigmoid_f32(p.s_in[t * p.E + g]);
         }
 #pragma unroll
@@ -300,7 +354,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
                 if (is_finite_f32(v)) kmin = min(kmin, f32_key(v));
                 else ++nonfin;
             } else if (Kind == KIND_FFN1) {
-                ((float*)p.H)[(g * p.M + m) * p.N + n] = apply_act(v, p.act);
+                ((float*)p.H)[(tl.row0 + m) * p.N + n] = apply_act(v, p.act);
             } else {
                 ((float*)p.out)[t * p.N + n] = gate * v + ((const float*)p.h)[t * p.N + n];
             }
@@ -334,19 +388,32 @@ static hipError_t run_bf16(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int Kind, int BN, int WM, int WN>
-static hipError_t run_dma(const GemmParams& p, hipStream_t st) {
-    const int64_t tiles = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN) * p.groups;
+// Blocks to launch for BM x BN tiles: exact for equal groups; for ragged
+// groups the block map is built on the device first and the launch covers
+// its upper bound (ceil(rows/BM) + groups column-tile rows; the rest exit).
+template <int BM, int BN>
+static int64_t grid_blocks(const GemmParams& p, int32_t* gblk, int64_t rows_total,
+                           hipStream_t st) {
+    const int64_t ntn = (p.N + BN - 1) / BN;
+    if (!p.goff) return ((p.M + BM - 1) / BM) * ntn * p.groups;
+    hipLaunchKernelGGL(group_blocks_kernel, dim3(1), dim3(1024), 0, st, p.goff, p.groups,
+                       (int64_t)BM, ntn, gblk);
+    return ((rows_total + BM - 1) / BM + p.groups) * ntn;
+}
+
+template <int Kind, int BN, int WM, int WN, int LAG>
+static hipError_t run_dma(const GemmParams& p, int32_t* gblk, int64_t rows_total, hipStream_t st) {
+    const int64_t tiles = grid_blocks<256, BN>(p, gblk, rows_total, st);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<Kind, BN, WM, WN>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<Kind, BN, WM, WN, LAG>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
 
 template <int Kind>
-static hipError_t run_f32(const GemmParams& p, hipStream_t st) {
-    const int64_t tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64) * p.groups;
+static hipError_t run_f32(const GemmParams& p, int32_t* gblk, int64_t rows_total, hipStream_t st) {
+    const int64_t tiles = grid_blocks<64, 64>(p, gblk, rows_total, st);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gemm_f32_kernel<Kind>, dim3((unsigned)tiles), dim3(256), 0, st, p);
@@ -358,30 +425,35 @@ hipError_t launch_affinity(const void* h, const void* w, float* s, int64_t T, in
     GemmParams p = {};
     p.A = h; p.B = w; p.M = T; p.N = E; p.K = D; p.groups = 1;
     p.s_out = s; p.scan = scan;
-    if (dt == 0) return run_f32<KIND_AFF>(p, st);
+    if (dt == 0) return run_f32<KIND_AFF>(p, nullptr, T, st);
     if (E <= 64) return run_bf16<KIND_AFF, 128, 64, 2, 2>(p, st);
     return run_bf16<KIND_AFF, 128, 128, 2, 2>(p, st);
 }
 
 hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1, void* H, int64_t E,
-                       int64_t k, int64_t D, int64_t F, int dt, int act, hipStream_t st) {
+                       int64_t k, int64_t D, int64_t F, int dt, int act, const int32_t* goff,
+                       int32_t* gblk, int64_t rows_total, hipStream_t st) {
     GemmParams p = {};
     p.A = h; p.B = W1; p.M = k; p.N = F; p.K = D; p.groups = E;
     p.perm = perm; p.b_gstride = F * D; p.H = H; p.act = act;
-    if (dt == 0) return run_f32<KIND_FFN1>(p, st);
-    return run_dma<KIND_FFN1, 256, 4, 2>(p, st);
+    p.goff = goff; p.gblk = gblk;
+    if (dt == 0) return run_f32<KIND_FFN1>(p, gblk, rows_total, st);
+    return run_dma<KIND_FFN1, 256, 4, 2, 0>(p, gblk, rows_total, st);
 }
 
 hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const float* s,
                        const void* h, void* out, int64_t E, int64_t k, int64_t D, int64_t F,
-                       int dt, hipStream_t st) {
+                       int dt, const int32_t* goff, int32_t* gblk, int64_t rows_total,
+                       hipStream_t st) {
     GemmParams p = {};
     p.A = H; p.B = W2; p.M = k; p.N = D; p.K = F; p.groups = E;
     p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
-    if (dt == 0) return run_f32<KIND_FFN2>(p, st);
+    p.goff = goff; p.gblk = gblk;
+    if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
     // 256-wide tiles unless that leaves under two workgroups per CU
-    if (((D + 255) / 256) * ((k + 255) / 256) * E >= 512) return run_dma<KIND_FFN2, 256, 4, 2>(p, st);
-    return run_dma<KIND_FFN2, 128, 4, 2>(p, st);
+    if (((D + 255) / 256) * ((rows_total + 255) / 256) >= 512)
+        return run_dma<KIND_FFN2, 256, 4, 2, 0>(p, gblk, rows_total, st);
+    return run_dma<KIND_FFN2, 128, 4, 2, 0>(p, gblk, rows_total, st);
 }
 
 }  // namespace base

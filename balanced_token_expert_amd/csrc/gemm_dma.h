@@ -42,7 +42,12 @@ BASE_DEV void wait_vmcnt() {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int Kind, int BN, int WM, int WN>
+// LAG = 0: a wave reads a K step's fragments right after the barrier that
+// makes the step ready, then issues its MFMAs (2 waves per SIMD hide each
+// other's LDS latency). LAG = 1: fragments are read one K step ahead of the
+// MFMAs that use them (two register sets), for one wave per SIMD with a
+// large sub-tile.
+template <int Kind, int BN, int WM, int WN, int LAG>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p) {
     constexpr int BM = 256, BK = 32, S = 4, NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -56,13 +61,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
-    const int64_t lid = xcd_logical(blockIdx.x, gridDim.x);
-    const int64_t g = lid / (ntm * ntn);
-    if (g >= p.groups) return;
-    const int64_t rr = lid % (ntm * ntn);
-    const int64_t tn = rr / ntm, tm = rr % ntm;  // M tiles fastest: they share B
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    Tile tl;
+    if (!locate_tile<BM, BN>(p, xcd_logical(blockIdx.x, gridDim.x), tl)) return;
+    const int64_t g = tl.g;
+    const int64_t m0 = tl.tm * BM, n0 = tl.tn * BN;
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
 
@@ -77,10 +79,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
         akc[j] = c * 8;
         const int64_t m = m0 + row;
         asrc[j] = nullptr;
-        if (m < p.M) {
+        if (m < tl.rows) {
             int64_t src;
-            if (Kind == KIND_FFN1) src = p.perm[g * p.M + m];
-            else if (Kind == KIND_FFN2) src = g * p.M + m;
+            if (Kind == KIND_FFN1) src = p.perm[tl.row0 + m];
+            else if (Kind == KIND_FFN2) src = tl.row0 + m;
             else src = m;
             asrc[j] = A + src * p.K + c * 8;
         }
@@ -133,28 +135,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // both 16-deep halves' fragments are read up front so the second half's
-    // reads overlap the first half's MFMAs
-    auto compute = [&](const char* st) {
-        bf16x8_t af[2][TM], bfr[2][TN];
+    auto load_frags = [&](const char* st, bf16x8_t (&fa_)[2][TM], bf16x8_t (&fb_)[2][TN]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[kk][i] = *(const bf16x8_t*)(st + fa[kk][i]);
+            for (int i = 0; i < TM; ++i) fa_[kk][i] = *(const bf16x8_t*)(st + fa[kk][i]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bfr[kk][j] = *(const bf16x8_t*)(st + fb[kk][j]);
+            for (int j = 0; j < TN; ++j) fb_[kk][j] = *(const bf16x8_t*)(st + fb[kk][j]);
         }
+    };
+    auto mfmas = [&](const bf16x8_t (&fa_)[2][TM], const bf16x8_t (&fb_)[2][TN]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[kk][i], fb_[kk][j],
                                                                          acc[i][j], 0, 0, 0);
     };
     const int64_t nk = (p.K + BK - 1) / BK;
-    // wait for K step kt (the loads of the steps issued after it may stay in flight)
+    // wait for K step kt (the loads of the steps issued after it may stay in
+    // flight) and for every wave's reads of the stage about to be refilled
     auto ready = [&](int64_t kt) {
         const int64_t rest = nk - 1 - kt;  // K steps issued after kt (at most S - 2)
         if (rest >= 2) wait_vmcnt<2 * PER>();
@@ -167,25 +169,71 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
     if (nk > 0) issue(0, dma_stage<0>());
     if (nk > 1) issue(1, dma_stage<1>());
     if (nk > 2) issue(2, dma_stage<2>());
-    for (int64_t kt = 0; kt < nk; kt += S) {
-        ready(kt);
-        if (kt + 3 < nk) issue(kt + 3, dma_stage<3>());
-        compute(dma_stage<0>());
-        if (kt + 1 < nk) {
-            ready(kt + 1);
-            if (kt + 4 < nk) issue(kt + 4, dma_stage<0>());
-            compute(dma_stage<1>());
+    if (LAG == 0) {
+        // both 16-deep halves' fragments are read up front so the second
+        // half's reads overlap the first half's MFMAs
+        bf16x8_t af[2][TM], bfr[2][TN];
+        auto compute = [&](const char* st) {
+            load_frags(st, af, bfr);
+            mfmas(af, bfr);
+        };
+        for (int64_t kt = 0; kt < nk; kt += S) {
+            ready(kt);
+            if (kt + 3 < nk) issue(kt + 3, dma_stage<3>());
+            compute(dma_stage<0>());
+            if (kt + 1 < nk) {
+                ready(kt + 1);
+                if (kt + 4 < nk) issue(kt + 4, dma_stage<0>());
+                compute(dma_stage<1>());
+            }
+            if (kt + 2 < nk) {
+                ready(kt + 2);
+                if (kt + 5 < nk) issue(kt + 5, dma_stage<1>());
+                compute(dma_stage<2>());
+            }
+            if (kt + 3 < nk) {
+                ready(kt + 3);
+                if (kt + 6 < nk) issue(kt + 6, dma_stage<2>());
+                compute(dma_stage<3>());
+            }
         }
-        if (kt + 2 < nk) {
-            ready(kt + 2);
-            if (kt + 5 < nk) issue(kt + 5, dma_stage<1>());
-            compute(dma_stage<2>());
+    } else {
+        // step kt: make step kt+1 ready, refill kt's stage with step kt+4,
+        // read step kt+1's fragments, then the MFMAs of step kt
+        bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
+        if (nk > 0) {
+            ready(0);
+            load_frags(dma_stage<0>(), a0, b0);
         }
-        if (kt + 3 < nk) {
-            ready(kt + 3);
-            if (kt + 6 < nk) issue(kt + 6, dma_stage<2>());
-            compute(dma_stage<3>());
+        for (int64_t kt = 0; kt < nk; kt += S) {
+            if (kt + 1 < nk) {
+                ready(kt + 1);
+                if (kt + 4 < nk) issue(kt + 4, dma_stage<0>());
+                load_frags(dma_stage<1>(), a1, b1);
+            }
+            mfmas(a0, b0);
+            if (kt + 1 >= nk) break;
+            if (kt + 2 < nk) {
+                ready(kt + 2);
+                if (kt + 5 < nk) issue(kt + 5, dma_stage<1>());
+                load_frags(dma_stage<2>(), a0, b0);
+            }
+            mfmas(a1, b1);
+            if (kt + 2 >= nk) break;
+            if (kt + 3 < nk) {
+                ready(kt + 3);
+                if (kt + 6 < nk) issue(kt + 6, dma_stage<2>());
+                load_frags(dma_stage<3>(), a1, b1);
+            }
+            mfmas(a0, b0);
+            if (kt + 3 >= nk) break;
+            if (kt + 4 < nk) {
+                ready(kt + 4);
+                if (kt + 7 < nk) issue(kt + 7, dma_stage<3>());
+                load_frags(dma_stage<0>(), a0, b0);
+            }
+            mfmas(a1, b1);
         }
     }
-    store_tile<Kind, TM, TN>(p, acc, g, m0 + wm * WTM, n0 + wn * WTN, lane);
+    store_tile<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane);
 }

@@ -26,14 +26,21 @@ struct AucStatsDev {
 hipError_t launch_affinity(const void* h, const void* w, float* s, int64_t T,
                            int64_t E, int64_t D, int dt, ScoreScan* scan,
                            hipStream_t st);
-// H[e*k+i, :] = act(h[perm[e*k+i], :] W1_e^T)      (bf16 or fp32 H)
+// Expert groups: equal (goff == nullptr: group e owns rows e*k .. e*k+k-1 of
+// the grouped order) or ragged (group e owns rows goff[e] .. goff[e+1]-1,
+// rows_total = goff[E]; gblk is E+1 ints of scratch for the launch's block
+// map).
+// H[r, :] = act(h[perm[r], :] W1_e^T) for every row r of group e (bf16 or fp32 H)
 hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1,
                        void* H, int64_t E, int64_t k, int64_t D, int64_t F,
-                       int dt, int act, hipStream_t st);
-// out[perm[e*k+i], :] = sigmoid(s[t, e]) * (H_e W2_e^T)[i, :] + h[t, :]
+                       int dt, int act, const int32_t* goff, int32_t* gblk,
+                       int64_t rows_total, hipStream_t st);
+// out[perm[r], :] = sigmoid(s[perm[r], e]) * (H W2_e^T)[r, :] + h[perm[r], :]
 hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2,
                        const float* s, const void* h, void* out, int64_t E,
-                       int64_t k, int64_t D, int64_t F, int dt, hipStream_t st);
+                       int64_t k, int64_t D, int64_t F, int dt,
+                       const int32_t* goff, int32_t* gblk, int64_t rows_total,
+                       hipStream_t st);
 
 // ---- route.hip
 hipError_t launch_scan_init(ScoreScan* scan, hipStream_t st);

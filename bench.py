@@ -171,6 +171,32 @@ def cpu_baseline(wl, h, w, W1, W2, sample_experts=48):
             "auction_s": round(t_auc, 3)}
 
 
+def greedy_layer(hd, wd, W1d, W2d, act, T, E, reps=5):
+    """The layer with test-time greedy routing (ragged expert groups) on the
+    same inputs: median ms of the whole call and the largest group."""
+    import torch
+    from balanced_token_expert_amd import api
+    bufs = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+                scores=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+                out=torch.empty_like(hd), stats=api.new_stats(),
+                ws=api.workspace(api.BASE_OP_LAYER, T, E, hd.shape[1], W1d.shape[1],
+                                 api.BASE_BF16 if hd.dtype == torch.bfloat16 else api.BASE_F32))
+    api.base_layer_forward(hd, wd, W1d, W2d, act, api.BASE_ROUTE_GREEDY, **bufs)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        api.base_layer_forward(hd, wd, W1d, W2d, act, api.BASE_ROUTE_GREEDY, **bufs)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    counts = np.bincount(bufs["assign"].cpu().numpy(), minlength=E)
+    return {"ms": round(float(np.median(times)), 4), "tokens_per_s": round(T / (np.median(times) * 1e-3), 1),
+            "largest_group": int(counts.max()), "empty_experts": int((counts == 0).sum())}
+
+
 def auction_solve(reps=10):
     """Auction solve ms on the mixture workload (device-resident fp32 scores)."""
     import torch
@@ -355,6 +381,7 @@ def main():
                            "max_share": round(float(gcount.max() / T), 5),
                            "uniform_share": round(1.0 / E, 5)},
            "roofline": roof, "wall_s_timed": round(wall, 3)}
+    res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
     if not args.no_auction:
         res["auction_solve_ms"] = auction_solve()
     if not args.no_cpu_baseline:

@@ -187,18 +187,20 @@ int base_route_greedy(const float *scores, int64_t T, int64_t E,
  *     act(W1 x) is stored as bf16 between the two products; for fp32 all
  *     arithmetic is fp32. The gate uses the fp32 affinity of the chosen
  *     expert.
- *   mode: BASE_ROUTE_BALANCED (auction, cfg used) or BASE_ROUTE_GIVEN
- *     (assign is an input; a token with an id outside [0,E) or an expert
- *     without exactly k tokens sets stats->status = BASE_ERR_UNBALANCED and
- *     out is left unspecified) or BASE_ROUTE_GREEDY (ragged expert groups:
- *     returns BASE_ERR_UNSUPPORTED in this build; base_route_greedy gives
- *     the routing).
- *   assign[T]: output (BALANCED) or input (GIVEN).
+ *   mode: BASE_ROUTE_BALANCED (the auction of eq. 2, cfg used; every
+ *     expert gets k = T/E tokens), BASE_ROUTE_GIVEN (assign is an input; a
+ *     token with an id outside [0,E) or an expert without exactly k tokens
+ *     sets stats->status = BASE_ERR_UNBALANCED and out is left unspecified)
+ *     or BASE_ROUTE_GREEDY (test-time routing, sec. 3.2.2: each token to its
+ *     highest-scoring expert, lowest id on ties, as base_route_greedy; the
+ *     expert groups are ragged -- any size, including empty -- and T % E
+ *     need not be 0; cfg is ignored).
+ *   assign[T]: output (BALANCED, GREEDY) or input (GIVEN).
  *   scores: T x E fp32 output, or NULL (then kept in the workspace).
  *   perm: T int32 output of the expert grouping, or NULL.
  *   stats: device pointer or NULL; prices are written to the workspace.
  *   ws: scratch of base_workspace_bytes(BASE_OP_LAYER, T, E, D, F, dt).
- * Errors: as base_assign_auction; INDIVISIBLE also for GIVEN mode.
+ * Errors: as base_assign_auction (INDIVISIBLE for BALANCED and GIVEN).
  */
 int base_layer_forward(const void *h, const void *w, const void *W1,
                        const void *W2, int64_t T, int64_t E, int64_t D,

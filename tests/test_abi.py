@@ -93,7 +93,9 @@ def test_layer_host_errors(lib):
                                       None, None, FAKE, None, FAKE, ws, None)
 
     assert call(T=10) == api.BASE_ERR_INDIVISIBLE
-    assert call(mode=api.BASE_ROUTE_GREEDY) == api.BASE_ERR_UNSUPPORTED
+    # greedy routing has ragged groups: T % E need not be 0 (here the
+    # workspace check is what fails)
+    assert call(T=10, mode=api.BASE_ROUTE_GREEDY, ws=1) == api.BASE_ERR_INVALID_ARG
     assert call(mode=7) == api.BASE_ERR_INVALID_ARG
     assert call(act=5) == api.BASE_ERR_INVALID_ARG
     assert call(dt=9) == api.BASE_ERR_INVALID_ARG

@@ -177,3 +177,42 @@ def test_full_layer(wid):
     torch.cuda.synchronize()
     assert api.read_stats(r0["stats"]).status == 0
     assert torch.equal(r0["out"], dev["h"])
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_full_greedy_layer(wid):
+    """Greedy-mode layer (ragged expert groups) at the skew workload (about
+    80 % of the tokens on one expert) and the large workload: routing
+    bit-exact with the oracle's argmax of the same scores, canonical
+    grouping, and sampled rows -- up to 256 of the largest group plus every
+    row of the smallest non-empty group and of expert E-1 -- against the fp64
+    layer."""
+    wl = W.workload(wid)
+    host = _gen(wl)
+    dev = {k: to_dev(v, wl.dtype) for k, v in host.items()}
+    r = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], dev["W2"], _act(wl),
+                               api.BASE_ROUTE_GREEDY)
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    s = r["scores"].cpu().numpy().astype(np.float64)
+    a = r["assign"].cpu().numpy()
+    ga, gc = oracle.greedy_route(s)
+    assert (a == ga).all()
+    cperm, _ = oracle.canonical_perm(a, wl.E)
+    assert (r["perm"].cpu().numpy() == cperm).all()
+    rng = np.random.default_rng(wid)
+    big = int(np.argmax(gc))
+    nonempty = np.nonzero(gc)[0]
+    small = int(nonempty[np.argmin(gc[nonempty])])
+    pick = [np.nonzero(a == big)[0]]
+    pick[0] = rng.choice(pick[0], size=min(256, pick[0].size), replace=False)
+    pick += [np.nonzero(a == small)[0], np.nonzero(a == wl.E - 1)[0]]
+    rows = np.unique(np.concatenate(pick))
+    sub = np.full(wl.T, -1, dtype=np.int64)  # only the sampled rows keep their expert
+    sub[rows] = a[rows]
+    ref = oracle.layer_forward(f64(host["h"], wl.dtype), f64(host["w"], wl.dtype),
+                               lambda e: f64(host["W1"][e], wl.dtype),
+                               lambda e: f64(host["W2"][e], wl.dtype), sub, wl.act,
+                               experts=sorted({big, small, wl.E - 1}), s=s)[rows]
+    y = dev_to_f64(r["out"])[rows]
+    assert rel_err(y, ref) <= 2e-2, rel_err(y, ref)
