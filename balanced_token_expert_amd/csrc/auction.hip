@@ -41,7 +41,7 @@ namespace base {
 
 constexpr int kBulkRounds = 16;      // multi-CU rounds per phase (at most)
 constexpr int kTailMax = 64;         // bidders left when the tail takes over
-constexpr int kResolveCap = 4096;    // candidates sorted at once per expert
+constexpr int kResolveCap = 2048;    // bidders sorted at once per expert
 constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
@@ -283,28 +283,47 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
         if (blockIdx.x == 0 && threadIdx.x == 0) ctl->bulk_done = 1;
         return;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) ctl->nbid[cur ^ 1] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        ctl->nbid[cur ^ 1] = 0;
+        ctl->bids_phase += (unsigned long long)nb;  // every listed token bids once
+    }
     const bool ident = ctl->identity;
     const int32_t* list = cur ? w.list1 : w.list0;
     const Sani sn = read_sani(scan);
     const int lane = threadIdx.x & 63;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    // the round's prices do not change during the kernel: keep this lane's
+    double pv[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t e = lane + 64 * c;
+        pv[c] = (e < E) ? w.pi[e] : 0.0;
+    }
     int64_t mine = 0;
-    for (int64_t j = wave; j < nb; j += nw) {
-        const int64_t t = ident ? j : list[j];
-        float v[NCH];
-        load_row<NCH>(s, t, E, lane, sn, v);
+    // each wave's tokens, the next token's row loaded while the current bids
+    int64_t j = wave;
+    float v[NCH], vn[NCH];
+    int64_t t = (j < nb) ? (ident ? j : list[j]) : -1;
+    if (t >= 0) load_row<NCH>(s, t, E, lane, sn, v);
+    while (t >= 0) {
+        const int64_t jn = j + nw;
+        const int64_t tn = (jn < nb) ? (ident ? jn : list[jn]) : -1;
+        if (tn >= 0) load_row<NCH>(s, tn, E, lane, sn, vn);
         int b1;
         double v1, v2, pb;
-        best_two<NCH>(v, w.pi, E, lane, b1, v1, v2, pb);
+        best_two_pv<NCH>(v, pv, E, lane, b1, v1, v2, pb);
         if (lane == 0) {
             w.bexp[t] = b1;
             w.bval[t] = bid_amount(pb, v1, v2, eps);
         }
         ++mine;
+        j = jn;
+        t = tn;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) v[c] = vn[c];
     }
-    if (lane == 0 && mine) atomicAdd(&ctl->bids_phase, (unsigned long long)mine);
+    (void)mine;
 }
 
 // One block per expert: keep the k best of (current holders + this round's
@@ -318,6 +337,22 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
 // Bidders are gathered kResolveCap at a time; a full buffer is merged before
 // the scan goes on.
 BASE_DEV bool better(double ba, int ta, double bb, int tb) { return ba > bb || (ba == bb && ta < tb); }
+
+// Sort (bid, token) pairs across the wave, best first (bitonic network over
+// the 64 lanes by shuffles).
+BASE_DEV void wave_sort_best(double& b, int& t, int lane) {
+#pragma unroll
+    for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+#pragma unroll
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            const double ob = shfl_xor_f64(b, j);
+            const int ot = __shfl_xor(t, j, 64);
+            const bool take_first = ((lane & j) == 0) == ((lane & k2) == 0);
+            const bool swap = take_first ? better(ob, ot, b, t) : better(b, t, ob, ot);
+            if (swap) { b = ob; t = ot; }
+        }
+    }
+}
 
 __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
                                                                AucWs w) {
@@ -353,27 +388,59 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         }
     };
     // merge the n gathered bidders into the holders
-    auto merge = [&](int n) {
-        int P = 1;
+    // sort cb/ct[0, n) best first (n <= kResolveCap): each wave sorts runs of
+    // 64 in registers, then runs are merged pairwise by rank (an element's
+    // place = its index in its run + the partner run's elements ahead of it;
+    // ties between runs go to the left run), ping-ponging with ob/ot
+    auto sort_bidders = [&](int n) {
+        int P = 64;
         while (P < n) P <<= 1;
         for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
         __syncthreads();
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < P / 2; i += blockDim.x) {
-                    const int lo = (i / stride) * stride * 2 + (i % stride);
-                    const int hi = lo + stride;
-                    const bool best_first = ((lo & size) == 0);
-                    const double b0 = cb[lo], b1 = cb[hi];
-                    const int t0 = ct[lo], t1 = ct[hi];
-                    if (better(b1, t1, b0, t0) == best_first) {
-                        cb[lo] = b1; cb[hi] = b0;
-                        ct[lo] = t1; ct[hi] = t0;
-                    }
-                }
-                __syncthreads();
-            }
+        const int wv = tid >> 6, nwv = blockDim.x >> 6;
+        for (int r = wv; r < P / 64; r += nwv) {
+            double b = cb[r * 64 + lane];
+            int t = ct[r * 64 + lane];
+            wave_sort_best(b, t, lane);
+            cb[r * 64 + lane] = b;
+            ct[r * 64 + lane] = t;
         }
+        __syncthreads();
+        double* sb = cb;
+        int32_t* st = ct;
+        double* db = ob;
+        int32_t* dt = ot;
+        for (int len = 64; len < P; len <<= 1) {
+            for (int i = tid; i < P; i += blockDim.x) {
+                const int run = i / len, pos = i - run * len;
+                const int other = (run ^ 1) * len;
+                const double b = sb[i];
+                const int t = st[i];
+                int lo = 0, hi = len;  // partner elements ahead of this one
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    const double pb = sb[other + mid];
+                    const int pt = st[other + mid];
+                    const bool ahead = (run & 1) ? !better(b, t, pb, pt) : better(pb, pt, b, t);
+                    if (ahead) lo = mid + 1;
+                    else hi = mid;
+                }
+                const int at = (run & ~1) * len + pos + lo;
+                db[at] = b;
+                dt[at] = t;
+            }
+            __syncthreads();
+            double* xb = sb; sb = db; db = xb;
+            int32_t* xt = st; st = dt; dt = xt;
+        }
+        if (sb != cb) {
+            for (int i = tid; i < P; i += blockDim.x) { cb[i] = sb[i]; ct[i] = st[i]; }
+            __syncthreads();
+        }
+    };
+    // merge the n gathered bidders into the holders
+    auto merge = [&](int n) {
+        sort_bidders(n);
         const int c = nhold;
         // holder i moves to i + (bidders better than it)
         for (int i0 = 0; i0 < c; i0 += blockDim.x) {
@@ -420,25 +487,60 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
 
     const int c0 = w.cnt[e];
     for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
+    // gather this expert's bidders in one pass with 16 loads in flight per
+    // thread (the bids were written by other XCDs: every load is a far round
+    // trip); tokens first, their bids in a second, parallel sweep. More
+    // bidders than the buffer holds (rare) fall back to chunks merged in turn.
     if (tid == 0) { ncand = 0; nhold = c0; }
     __syncthreads();
-    bool changed = false;
-    for (int64_t j0 = 0; j0 < nb; j0 += blockDim.x) {
-        const int64_t j = j0 + tid;
-        if (j < nb) {
-            const int64_t t = ident ? j : list[j];
-            if (w.bexp[t] == e) {
-                const int pos = atomicAdd(&ncand, 1);
-                cb[pos] = w.bval[t];
-                ct[pos] = (int32_t)t;
+    auto scan_bidders = [&](auto&& fn) {
+        constexpr int U = 16;
+        for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
+            int64_t tt[U];
+            int ee[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = j0 + (int64_t)u * blockDim.x + tid;
+                tt[u] = (j < nb) ? (ident ? j : (int64_t)list[j]) : -1;
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u) ee[u] = (tt[u] >= 0) ? w.bexp[tt[u]] : -1;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ee[u] == e) fn(tt[u]);
         }
+    };
+    scan_bidders([&](int64_t t) {
+        const int pos = atomicAdd(&ncand, 1);
+        if (pos < kResolveCap) ct[pos] = (int32_t)t;
+    });
+    __syncthreads();
+    const int nbe = ncand;
+    const bool changed = nbe > 0;
+    if (nbe > 0 && nbe <= kResolveCap) {
+        for (int i = tid; i < nbe; i += blockDim.x) cb[i] = w.bval[ct[i]];
         __syncthreads();
-        const int n = ncand;
-        changed = changed || n > 0;
-        if (n > kResolveCap - (int)blockDim.x) merge(n);
+        merge(nbe);
+    } else if (nbe > 0) {
+        __syncthreads();
+        if (tid == 0) ncand = 0;
+        __syncthreads();
+        for (int64_t j0 = 0; j0 < nb; j0 += blockDim.x) {
+            const int64_t j = j0 + tid;
+            if (j < nb) {
+                const int64_t t = ident ? j : list[j];
+                if (w.bexp[t] == e) {
+                    const int pos = atomicAdd(&ncand, 1);
+                    cb[pos] = w.bval[t];
+                    ct[pos] = (int32_t)t;
+                }
+            }
+            __syncthreads();
+            const int n = ncand;
+            if (n > kResolveCap - (int)blockDim.x) merge(n);
+        }
+        if (ncand > 0) merge(ncand);
     }
-    if (ncand > 0) merge(ncand);
     if (changed) {
         const int m = nhold;
         for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
