@@ -45,12 +45,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99994
+FETCH_SCALE = 1.99995
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", None, 2367059.5, 1048576.0),
-    "ffn2": ("large_t64k_e128_d2048", None, 2809011.4, 262162.5),
+    "ffn1": ("large_t64k_e128_d2048", "fdcc25bae966ce76f47afe135e2545629f928e14601fa447eb183f0e60cb4423",
+             2369202.2, 1114112.0),
+    "ffn2": ("large_t64k_e128_d2048", "fdcc25bae966ce76f47afe135e2545629f928e14601fa447eb183f0e60cb4423",
+             2812228.4, 278543.2),
 }
 
 
@@ -137,7 +139,7 @@ def stack_dev(parts, dtype="bf16"):
     return out
 
 
-def cpu_baseline(wl, h, w, W1, W2, sample_experts=48):
+def cpu_baseline(wl, h, w, W1, W2, sample_experts=96):
     """The oracle as it stands, on a bounded sample: affinities, CPU auction
     and greedy routing over all T tokens; the fp64 layer forward for the
     tokens of `sample_experts` experts. Scaled to tokens/s of the full step."""
