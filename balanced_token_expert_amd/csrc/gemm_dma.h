@@ -1,17 +1,22 @@
 // bf16 MFMA GEMM fed by direct global -> LDS loads (included by gemm.hip,
-// inside namespace base).
+// inside namespace base). Used for both expert products.
 //
 // 256 x BN output tile per workgroup of WM x WN waves; K steps of 32 held in
 // 4 LDS stages that global_load_lds (16 bytes per lane) fills three K steps
 // ahead of the MFMAs, so about 96 KB per CU are in flight -- enough to cover
 // HBM latency without registers. Each stage is its own LDS object and the
 // K loop is unrolled by the stage count, so the compiler can tell the stage
-// being read from the stages being filled and keeps its LDS reads free of
-// waits on the loads in flight; the loop waits explicitly for the one K step
-// it is about to use. A row of a stage is 4 chunks of 16 bytes; chunk c of
-// row r sits at position c ^ ((r >> 2) & 3), so a fragment read (32 rows x
-// one chunk per half wave) touches 16 different bank groups. Lanes whose row
-// or K range lies outside the operand load a 16-byte block of zeros.
+// being read from the stages being filled; the loop waits explicitly for the
+// one K step it is about to use. A row of a stage is 4 chunks of 16 bytes;
+// chunk c of row r sits at position c ^ swz(r), which keeps the fragment
+// reads (32 rows x one chunk per half wave) free of LDS bank conflicts.
+// Lanes whose row or K range lies outside the operand load a 16-byte block
+// of zeros.
+//
+// The MFMAs take the weight fragment as their first operand, so each
+// accumulator holds C transposed: a lane owns one output row and runs of 4
+// consecutive columns. The epilogue then writes 8-byte pieces of rows and
+// needs one gate and one token index per row per lane.
 
 constexpr int kDmaStageBytes = (256 + 256) * 32 * 2;
 __shared__ __attribute__((aligned(16))) char g_stage0[kDmaStageBytes];
@@ -20,6 +25,8 @@ __shared__ __attribute__((aligned(16))) char g_stage2[kDmaStageBytes];
 __shared__ __attribute__((aligned(16))) char g_stage3[kDmaStageBytes];
 
 __device__ __attribute__((aligned(16))) uint4 g_zero16;
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 template <int S>
 BASE_DEV char* dma_stage() {
@@ -30,25 +37,147 @@ BASE_DEV void dma16(const void* src, char* dst) {
     __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
 }
 
+// Chunk swizzle of a stage row. ds_read_b128 serves 16 lanes per pass from
+// 64 banks, and a fragment read gives lanes 0..15 rows r..r+15 at the same
+// logical chunk: rows 4 apart then need different positions. The extra terms
+// also separate rows 2 apart within each group of 8 lanes, which measured
+// about 10 % faster than the 4-apart rule alone on an LDS read probe.
+BASE_DEV int swz(int r) { return ((r >> 1) & 1) ^ (((r >> 2) & 1) << 1) ^ ((r >> 3) & 1); }
+
+// s_waitcnt through the builtin rather than inline asm, so that the
+// compiler's own wait insertion knows which loads have completed; with an
+// opaque wait it assumes the stage about to be read may still be in flight
+// and drains every outstanding DMA first.
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
 template <int N>
 BASE_DEV void wait_vmcnt() {
-    if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 
-// LAG = 0: a wave reads a K step's fragments right after the barrier that
-// makes the step ready, then issues its MFMAs (2 waves per SIMD hide each
-// other's LDS latency). LAG = 1: fragments are read one K step ahead of the
-// MFMAs that use them (two register sets), for one wave per SIMD with a
-// large sub-tile.
-template <int Kind, int BN, int WM, int WN, int LAG>
+BASE_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// GELU(x) = x/2 (1 + erf(x / sqrt 2)) with erf from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7):
+// erf(z) = 1 - P(u) e^(-z^2), u = 1 / (1 + p z), z >= 0. Written so that the
+// negative side uses P(u) e^(-z^2) = 1 - erf(z) directly, without
+// cancellation. Two transcendental instructions (rcp, exp2) and 12 FMA-class
+// ones. The result is rounded to bf16 afterwards (relative error up to
+// 2^-8), far above the formula's error.
+BASE_DEV float gelu_as7126(float x) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float u = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float q = fmaf(u, 1.061405429f, -1.453152027f);
+    q = fmaf(u, q, 1.421413741f);
+    q = fmaf(u, q, -0.284496736f);
+    q = fmaf(u, q, 0.254829592f);
+    q *= u;
+    const float tail = q * __builtin_amdgcn_exp2f(-(z * z) * 1.44269504088896341f);  // 1 - erf(z)
+    const float two_phi = x >= 0.0f ? 2.0f - tail : tail;  // 1 + erf(x / sqrt 2)
+    return 0.5f * x * two_phi;
+}
+
+// Epilogue for one wave's TM x TN block of transposed 32x32 accumulators:
+// acc[i][j][4q + c] is C[row][col] with
+//   row = mw + i*32 + lane%32,  col = nw + j*32 + 8q + 4*(lane/32) + c.
+// FFN1: H[row0 + row][col] = act(C) (bf16). FFN2 (eq. 1): for token
+// t = perm[row0 + row], out[t][col] = bf16(gate * C + h[t][col]), with the
+// row's gate sigma(s[t][g]) and t loaded before the K loop.
+template <int Kind, int TM, int TN, bool FULL>
+BASE_DEV void dma_epilogue_rows(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                                int64_t mw, int64_t nw, int lane, const int32_t (&trow)[TM],
+                                const float (&gate)[TM]) {
+    // FULL: every row and column of the wave's block exists and N % 4 == 0,
+    // so no piece needs a bounds check and all pieces are 8-byte aligned
+    const bool vec = FULL || (p.N & 3) == 0;
+    const int64_t cb = nw + 4 * (lane >> 5);
+    if (Kind == KIND_FFN1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + i * 32 + (lane & 31);
+            if (!FULL && m >= tl.rows) continue;
+            uint16_t* hrow = (uint16_t*)p.H + (tl.row0 + m) * p.N;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = cb + j * 32 + 8 * q;
+                    f32x4_t y;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float v = acc[i][j][4 * q + c];
+                        y[c] = p.act ? gelu_as7126(v) : fmaxf(v, 0.0f);
+                    }
+                    if (vec) {
+                        if (FULL || n < p.N)
+                            *(bf16x4_t*)(hrow + n) = __builtin_convertvector(y, bf16x4_t);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (n + c < p.N) hrow[n + c] = f32_to_bf16(y[c]);
+                    }
+                }
+        }
+    } else {
+        // all residual pieces of the lane are loaded first (one latency)
+        bf16x4_t res[TM][TN][4];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + i * 32 + (lane & 31);
+            const uint16_t* hrow = (const uint16_t*)p.h + (int64_t)trow[i] * p.N;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = cb + j * 32 + 8 * q;
+                    if (FULL || (m < tl.rows && vec && n < p.N))
+                        res[i][j][q] = *(const bf16x4_t*)(hrow + n);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + i * 32 + (lane & 31);
+            if (!FULL && m >= tl.rows) continue;
+            const int64_t t = trow[i];
+            const uint16_t* hrow = (const uint16_t*)p.h + t * p.N;
+            uint16_t* orow = (uint16_t*)p.out + t * p.N;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = cb + j * 32 + 8 * q;
+                    if (vec) {
+                        if (!FULL && n >= p.N) continue;
+                        const f32x4_t r = __builtin_convertvector(res[i][j][q], f32x4_t);
+                        f32x4_t y;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) y[c] = fmaf(gate[i], acc[i][j][4 * q + c], r[c]);
+                        *(bf16x4_t*)(orow + n) = __builtin_convertvector(y, bf16x4_t);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (n + c < p.N)
+                                orow[n + c] = f32_to_bf16(
+                                    fmaf(gate[i], acc[i][j][4 * q + c], bf16_to_f32(hrow[n + c])));
+                    }
+                }
+        }
+    }
+}
+
+template <int Kind, int TM, int TN>
+BASE_DEV void dma_epilogue(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                           int64_t mw, int64_t nw, int lane, const int32_t (&trow)[TM],
+                           const float (&gate)[TM]) {
+    if ((p.N & 3) == 0 && nw + TN * 32 <= p.N && mw + TM * 32 <= tl.rows)
+        dma_epilogue_rows<Kind, TM, TN, true>(p, acc, tl, mw, nw, lane, trow, gate);
+    else
+        dma_epilogue_rows<Kind, TM, TN, false>(p, acc, tl, mw, nw, lane, trow, gate);
+}
+
+template <int Kind, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p) {
+    static_assert(Kind == KIND_FFN1 || Kind == KIND_FFN2, "expert products only");
     constexpr int BM = 256, BK = 32, S = 4, NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -68,6 +197,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
 
+    // FFN2 epilogue inputs of this lane's rows, fetched now so that their
+    // latency hides behind the prologue's loads
+    int32_t trow[TM];
+    float gate[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        trow[i] = 0;
+        gate[i] = 0.0f;
+        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (Kind == KIND_FFN2 && m < tl.rows) {
+            trow[i] = p.perm[tl.row0 + m];
+            gate[i] = sigmoid_f32(p.s_in[(int64_t)trow[i] * p.E + g]);
+        }
+    }
+
     // this lane's DMA sources (row pointer + chunk offset, or null)
     const uint16_t* asrc[AI];
     const uint16_t* bsrc[BI];
@@ -75,22 +219,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
     for (int j = 0; j < AI; ++j) {
         const int slot = (wave * AI + j) * 64 + lane;
-        const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+        const int row = slot >> 2, c = (slot & 3) ^ swz(row);
         akc[j] = c * 8;
         const int64_t m = m0 + row;
         asrc[j] = nullptr;
         if (m < tl.rows) {
-            int64_t src;
-            if (Kind == KIND_FFN1) src = p.perm[tl.row0 + m];
-            else if (Kind == KIND_FFN2) src = tl.row0 + m;
-            else src = m;
+            const int64_t src = (Kind == KIND_FFN1) ? p.perm[tl.row0 + m] : tl.row0 + m;
             asrc[j] = A + src * p.K + c * 8;
         }
     }
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int slot = (wave * BI + j) * 64 + lane;
-        const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+        const int row = slot >> 2, c = (slot & 3) ^ swz(row);
         bkc[j] = c * 8;
         const int64_t n = n0 + row;
         bsrc[j] = (n < p.N) ? B + n * p.K + c * 8 : nullptr;
@@ -118,12 +259,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = wm * WTM + i * 32 + (lane & 31);
-            fa[kk][i] = (row * 4 + (c ^ ((row >> 2) & 3))) * 16;
+            fa[kk][i] = (row * 4 + (c ^ swz(row))) * 16;
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int row = wn * WTN + j * 32 + (lane & 31);
-            fb[kk][j] = A_BYTES + (row * 4 + (c ^ ((row >> 2) & 3))) * 16;
+            fb[kk][j] = A_BYTES + (row * 4 + (c ^ swz(row))) * 16;
         }
     }
 
@@ -135,105 +276,73 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto load_frags = [&](const char* st, bf16x8_t (&fa_)[2][TM], bf16x8_t (&fb_)[2][TN]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa_[kk][i] = *(const bf16x8_t*)(st + fa[kk][i]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb_[kk][j] = *(const bf16x8_t*)(st + fb[kk][j]);
-        }
-    };
-    auto mfmas = [&](const bf16x8_t (&fa_)[2][TM], const bf16x8_t (&fb_)[2][TN]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[kk][i], fb_[kk][j],
-                                                                         acc[i][j], 0, 0, 0);
-    };
-    const int64_t nk = (p.K + BK - 1) / BK;
-    // wait for K step kt (the loads of the steps issued after it may stay in
-    // flight) and for every wave's reads of the stage about to be refilled
-    auto ready = [&](int64_t kt) {
-        const int64_t rest = nk - 1 - kt;  // K steps issued after kt (at most S - 2)
-        if (rest >= 2) wait_vmcnt<2 * PER>();
-        else if (rest == 1) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the stage refilled next
+    // K steps, padded to whole groups of S. A step at or past K loads the
+    // zero block, so padded steps add nothing; the configurations' K are
+    // multiples of S * BK anyway. Every group issues the same DMAs and waits
+    // on every path: the compiler's own wait insertion, which does not
+    // correlate branch conditions, would otherwise assume on some path that
+    // the stage about to be read is still being filled and drain all DMAs.
+    const int64_t nk = ((p.K + BK * S - 1) / (BK * S)) * S;
+    // wait for the K step about to be read (the two steps issued after it
+    // stay in flight) and for every wave's reads of the stage refilled next
+    auto ready = [&]() {
+        wait_vmcnt<2 * PER>();
+        wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
     };
 
-    if (nk > 0) issue(0, dma_stage<0>());
-    if (nk > 1) issue(1, dma_stage<1>());
-    if (nk > 2) issue(2, dma_stage<2>());
-    if (LAG == 0) {
-        // both 16-deep halves' fragments are read up front so the second
-        // half's reads overlap the first half's MFMAs
-        bf16x8_t af[2][TM], bfr[2][TN];
-        auto compute = [&](const char* st) {
-            load_frags(st, af, bfr);
-            mfmas(af, bfr);
-        };
-        for (int64_t kt = 0; kt < nk; kt += S) {
-            ready(kt);
-            if (kt + 3 < nk) issue(kt + 3, dma_stage<3>());
-            compute(dma_stage<0>());
-            if (kt + 1 < nk) {
-                ready(kt + 1);
-                if (kt + 4 < nk) issue(kt + 4, dma_stage<0>());
-                compute(dma_stage<1>());
-            }
-            if (kt + 2 < nk) {
-                ready(kt + 2);
-                if (kt + 5 < nk) issue(kt + 5, dma_stage<1>());
-                compute(dma_stage<2>());
-            }
-            if (kt + 3 < nk) {
-                ready(kt + 3);
-                if (kt + 6 < nk) issue(kt + 6, dma_stage<2>());
-                compute(dma_stage<3>());
-            }
-        }
-    } else {
-        // step kt: make step kt+1 ready, refill kt's stage with step kt+4,
-        // read step kt+1's fragments, then the MFMAs of step kt
-        bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-        if (nk > 0) {
-            ready(0);
-            load_frags(dma_stage<0>(), a0, b0);
-        }
-        for (int64_t kt = 0; kt < nk; kt += S) {
-            if (kt + 1 < nk) {
-                ready(kt + 1);
-                if (kt + 4 < nk) issue(kt + 4, dma_stage<0>());
-                load_frags(dma_stage<1>(), a1, b1);
-            }
-            mfmas(a0, b0);
-            if (kt + 1 >= nk) break;
-            if (kt + 2 < nk) {
-                ready(kt + 2);
-                if (kt + 5 < nk) issue(kt + 5, dma_stage<1>());
-                load_frags(dma_stage<2>(), a0, b0);
-            }
-            mfmas(a1, b1);
-            if (kt + 2 >= nk) break;
-            if (kt + 3 < nk) {
-                ready(kt + 3);
-                if (kt + 6 < nk) issue(kt + 6, dma_stage<2>());
-                load_frags(dma_stage<3>(), a1, b1);
-            }
-            mfmas(a0, b0);
-            if (kt + 3 >= nk) break;
-            if (kt + 4 < nk) {
-                ready(kt + 4);
-                if (kt + 7 < nk) issue(kt + 7, dma_stage<3>());
-                load_frags(dma_stage<0>(), a0, b0);
-            }
-            mfmas(a1, b1);
-        }
+    issue(0, dma_stage<0>());
+    issue(1, dma_stage<1>());
+    issue(2, dma_stage<2>());
+    issue(3, dma_stage<3>());
+    // Nothing in flight at loop entry either, for the same reason (costs one
+    // load latency per tile, which the first K step waits for anyway).
+    wait_vmcnt<0>();
+
+    // Half-step pipeline: the fragments of the next 16-deep half are read
+    // while the MFMAs of the current half run. A K step's first half is read
+    // right after the barrier that makes the step ready and lands while the
+    // previous step's second half is multiplied, so the matrix cores have
+    // register-resident work across every barrier.
+    bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+    auto load_half = [&](const char* st, int kk, bf16x8_t (&fa_)[TM], bf16x8_t (&fb_)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa_[i] = *(const bf16x8_t*)(st + fa[kk][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb_[j] = *(const bf16x8_t*)(st + fb[kk][j]);
+    };
+    auto mfma_half = [&](const bf16x8_t (&fa_)[TM], const bf16x8_t (&fb_)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
+    };
+    // step kt lives in stage `cur`, step kt+1 in `next`; once every wave has
+    // read `cur` (the barrier in ready), it is refilled with kt+4. The last
+    // step also waits for and reads step nk (zeros), unused. sched_barrier
+    // keeps the compiler from sinking a half's reads below the MFMAs they are
+    // meant to overlap.
+    auto step = [&](int64_t kt, char* cur, char* next) {
+        load_half(cur, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(a0, b0);
+        ready();
+        issue(kt + 4, cur);
+        load_half(next, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(a1, b1);
+    };
+    ready();
+    load_half(dma_stage<0>(), 0, a0, b0);
+    for (int64_t kt = 0; kt < nk; kt += S) {
+        step(kt, dma_stage<0>(), dma_stage<1>());
+        step(kt + 1, dma_stage<1>(), dma_stage<2>());
+        step(kt + 2, dma_stage<2>(), dma_stage<3>());
+        step(kt + 3, dma_stage<3>(), dma_stage<0>());
     }
-    store_tile<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane);
+    // the zero-block loads issued past the last step must land before the
+    // workgroup's LDS is handed to the next one
+    wait_vmcnt<0>();
+    dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
 }
