@@ -402,11 +402,11 @@ static int64_t grid_blocks(const GemmParams& p, int32_t* gblk, int64_t rows_tota
 }
 
 template <int Kind, int BN, int WM, int WN>
-static hipError_t run_dma(const GemmParams& p, int32_t* gblk, int64_t rows_total, hipStream_t st) {
+static hipError_t run_dma64(const GemmParams& p, int32_t* gblk, int64_t rows_total, hipStream_t st) {
     const int64_t tiles = grid_blocks<256, BN>(p, gblk, rows_total, st);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<Kind, BN, WM, WN>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_bf16_dma64_kernel<Kind, BN, WM, WN>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
@@ -438,7 +438,7 @@ hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1, void*
     p.perm = perm; p.b_gstride = F * D; p.H = H; p.act = act;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32<KIND_FFN1>(p, gblk, rows_total, st);
-    return run_dma<KIND_FFN1, 256, 4, 2>(p, gblk, rows_total, st);
+    return run_dma64<KIND_FFN1, 256, 4, 2>(p, gblk, rows_total, st);
 }
 
 hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const float* s,
@@ -450,10 +450,7 @@ hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const
     p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
-    // 256-wide tiles unless that leaves under two workgroups per CU
-    if (((D + 255) / 256) * ((rows_total + 255) / 256) >= 512)
-        return run_dma<KIND_FFN2, 256, 4, 2>(p, gblk, rows_total, st);
-    return run_dma<KIND_FFN2, 128, 4, 2>(p, gblk, rows_total, st);
+    return run_dma64<KIND_FFN2, 256, 4, 2>(p, gblk, rows_total, st);
 }
 
 }  // namespace base

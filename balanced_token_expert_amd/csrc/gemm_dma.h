@@ -1,48 +1,32 @@
 // bf16 MFMA GEMM fed by direct global -> LDS loads (included by gemm.hip,
 // inside namespace base). Used for both expert products.
 //
-// 256 x BN output tile per workgroup of WM x WN waves; K steps of 32 held in
-// 4 LDS stages that global_load_lds (16 bytes per lane) fills three K steps
-// ahead of the MFMAs, so about 96 KB per CU are in flight -- enough to cover
-// HBM latency without registers. Each stage is its own LDS object and the
-// K loop is unrolled by the stage count, so the compiler can tell the stage
-// being read from the stages being filled; the loop waits explicitly for the
-// one K step it is about to use. A row of a stage is 4 chunks of 16 bytes;
-// chunk c of row r sits at position c ^ swz(r), which keeps the fragment
-// reads (32 rows x one chunk per half wave) free of LDS bank conflicts.
-// Lanes whose row or K range lies outside the operand load a 16-byte block
-// of zeros.
+// 256 x BN output tile per workgroup of WM x WN waves; K steps of 64 held in
+// two LDS stages of 64 KB that global_load_lds (16 bytes per lane) fills one
+// step ahead of the MFMAs. A stage row is 128 bytes, so the 8 lanes that fill
+// one row read a whole 128-byte line: half the L2 requests of 32-deep stages
+// for the same bytes (an L2-resident DMA probe moved 27 TB/s this way against
+// 16 TB/s with 64-byte row pieces; in the GEMM the 64-deep stages beat four
+// 32-deep stages with three steps of lead by about 9 %). Each stage is its
+// own LDS object and the K loop is unrolled by the stage count, so the
+// compiler can tell the stage being read from the stage being filled; the
+// loop waits explicitly for the step it is about to use. Chunk c of row r
+// sits at position c ^ swz8(r), which keeps the fragment reads (32 rows x one
+// chunk per half wave) free of LDS bank conflicts. Lanes whose row or K range
+// lies outside the operand load a 16-byte block of zeros.
 //
 // The MFMAs take the weight fragment as their first operand, so each
 // accumulator holds C transposed: a lane owns one output row and runs of 4
 // consecutive columns. The epilogue then writes 8-byte pieces of rows and
 // needs one gate and one token index per row per lane.
 
-constexpr int kDmaStageBytes = (256 + 256) * 32 * 2;
-__shared__ __attribute__((aligned(16))) char g_stage0[kDmaStageBytes];
-__shared__ __attribute__((aligned(16))) char g_stage1[kDmaStageBytes];
-__shared__ __attribute__((aligned(16))) char g_stage2[kDmaStageBytes];
-__shared__ __attribute__((aligned(16))) char g_stage3[kDmaStageBytes];
-
 __device__ __attribute__((aligned(16))) uint4 g_zero16;
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <int S>
-BASE_DEV char* dma_stage() {
-    return S == 0 ? g_stage0 : (S == 1 ? g_stage1 : (S == 2 ? g_stage2 : g_stage3));
-}
-
 BASE_DEV void dma16(const void* src, char* dst) {
     __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
 }
-
-// Chunk swizzle of a stage row. ds_read_b128 serves 16 lanes per pass from
-// 64 banks, and a fragment read gives lanes 0..15 rows r..r+15 at the same
-// logical chunk: rows 4 apart then need different positions. The extra terms
-// also separate rows 2 apart within each group of 8 lanes, which measured
-// about 10 % faster than the 4-apart rule alone on an LDS read probe.
-BASE_DEV int swz(int r) { return ((r >> 1) & 1) ^ (((r >> 2) & 1) << 1) ^ ((r >> 3) & 1); }
 
 // s_waitcnt through the builtin rather than inline asm, so that the
 // compiler's own wait insertion knows which loads have completed; with an
@@ -175,18 +159,32 @@ BASE_DEV void dma_epilogue(const GemmParams& p, f32x16_t (&acc)[TM][TN], const T
         dma_epilogue_rows<Kind, TM, TN, false>(p, acc, tl, mw, nw, lane, trow, gate);
 }
 
+constexpr int kDma64StageBytes = (256 + 256) * 64 * 2;
+__shared__ __attribute__((aligned(16))) char g_d64_0[kDma64StageBytes];
+__shared__ __attribute__((aligned(16))) char g_d64_1[kDma64StageBytes];
+
+template <int S>
+BASE_DEV char* dma64_stage() {
+    return S == 0 ? g_d64_0 : g_d64_1;
+}
+
+// 8 chunks of 16 bytes per row: rows 2 apart differ in bits 1..3 of the row,
+// so 16 consecutive rows (one ds_read_b128 pass) hit 16 distinct bank groups.
+BASE_DEV int swz8(int r) { return (r >> 1) & 7; }
+
 template <int Kind, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p) {
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams p) {
     static_assert(Kind == KIND_FFN1 || Kind == KIND_FFN2, "expert products only");
-    constexpr int BM = 256, BK = 32, S = 4, NT = WM * WN * 64;
+    constexpr int BM = 256, BK = 64, NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int A_BYTES = BM * BK * 2;
-    constexpr int AI = BM * (BK / 8) / NT;  // DMA instructions per wave per stage: A
-    constexpr int BI = BN * (BK / 8) / NT;  //                                      B
-    constexpr int PER = AI + BI;
+    constexpr int ROWB = BK * 2;            // bytes of a stage row
+    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    constexpr int A_BYTES = BM * ROWB;
+    constexpr int AI = BM * CPR / NT;       // DMA instructions per wave per stage: A
+    constexpr int BI = BN * CPR / NT;       //                                      B
     static_assert(AI >= 1 && BI >= 1 && TM >= 1 && TN >= 1, "tile shape");
-    static_assert(A_BYTES + BN * BK * 2 <= kDmaStageBytes, "stage size");
+    static_assert(A_BYTES + BN * ROWB <= kDma64StageBytes, "stage size");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -197,8 +195,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
 
-    // FFN2 epilogue inputs of this lane's rows, fetched now so that their
-    // latency hides behind the prologue's loads
     int32_t trow[TM];
     float gate[TM];
 #pragma unroll
@@ -212,14 +208,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
         }
     }
 
-    // this lane's DMA sources (row pointer + chunk offset, or null)
     const uint16_t* asrc[AI];
     const uint16_t* bsrc[BI];
     int akc[AI], bkc[BI];
 #pragma unroll
     for (int j = 0; j < AI; ++j) {
         const int slot = (wave * AI + j) * 64 + lane;
-        const int row = slot >> 2, c = (slot & 3) ^ swz(row);
+        const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
         akc[j] = c * 8;
         const int64_t m = m0 + row;
         asrc[j] = nullptr;
@@ -231,7 +226,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int slot = (wave * BI + j) * 64 + lane;
-        const int row = slot >> 2, c = (slot & 3) ^ swz(row);
+        const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
         bkc[j] = c * 8;
         const int64_t n = n0 + row;
         bsrc[j] = (n < p.N) ? B + n * p.K + c * 8 : nullptr;
@@ -251,22 +246,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
         }
     };
 
-    // fragment byte offsets inside a stage: [kk][tile]
-    int fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 32 + (lane & 31);
-            fa[kk][i] = (row * 4 + (c ^ swz(row))) * 16;
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int row = wn * WTN + j * 32 + (lane & 31);
-            fb[kk][j] = A_BYTES + (row * 4 + (c ^ swz(row))) * 16;
-        }
-    }
+    // A lane's fragment rows all share bits 1..3 (they differ by multiples of
+    // 32 rows), hence one swizzle term; fragment i / j then sits a fixed
+    // number of bytes after the lane's first row.
+    const int sx = swz8(lane & 31);
+    const int arow0 = (wm * WTM + (lane & 31)) * ROWB;
+    const int brow0 = A_BYTES + (wn * WTN + (lane & 31)) * ROWB;
 
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -276,73 +261,59 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmParams p
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // K steps, padded to whole groups of S. A step at or past K loads the
-    // zero block, so padded steps add nothing; the configurations' K are
-    // multiples of S * BK anyway. Every group issues the same DMAs and waits
-    // on every path: the compiler's own wait insertion, which does not
-    // correlate branch conditions, would otherwise assume on some path that
-    // the stage about to be read is still being filled and drain all DMAs.
-    const int64_t nk = ((p.K + BK * S - 1) / (BK * S)) * S;
-    // wait for the K step about to be read (the two steps issued after it
-    // stay in flight) and for every wave's reads of the stage refilled next
+    // K steps of 64, padded to an even count (zero blocks past K)
+    const int64_t nk = ((p.K + 2 * BK - 1) / (2 * BK)) * 2;
+    // wait for the step about to be read (the only one in flight) and for
+    // every wave's reads of the stage refilled next
     auto ready = [&]() {
-        wait_vmcnt<2 * PER>();
+        wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
     };
 
-    issue(0, dma_stage<0>());
-    issue(1, dma_stage<1>());
-    issue(2, dma_stage<2>());
-    issue(3, dma_stage<3>());
-    // Nothing in flight at loop entry either, for the same reason (costs one
-    // load latency per tile, which the first K step waits for anyway).
-    wait_vmcnt<0>();
-
-    // Half-step pipeline: the fragments of the next 16-deep half are read
-    // while the MFMAs of the current half run. A K step's first half is read
-    // right after the barrier that makes the step ready and lands while the
-    // previous step's second half is multiplied, so the matrix cores have
-    // register-resident work across every barrier.
     bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-    auto load_half = [&](const char* st, int kk, bf16x8_t (&fa_)[TM], bf16x8_t (&fb_)[TN]) {
+    // sub-step s (16 deep) of the stage at st: chunk 2s + lane/32
+    auto load_sub = [&](const char* st, int s, bf16x8_t (&fa_)[TM], bf16x8_t (&fb_)[TN]) {
+        const int co = ((2 * s + (lane >> 5)) ^ sx) * 16;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa_[i] = *(const bf16x8_t*)(st + fa[kk][i]);
+        for (int i = 0; i < TM; ++i) fa_[i] = *(const bf16x8_t*)(st + arow0 + co + i * 32 * ROWB);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb_[j] = *(const bf16x8_t*)(st + fb[kk][j]);
+        for (int j = 0; j < TN; ++j) fb_[j] = *(const bf16x8_t*)(st + brow0 + co + j * 32 * ROWB);
     };
-    auto mfma_half = [&](const bf16x8_t (&fa_)[TM], const bf16x8_t (&fb_)[TN]) {
+    auto mfma_sub = [&](const bf16x8_t (&fa_)[TM], const bf16x8_t (&fb_)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
     };
-    // step kt lives in stage `cur`, step kt+1 in `next`; once every wave has
-    // read `cur` (the barrier in ready), it is refilled with kt+4. The last
-    // step also waits for and reads step nk (zeros), unused. sched_barrier
-    // keeps the compiler from sinking a half's reads below the MFMAs they are
-    // meant to overlap.
+    // step kt in stage `cur`, kt+1 in `next` (issued one step earlier); the
+    // fragments of sub-step s+1 are read while sub-step s is multiplied
     auto step = [&](int64_t kt, char* cur, char* next) {
-        load_half(cur, 1, a1, b1);
+        load_sub(cur, 1, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(a0, b0);
+        mfma_sub(a0, b0);
+        load_sub(cur, 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a1, b1);
+        load_sub(cur, 3, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a0, b0);
         ready();
-        issue(kt + 4, cur);
-        load_half(next, 0, a0, b0);
+        issue(kt + 2, cur);
+        load_sub(next, 0, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(a1, b1);
+        mfma_sub(a1, b1);
     };
+
+    issue(0, dma64_stage<0>());
+    issue(1, dma64_stage<1>());
     ready();
-    load_half(dma_stage<0>(), 0, a0, b0);
-    for (int64_t kt = 0; kt < nk; kt += S) {
-        step(kt, dma_stage<0>(), dma_stage<1>());
-        step(kt + 1, dma_stage<1>(), dma_stage<2>());
-        step(kt + 2, dma_stage<2>(), dma_stage<3>());
-        step(kt + 3, dma_stage<3>(), dma_stage<0>());
+    load_sub(dma64_stage<0>(), 0, a0, b0);
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        step(kt, dma64_stage<0>(), dma64_stage<1>());
+        step(kt + 1, dma64_stage<1>(), dma64_stage<0>());
     }
-    // the zero-block loads issued past the last step must land before the
-    // workgroup's LDS is handed to the next one
     wait_vmcnt<0>();
     dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
 }

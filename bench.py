@@ -45,14 +45,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99995
+FETCH_SCALE = 1.99994
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "fdcc25bae966ce76f47afe135e2545629f928e14601fa447eb183f0e60cb4423",
-             2369202.2, 1114112.0),
-    "ffn2": ("large_t64k_e128_d2048", "fdcc25bae966ce76f47afe135e2545629f928e14601fa447eb183f0e60cb4423",
-             2812228.4, 278543.2),
+    "ffn1": ("large_t64k_e128_d2048", "28e4bbd3df52e8673122e0f686215679678c7925e24de2690c9f5854017aa03b",
+             2397531.0, 1185960.8),
+    "ffn2": ("large_t64k_e128_d2048", "28e4bbd3df52e8673122e0f686215679678c7925e24de2690c9f5854017aa03b",
+             2780553.4, 306317.9),
 }
 
 
