@@ -47,8 +47,11 @@ constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
 constexpr int32_t kNoTok = 0x7fffffff;
 
-// lowest-holder list length per expert (LDS budget of the tail)
-static int low_len(int64_t E) { return E <= 256 ? 16 : (E <= 512 ? 8 : 4); }
+// lowest-holder list length per expert (LDS budget of the tail; at most 64,
+// one entry per lane). A longer list means fewer rebuilds from the slots.
+static int low_len(int64_t E) {
+    return E <= 64 ? 64 : (E <= 128 ? 32 : (E <= 256 ? 16 : (E <= 512 ? 8 : 4)));
+}
 
 struct AucCtl {
     int32_t cur;          // bidder list in use (0/1)
@@ -354,6 +357,78 @@ BASE_DEV void wave_sort_best(double& b, int& t, int lane) {
     }
 }
 
+// Sort cb/ct[0, n) best first (n <= 2048, arrays of the next power of two
+// at least 64): each wave sorts runs of 64 in registers, then runs are merged
+// pairwise by rank (an element's place = its index in its run + the partner
+// run's elements ahead of it; ties between runs go to the left run),
+// ping-ponging with ob/ot. Called by every thread of the block.
+BASE_DEV void block_sort_best(double* cb, int32_t* ct, double* ob, int32_t* ot, int n) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    int P = 64;
+    while (P < n) P <<= 1;
+    for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
+    __syncthreads();
+    const int wv = tid >> 6, nwv = blockDim.x >> 6;
+    for (int r = wv; r < P / 64; r += nwv) {
+        double b = cb[r * 64 + lane];
+        int t = ct[r * 64 + lane];
+        wave_sort_best(b, t, lane);
+        cb[r * 64 + lane] = b;
+        ct[r * 64 + lane] = t;
+    }
+    __syncthreads();
+    double* sb = cb;
+    int32_t* st = ct;
+    double* db = ob;
+    int32_t* dt = ot;
+    for (int len = 64; len < P; len <<= 1) {
+        for (int i = tid; i < P; i += blockDim.x) {
+            const int run = i / len, pos = i - run * len;
+            const int other = (run ^ 1) * len;
+            const double b = sb[i];
+            const int t = st[i];
+            int lo = 0, hi = len;  // partner elements ahead of this one
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                const double pb = sb[other + mid];
+                const int pt = st[other + mid];
+                const bool ahead = (run & 1) ? !better(b, t, pb, pt) : better(pb, pt, b, t);
+                if (ahead) lo = mid + 1;
+                else hi = mid;
+            }
+            const int at = (run & ~1) * len + pos + lo;
+            db[at] = b;
+            dt[at] = t;
+        }
+        __syncthreads();
+        double* xb = sb; sb = db; db = xb;
+        int32_t* xt = st; st = dt; dt = xt;
+    }
+    if (sb != cb) {
+        for (int i = tid; i < P; i += blockDim.x) { cb[i] = sb[i]; ct[i] = st[i]; }
+        __syncthreads();
+    }
+}
+
+// An expert's lowest holders in eviction order (slots m-1, m-2, ... of its
+// best-first slots), its count, list state and price.
+BASE_DEV void publish_expert(AucWs& w, int e, int64_t k, int m, const double* hb,
+                             const int32_t* ht) {
+    const int L = w.L;
+    const int nl = min(m, L);
+    for (int i = threadIdx.x; i < nl; i += blockDim.x) {
+        w.lowb[(int64_t)e * L + i] = hb[m - 1 - i];
+        w.lowt[(int64_t)e * L + i] = ht[m - 1 - i];
+        w.lows[(int64_t)e * L + i] = m - 1 - i;
+    }
+    if (threadIdx.x == 0) {
+        w.cnt[e] = m;
+        w.nlow[e] = nl;
+        w.comp[e] = (m <= L) ? 1 : 0;
+        w.pi[e] = (m == k) ? hb[k - 1] : w.floor_[e];
+    }
+}
+
 __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
                                                                AucWs w) {
     __shared__ double cb[kResolveCap];   // bidders
@@ -388,59 +463,8 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         }
     };
     // merge the n gathered bidders into the holders
-    // sort cb/ct[0, n) best first (n <= kResolveCap): each wave sorts runs of
-    // 64 in registers, then runs are merged pairwise by rank (an element's
-    // place = its index in its run + the partner run's elements ahead of it;
-    // ties between runs go to the left run), ping-ponging with ob/ot
-    auto sort_bidders = [&](int n) {
-        int P = 64;
-        while (P < n) P <<= 1;
-        for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
-        __syncthreads();
-        const int wv = tid >> 6, nwv = blockDim.x >> 6;
-        for (int r = wv; r < P / 64; r += nwv) {
-            double b = cb[r * 64 + lane];
-            int t = ct[r * 64 + lane];
-            wave_sort_best(b, t, lane);
-            cb[r * 64 + lane] = b;
-            ct[r * 64 + lane] = t;
-        }
-        __syncthreads();
-        double* sb = cb;
-        int32_t* st = ct;
-        double* db = ob;
-        int32_t* dt = ot;
-        for (int len = 64; len < P; len <<= 1) {
-            for (int i = tid; i < P; i += blockDim.x) {
-                const int run = i / len, pos = i - run * len;
-                const int other = (run ^ 1) * len;
-                const double b = sb[i];
-                const int t = st[i];
-                int lo = 0, hi = len;  // partner elements ahead of this one
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    const double pb = sb[other + mid];
-                    const int pt = st[other + mid];
-                    const bool ahead = (run & 1) ? !better(b, t, pb, pt) : better(pb, pt, b, t);
-                    if (ahead) lo = mid + 1;
-                    else hi = mid;
-                }
-                const int at = (run & ~1) * len + pos + lo;
-                db[at] = b;
-                dt[at] = t;
-            }
-            __syncthreads();
-            double* xb = sb; sb = db; db = xb;
-            int32_t* xt = st; st = dt; dt = xt;
-        }
-        if (sb != cb) {
-            for (int i = tid; i < P; i += blockDim.x) { cb[i] = sb[i]; ct[i] = st[i]; }
-            __syncthreads();
-        }
-    };
-    // merge the n gathered bidders into the holders
     auto merge = [&](int n) {
-        sort_bidders(n);
+        block_sort_best(cb, ct, ob, ot, n);
         const int c = nhold;
         // holder i moves to i + (bidders better than it)
         for (int i0 = 0; i0 < c; i0 += blockDim.x) {
@@ -544,19 +568,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     if (changed) {
         const int m = nhold;
         for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
-        // lowest holders in eviction order: slot m-1, m-2, ...
-        const int nl = min(m, L);
-        for (int i = tid; i < nl; i += blockDim.x) {
-            w.lowb[(int64_t)e * L + i] = hb[m - 1 - i];
-            w.lowt[(int64_t)e * L + i] = ht[m - 1 - i];
-            w.lows[(int64_t)e * L + i] = m - 1 - i;
-        }
-        if (tid == 0) {
-            w.cnt[e] = m;
-            w.nlow[e] = nl;
-            w.comp[e] = (m <= L) ? 1 : 0;
-            w.pi[e] = (m == k) ? hb[k - 1] : w.floor_[e];
-        }
+        publish_expert(w, e, k, m, hb, ht);
     }
     __syncthreads();
     if (tid == 0) {

@@ -351,9 +351,9 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                     // pop the lowest holder (lane 0 of the list)
                     victim = readlane_i32(lt, 0);
                     slot = readlane_i32(ls, 0);
-                    const double nb_ = dpp_f64<kDppShl1>(lb);
-                    const int nt = dpp_i32<kDppShl1>(lt);
-                    const int ns = dpp_i32<kDppShl1>(ls);
+                    const double nb_ = dpp_f64<kDppWaveShl1>(lb);
+                    const int nt = dpp_i32<kDppWaveShl1>(lt);
+                    const int ns = dpp_i32<kDppWaveShl1>(ls);
                     if (lane + 1 < nl) { lb = nb_; lt = nt; ls = ns; }
                     else { lb = DBL_MAX; lt = kNoTok; ls = -1; }
                     --nl;
@@ -368,9 +368,9 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                 const bool before = lane < nl && evict_first(lb, lt, beta, t);
                 const int pos = __popcll(__ballot(before));
                 if ((nl < L && cp) || pos < nl) {
-                    const double pb_ = dpp_f64<kDppShr1>(lb);
-                    const int pt_ = dpp_i32<kDppShr1>(lt);
-                    const int ps = dpp_i32<kDppShr1>(ls);
+                    const double pb_ = dpp_f64<kDppWaveShr1>(lb);
+                    const int pt_ = dpp_i32<kDppWaveShr1>(lt);
+                    const int ps = dpp_i32<kDppWaveShr1>(ls);
                     if (lane == pos) { lb = beta; lt = t; ls = slot; }
                     else if (lane > pos) { lb = pb_; lt = pt_; ls = ps; }
                     if (nl == L) cp = 0;  // the old last entry dropped out

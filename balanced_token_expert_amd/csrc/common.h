@@ -88,8 +88,8 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16
-constexpr int kDppShl1 = 0x101;       // lane i <- i+1 within a row of 16
-constexpr int kDppShr1 = 0x111;       // lane i <- i-1 within a row of 16
+constexpr int kDppWaveShl1 = 0x130;   // lane i <- i+1 across the wave (lane 63: old value)
+constexpr int kDppWaveShr1 = 0x138;   // lane i <- i-1 across the wave (lane 0: old value)
 constexpr int kDppRowBcast0 = 0x150;  // every lane <- lane 0 of its row of 16
 constexpr int kDppBcast15 = 0x142;    // row r <- lane 15 of row r-1 (rows in the row mask)
 constexpr int kDppBcast31 = 0x143;    // rows 2, 3 <- lane 31 (rows in the row mask)
