@@ -45,14 +45,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99994
+FETCH_SCALE = 1.99995
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "28e4bbd3df52e8673122e0f686215679678c7925e24de2690c9f5854017aa03b",
-             2397531.0, 1185960.8),
-    "ffn2": ("large_t64k_e128_d2048", "28e4bbd3df52e8673122e0f686215679678c7925e24de2690c9f5854017aa03b",
-             2780553.4, 306317.9),
+    "ffn1": ("large_t64k_e128_d2048", "e24a68db278f7feb79e8f56226b2ec2ee4f7c0266f83c5114b6a1e944e9e8062",
+             2397259.8, 1188216.9),
+    "ffn2": ("large_t64k_e128_d2048", "e24a68db278f7feb79e8f56226b2ec2ee4f7c0266f83c5114b6a1e944e9e8062",
+             2785302.6, 307358.4),
 }
 
 
