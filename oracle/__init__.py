@@ -20,7 +20,7 @@ invariants or an independent library routine.
 from .reference import (  # noqa: F401
     affinity, sanitize, greedy_route, canonical_perm, layer_forward,
     expert_ffn, gelu, sigmoid, dual_value, eps_cs_violation, objective,
-    counts_of,
+    counts_of, layer_norm, expert_blocks, layer_forward_ex,
 )
 from .solvers import (  # noqa: F401
     auction, hungarian, cycle_cancel, min_cycle_gap, exact_assignment,

@@ -146,3 +146,88 @@ def layer_forward(h, w, W1, W2, a, act: str, experts=None, s=None):
             g = sigmoid(np.asarray(s, dtype=np.float64)[rows, e])
         out[rows] = g[:, None] * expert_ffn(x, w1, w2, act) + x
     return out
+
+
+# ---------------------------------------------------------------- layer variants
+# The released code mixes with a convex blend, and the paper's experts are
+# stacks of feed-forward blocks (sec. 4.1; the "Paper vs code" notes list
+# both differences). These definitions serve base_layer_forward_ex.
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """Layer norm over the last axis: (x - mean) / sqrt(var + eps) * gamma
+    + beta, with the population (biased) variance; gamma = 1 and beta = 0
+    when not given. Parity: pinned against torch's layer_norm in fp64 and
+    by its invariances (tests/test_oracle_variants.py)."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    y = (x - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)
+    return y
+
+
+def expert_blocks(x, W1s, W2s, act: str, gammas=None, betas=None, ln_eps: float = 1e-5):
+    """Sec. 4.1's expert: N feed-forward blocks, each with layer norm, the
+    projection up, the activation, the projection back and a residual
+    connection: x <- x + W2_n act(W1_n LN_n(x)), n = 0 .. N-1. W1s / W2s /
+    gammas / betas are sequences over n (gammas, betas may be None or hold
+    None). Parity: pinned against the same block built from torch.nn modules
+    in fp64, and by structural cases (zero second projections)."""
+    x = np.asarray(x, dtype=np.float64)
+    for n in range(len(W1s)):
+        g = None if gammas is None else gammas[n]
+        b = None if betas is None else betas[n]
+        x = x + expert_ffn(layer_norm(x, g, b, ln_eps), W1s[n], W2s[n], act)
+    return x
+
+
+def layer_forward_ex(h, w, W1, W2, a, act: str, mix: str = "residual", sublayers: int = 0,
+                     gamma=None, beta=None, ln_eps: float = 1e-5, experts=None, s=None):
+    """BASE layer with the variants of the released code and sec. 4.1:
+
+      y_t = g f_{a_t}(h_t) + h_t          (mix "residual", eq. 1)
+      y_t = g f_{a_t}(h_t) + (1 - g) h_t  (mix "convex", the released code)
+
+    with g = sigma(h_t . w_{a_t}) (or of ``s``). sublayers = 0: f_e is the
+    plain W2 act(W1 x) of ``layer_forward`` (W1, W2 indexed [e] or callables
+    e -> matrix); sublayers = N >= 1: f_e = expert_blocks with N blocks (W1,
+    W2 indexed [n][e] or callables (n, e) -> matrix; gamma, beta N x E x D or
+    None). Rows of experts not in ``experts`` are NaN. Parity: reduces to the
+    pinned ``layer_forward`` for residual / 0 sublayers; the convex mix is
+    pinned by its gate-to-0 and gate-to-1 limits."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    a = np.asarray(a, dtype=np.int64)
+    T, D = h.shape
+    E = w.shape[0]
+    out = np.full((T, D), np.nan)
+    todo = range(E) if experts is None else experts
+    for e in todo:
+        rows = np.nonzero(a == e)[0]
+        if rows.size == 0:
+            continue
+        x = h[rows]
+        if s is None:
+            g = sigmoid(x @ w[e])
+        else:
+            g = sigmoid(np.asarray(s, dtype=np.float64)[rows, e])
+        if sublayers == 0:
+            w1 = W1(e) if callable(W1) else W1[e]
+            w2 = W2(e) if callable(W2) else W2[e]
+            f = expert_ffn(x, w1, w2, act)
+        else:
+            w1s = [W1(n, e) if callable(W1) else W1[n][e] for n in range(sublayers)]
+            w2s = [W2(n, e) if callable(W2) else W2[n][e] for n in range(sublayers)]
+            gs = None if gamma is None else [gamma[n][e] for n in range(sublayers)]
+            bs = None if beta is None else [beta[n][e] for n in range(sublayers)]
+            f = expert_blocks(x, w1s, w2s, act, gs, bs, ln_eps)
+        if mix == "residual":
+            out[rows] = g[:, None] * f + x
+        elif mix == "convex":
+            out[rows] = g[:, None] * f + (1.0 - g[:, None]) * x
+        else:
+            raise ValueError(f"unknown mix {mix!r}")
+    return out
