@@ -23,15 +23,23 @@ BASE_F32, BASE_BF16 = 0, 1
 BASE_ACT_RELU, BASE_ACT_GELU = 0, 1
 BASE_ROUTE_BALANCED, BASE_ROUTE_GREEDY, BASE_ROUTE_GIVEN = 0, 1, 2
 BASE_OP_AFFINITY, BASE_OP_AUCTION, BASE_OP_GREEDY, BASE_OP_LAYER = 0, 1, 2, 3
+BASE_OP_LAYER_EX = 4
+BASE_MIX_RESIDUAL, BASE_MIX_CONVEX = 0, 1
 EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
             "base_assign_auction", "base_route_greedy", "base_layer_forward",
-            "base_set_phase_events")
+            "base_layer_forward_ex", "base_set_phase_events")
 STATS_BYTES = 8 + 16 * 8 * 2
 
 
 class AuctionCfg(ctypes.Structure):
     _fields_ = [("eps_start", ctypes.c_double), ("eps_end", ctypes.c_double),
                 ("eps_factor", ctypes.c_double), ("max_bids", ctypes.c_int64)]
+
+
+class LayerOpts(ctypes.Structure):
+    _fields_ = [("mix", ctypes.c_int32), ("sublayers", ctypes.c_int32),
+                ("ln_eps", ctypes.c_double), ("ln_gamma", ctypes.c_void_p),
+                ("ln_beta", ctypes.c_void_p)]
 
 
 class BaseError(RuntimeError):
@@ -63,9 +71,12 @@ def load(path: str = LIB_PATH):
     lib.base_route_greedy.argtypes = [P, i64, i64, P, P, P, P, P, ctypes.c_size_t, P]
     lib.base_layer_forward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, i32,
                                        AuctionCfg, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.base_layer_forward_ex.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, i32,
+                                          AuctionCfg, P, P, P, P, P, ctypes.POINTER(LayerOpts),
+                                          P, ctypes.c_size_t, P]
     lib.base_set_phase_events.argtypes = [P, i32]
     for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
-              "base_set_phase_events"):
+              "base_layer_forward_ex", "base_set_phase_events"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -209,6 +220,44 @@ def base_layer_forward(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = None, 
                                    mode, c, _ptr(assign), _ptr(scores), _ptr(perm), _ptr(out),
                                    _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "base_layer_forward")
+    return {"out": out, "assign": assign, "scores": scores, "perm": perm, "stats": stats}
+
+
+def base_layer_forward_ex(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = None, mix: int = 0,
+                          sublayers: int = 0, ln_gamma=None, ln_beta=None, ln_eps: float = 1e-5,
+                          assign=None, scores=None, perm=None, out=None, stats=None, ws=None,
+                          stream=None, want_scores=True):
+    """The layer variants: W1 / W2 are E x F x D / E x D x F (sublayers = 0)
+    or N x E x F x D / N x E x D x F; ln_gamma / ln_beta N x E x D fp32 or
+    None."""
+    _dev(h, w, W1, W2, assign, scores, perm, out, ln_gamma, ln_beta)
+    for t in (ln_gamma, ln_beta):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("layer-norm parameters are fp32")
+    T, D = h.shape
+    E = w.shape[0]
+    F = W1.shape[-2]
+    dev = h.device
+    dt = _dt(h)
+    c = cfg() if c is None else c
+    if assign is None:
+        if mode == BASE_ROUTE_GIVEN:
+            raise ValueError("GIVEN routing needs an assignment")
+        assign = torch.empty(T, dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((T, E), dtype=torch.float32, device=dev)
+    perm = torch.empty(T, dtype=torch.int32, device=dev) if perm is None else perm
+    out = torch.empty_like(h) if out is None else out
+    stats = new_stats(dev) if stats is None else stats
+    ws = workspace(BASE_OP_LAYER_EX, T, E, D, F, dt, device=dev) if ws is None else ws
+    opts = LayerOpts(int(mix), int(sublayers), float(ln_eps),
+                     None if ln_gamma is None else ln_gamma.data_ptr(),
+                     None if ln_beta is None else ln_beta.data_ptr())
+    rc = load().base_layer_forward_ex(_ptr(h), _ptr(w), _ptr(W1), _ptr(W2), T, E, D, F, dt, act,
+                                      mode, c, _ptr(assign), _ptr(scores), _ptr(perm), _ptr(out),
+                                      _ptr(stats), ctypes.byref(opts), _ptr(ws), ws.numel(),
+                                      _stream(stream))
+    _check(rc, "base_layer_forward_ex")
     return {"out": out, "assign": assign, "scores": scores, "perm": perm, "stats": stats}
 
 

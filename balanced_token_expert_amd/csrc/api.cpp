@@ -14,17 +14,17 @@ namespace {
 constexpr int64_t kMaxT = int64_t(1) << 24;  // int32 token ids and offsets
 constexpr int64_t kMaxE = 1024;              // auction keeps E prices per lane group
 constexpr int kMaxPhases = 64;
+constexpr int kMaxSublayers = 64;
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout shared by base_workspace_bytes and the entry points.
 struct Layout {
     size_t scan = 0, stats = 0, prices = 0, scores = 0, perm = 0, offsets = 0, hidden = 0,
-           auction = 0, permws = 0, assign = 0, gblk = 0, total = 0;
+           auction = 0, permws = 0, assign = 0, gblk = 0, xbuf = 0, ybuf = 0, total = 0;
 };
 
 Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
-    (void)D;
     Layout L;
     size_t off = 0;
     auto take = [&](size_t& slot, size_t bytes) {
@@ -46,11 +46,16 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
     }
     take(L.prices, (size_t)E * 8);
     take(L.offsets, (size_t)(E + 1) * 4);
-    if (op == BASE_OP_LAYER) {
+    if (op == BASE_OP_LAYER || op == BASE_OP_LAYER_EX) {
+        const size_t b = dt == BASE_BF16 ? 2 : 4;
         take(L.scores, (size_t)T * E * 4);
         take(L.perm, (size_t)T * 4);
-        take(L.hidden, (size_t)T * F * (dt == BASE_BF16 ? 2 : 4));
+        take(L.hidden, (size_t)T * F * b);
         take(L.gblk, (size_t)(E + 1) * 4);
+        if (op == BASE_OP_LAYER_EX) {
+            take(L.xbuf, (size_t)T * D * b);  // an expert's running block output
+            take(L.ybuf, (size_t)T * D * b);  // its layer-norm output
+        }
     }
     // the auction's own scratch, followed by the grouping's
     take(L.auction, auction_ws_bytes(T, E) + perm_ws_bytes(T, E));
@@ -86,6 +91,112 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? BASE_OK : BASE_ERR_HIP; }
 
 }  // namespace
 
+// Shared body of base_layer_forward (o == nullptr: eq. 1, plain experts)
+// and base_layer_forward_ex.
+static int layer_forward(const void* h, const void* w, const void* W1, const void* W2, int64_t T,
+                         int64_t E, int64_t D, int64_t F, int dt, int act, int mode,
+                         base_auction_cfg cfg, int32_t* assign, float* scores, int32_t* perm,
+                         void* out, base_auction_stats* stats, const base_layer_opts* o,
+                         void* ws, size_t ws_bytes, base_stream_t stream) {
+    if (!h || !w || !W1 || !W2 || !assign || !out) return BASE_ERR_INVALID_ARG;
+    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
+    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
+    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
+    if (mode != BASE_ROUTE_BALANCED && mode != BASE_ROUTE_GREEDY && mode != BASE_ROUTE_GIVEN)
+        return BASE_ERR_INVALID_ARG;
+    const int mix = o ? o->mix : BASE_MIX_RESIDUAL;
+    const int nsub = o ? o->sublayers : 0;
+    if (mix != BASE_MIX_RESIDUAL && mix != BASE_MIX_CONVEX) return BASE_ERR_INVALID_ARG;
+    if (nsub < 0 || nsub > kMaxSublayers) return BASE_ERR_INVALID_ARG;
+    if (nsub > 0 && !(o->ln_eps >= 0) ) return BASE_ERR_INVALID_ARG;
+    if (mode == BASE_ROUTE_BALANCED && cfg_phases(cfg) < 0) return BASE_ERR_INVALID_ARG;
+    if (mode != BASE_ROUTE_GREEDY && T % E) return BASE_ERR_INDIVISIBLE;
+    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
+    if (dt == BASE_BF16 && (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) ||
+                            misaligned(W1) || misaligned(W2) || misaligned(out)))
+        return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(o ? BASE_OP_LAYER_EX : BASE_OP_LAYER, T, E, D, F, dt);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    const int64_t k = T / E;
+    ScoreScan* scan = (ScoreScan*)(W + L.scan);
+    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
+    float* s = scores ? scores : (float*)(W + L.scores);
+    int32_t* pm = perm ? perm : (int32_t*)(W + L.perm);
+    int32_t* offs = (int32_t*)(W + L.offsets);
+    double* prices = (double*)(W + L.prices);
+    void* H = W + L.hidden;
+    int32_t* gblk = (int32_t*)(W + L.gblk);
+    // greedy routing gives ragged expert groups (rows offs[e] .. offs[e+1]-1)
+    const int32_t* goff = (mode == BASE_ROUTE_GREEDY) ? offs : nullptr;
+
+    mark(0, st);
+    hipError_t e = launch_scan_init(scan, st);
+    if (e == hipSuccess) e = launch_affinity(h, w, s, T, E, D, dt, scan, st);
+    mark(1, st);
+    if (e == hipSuccess) {
+        if (mode == BASE_ROUTE_BALANCED) {
+            e = launch_auction(s, T, E, cfg.eps_start, cfg.eps_end, cfg.eps_factor, cfg.max_bids,
+                               scan, assign, pm, offs, prices, sd, W + L.auction, st);
+        } else if (mode == BASE_ROUTE_GREEDY) {
+            e = launch_stats_reset(sd, st);
+            if (e == hipSuccess) e = launch_greedy(s, T, E, scan, assign, nullptr, st);
+            if (e == hipSuccess)
+                e = launch_perm(assign, T, E, pm, offs, nullptr, 0, nullptr, W + L.permws, st);
+        } else {
+            e = launch_stats_reset(sd, st);
+            if (e == hipSuccess)
+                e = launch_perm(assign, T, E, pm, offs, nullptr, k, &sd->status, W + L.permws, st);
+        }
+    }
+    mark(2, st);
+    if (nsub == 0) {
+        if (e == hipSuccess) e = launch_ffn1(h, pm, W1, H, E, k, D, F, dt, act, goff, gblk, T, st);
+        mark(3, st);
+        if (e == hipSuccess) {
+            if (mix == BASE_MIX_RESIDUAL) {
+                e = launch_ffn2(H, pm, W2, s, h, out, E, k, D, F, dt, goff, gblk, T, st);
+            } else {
+                const Ffn2Epi epi = {0, 1, 0, nullptr, nullptr};  // g C + (1 - g) h
+                e = launch_ffn2_ex(H, pm, W2, s, h, out, E, k, D, F, dt, goff, gblk, T, epi, st);
+            }
+        }
+    } else {
+        // sec. 4.1 experts: blocks x <- x + W2_n act(W1_n LN_n(x)); block 0
+        // reads the token rows through perm, later blocks the grouped running
+        // output X (updated in place: each element is read and rewritten by
+        // the lane that owns it); the last block mixes into out
+        const size_t b = dt == BASE_BF16 ? 2 : 4;
+        void* X = W + L.xbuf;
+        void* Y = W + L.ybuf;
+        for (int n = 0; n < nsub && e == hipSuccess; ++n) {
+            const float* ga = o->ln_gamma ? o->ln_gamma + (size_t)n * E * D : nullptr;
+            const float* be = o->ln_beta ? o->ln_beta + (size_t)n * E * D : nullptr;
+            const char* w1 = (const char*)W1 + (size_t)n * E * F * D * b;
+            const char* w2 = (const char*)W2 + (size_t)n * E * D * F * b;
+            e = launch_layernorm(n == 0 ? h : X, n == 0, pm, assign, ga, be, o->ln_eps, Y, T, E,
+                                 D, dt, st);
+            if (e == hipSuccess)
+                e = launch_ffn1(Y, nullptr, w1, H, E, k, D, F, dt, act, goff, gblk, T, st);
+            if (n == nsub - 1) mark(3, st);
+            if (e != hipSuccess) break;
+            const int res = n == 0 ? 1 : 2;  // R = x (block 0) or X
+            if (n < nsub - 1) {
+                const Ffn2Epi epi = {1, 2, res, X, X};  // X = R + C, grouped
+                e = launch_ffn2_ex(H, pm, w2, s, h, out, E, k, D, F, dt, goff, gblk, T, epi, st);
+            } else {
+                const int keep = mix == BASE_MIX_CONVEX ? 1 : 0;
+                const Ffn2Epi epi = {0, keep, res, X, nullptr};  // g (R + C) + c2 x
+                e = launch_ffn2_ex(H, pm, w2, s, h, out, E, k, D, F, dt, goff, gblk, T, epi, st);
+            }
+        }
+    }
+    mark(4, st);
+    mark(5, st);
+    return hip_rc(e);
+}
+
 extern "C" {
 
 const char* base_strerror(int code) {
@@ -111,8 +222,8 @@ int base_set_phase_events(void** events, int n) {
 }
 
 size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dtype) {
-    if (T <= 0 || E <= 0 || op < 0 || op > BASE_OP_LAYER) return 0;
-    if (op == BASE_OP_LAYER && F <= 0) return 0;
+    if (T <= 0 || E <= 0 || op < 0 || op > BASE_OP_LAYER_EX) return 0;
+    if ((op == BASE_OP_LAYER || op == BASE_OP_LAYER_EX) && (F <= 0 || D <= 0)) return 0;
     return layout(op, T, E, D, F, dtype).total;
 }
 
@@ -176,60 +287,18 @@ int base_layer_forward(const void* h, const void* w, const void* W1, const void*
                        base_auction_cfg cfg, int32_t* assign, float* scores, int32_t* perm,
                        void* out, base_auction_stats* stats, void* ws, size_t ws_bytes,
                        base_stream_t stream) {
-    if (!h || !w || !W1 || !W2 || !assign || !out) return BASE_ERR_INVALID_ARG;
-    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
-    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
-    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
-    if (mode != BASE_ROUTE_BALANCED && mode != BASE_ROUTE_GREEDY && mode != BASE_ROUTE_GIVEN)
-        return BASE_ERR_INVALID_ARG;
-    if (mode == BASE_ROUTE_BALANCED && cfg_phases(cfg) < 0) return BASE_ERR_INVALID_ARG;
-    if (mode != BASE_ROUTE_GREEDY && T % E) return BASE_ERR_INDIVISIBLE;
-    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
-    if (dt == BASE_BF16 && (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) ||
-                            misaligned(W1) || misaligned(W2) || misaligned(out)))
-        return BASE_ERR_UNSUPPORTED;
-    const Layout L = layout(BASE_OP_LAYER, T, E, D, F, dt);
-    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    char* W = (char*)ws;
-    const int64_t k = T / E;
-    ScoreScan* scan = (ScoreScan*)(W + L.scan);
-    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
-    float* s = scores ? scores : (float*)(W + L.scores);
-    int32_t* pm = perm ? perm : (int32_t*)(W + L.perm);
-    int32_t* offs = (int32_t*)(W + L.offsets);
-    double* prices = (double*)(W + L.prices);
-    void* H = W + L.hidden;
-    int32_t* gblk = (int32_t*)(W + L.gblk);
-    // greedy routing gives ragged expert groups (rows offs[e] .. offs[e+1]-1)
-    const int32_t* goff = (mode == BASE_ROUTE_GREEDY) ? offs : nullptr;
+    return layer_forward(h, w, W1, W2, T, E, D, F, dt, act, mode, cfg, assign, scores, perm, out,
+                         stats, nullptr, ws, ws_bytes, stream);
+}
 
-    mark(0, st);
-    hipError_t e = launch_scan_init(scan, st);
-    if (e == hipSuccess) e = launch_affinity(h, w, s, T, E, D, dt, scan, st);
-    mark(1, st);
-    if (e == hipSuccess) {
-        if (mode == BASE_ROUTE_BALANCED) {
-            e = launch_auction(s, T, E, cfg.eps_start, cfg.eps_end, cfg.eps_factor, cfg.max_bids,
-                               scan, assign, pm, offs, prices, sd, W + L.auction, st);
-        } else if (mode == BASE_ROUTE_GREEDY) {
-            e = launch_stats_reset(sd, st);
-            if (e == hipSuccess) e = launch_greedy(s, T, E, scan, assign, nullptr, st);
-            if (e == hipSuccess)
-                e = launch_perm(assign, T, E, pm, offs, nullptr, 0, nullptr, W + L.permws, st);
-        } else {
-            e = launch_stats_reset(sd, st);
-            if (e == hipSuccess)
-                e = launch_perm(assign, T, E, pm, offs, nullptr, k, &sd->status, W + L.permws, st);
-        }
-    }
-    mark(2, st);
-    if (e == hipSuccess) e = launch_ffn1(h, pm, W1, H, E, k, D, F, dt, act, goff, gblk, T, st);
-    mark(3, st);
-    if (e == hipSuccess) e = launch_ffn2(H, pm, W2, s, h, out, E, k, D, F, dt, goff, gblk, T, st);
-    mark(4, st);
-    mark(5, st);
-    return hip_rc(e);
+int base_layer_forward_ex(const void* h, const void* w, const void* W1, const void* W2,
+                          int64_t T, int64_t E, int64_t D, int64_t F, int dt, int act, int mode,
+                          base_auction_cfg cfg, int32_t* assign, float* scores, int32_t* perm,
+                          void* out, base_auction_stats* stats, const base_layer_opts* opts,
+                          void* ws, size_t ws_bytes, base_stream_t stream) {
+    const base_layer_opts dflt = {BASE_MIX_RESIDUAL, 0, 1e-5, nullptr, nullptr};
+    return layer_forward(h, w, W1, W2, T, E, D, F, dt, act, mode, cfg, assign, scores, perm, out,
+                         stats, opts ? opts : &dflt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -42,6 +42,11 @@ struct GemmParams {
     // [goff[g], goff[g+1]) and the blocks [gblk[g], gblk[g+1]) of the launch
     const int32_t* goff;
     const int32_t* gblk;
+    // FFN2 epilogue of the layer variants (see Ffn2Epi); epi_general == 0 is
+    // eq. 1's y = sigmoid(s) C + h, scattered to out
+    int epi_general, epi_gate, epi_keep, epi_res;
+    const void* xr;
+    void* xo;
 };
 
 // The tile a block computes: group g, tile (tm, tn), and the group's rows
@@ -302,8 +307,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     {
         int64_t m = m0 + lr;
         if (m < tl.rows) {
-            int64_t src = (Kind == KIND_FFN1) ? p.perm[tl.row0 + m]
-                        : (Kind == KIND_FFN2) ? tl.row0 + m : m;
+            int64_t src = (Kind == KIND_FFN1 && p.perm) ? p.perm[tl.row0 + m]
+                        : (Kind == KIND_FFN1 || Kind == KIND_FFN2) ? tl.row0 + m : m;
             arow = A + src * p.K;
         }
     }
@@ -342,8 +347,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         float gate = 0.0f;
         if (Kind == KIND_FFN2) {
             t = p.perm[tl.row0 + m];
-            gate = sigmoid_f32(p.s_in[t * p.E + g]);
+            gate = (p.epi_general && p.epi_gate) ? 1.0f : sigmoid_f32(p.s_in[t * p.E + g]);
         }
+        const float c2 = (!p.epi_general || p.epi_keep == 0) ? 1.0f
+                         : (p.epi_keep == 1 ? 1.0f - gate : 0.0f);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx * 4 + j;
@@ -355,8 +362,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
                 else ++nonfin;
             } else if (Kind == KIND_FFN1) {
                 ((float*)p.H)[(tl.row0 + m) * p.N + n] = apply_act(v, p.act);
-            } else {
+            } else if (!p.epi_general) {
                 ((float*)p.out)[t * p.N + n] = gate * v + ((const float*)p.h)[t * p.N + n];
+            } else {
+                const float ht = (c2 != 0.0f || p.epi_res == 1) ? ((const float*)p.h)[t * p.N + n] : 0.0f;
+                const float r = p.epi_res == 1 ? ht
+                              : (p.epi_res == 2 ? ((const float*)p.xr)[(tl.row0 + m) * p.N + n] : 0.0f);
+                const float y = fmaf(gate, r + v, c2 * ht);
+                if (p.xo) ((float*)p.xo)[(tl.row0 + m) * p.N + n] = y;
+                else ((float*)p.out)[t * p.N + n] = y;
             }
         }
     }
@@ -401,12 +415,12 @@ static int64_t grid_blocks(const GemmParams& p, int32_t* gblk, int64_t rows_tota
     return ((rows_total + BM - 1) / BM + p.groups) * ntn;
 }
 
-template <int Kind, int BN, int WM, int WN>
+template <int Kind, int BN, int WM, int WN, bool GEN = false>
 static hipError_t run_dma64(const GemmParams& p, int32_t* gblk, int64_t rows_total, hipStream_t st) {
     const int64_t tiles = grid_blocks<256, BN>(p, gblk, rows_total, st);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_dma64_kernel<Kind, BN, WM, WN>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_bf16_dma64_kernel<Kind, BN, WM, WN, GEN>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
@@ -451,6 +465,24 @@ hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
     return run_dma64<KIND_FFN2, 256, 4, 2>(p, gblk, rows_total, st);
+}
+
+hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2, const float* s,
+                          const void* h, void* out, int64_t E, int64_t k, int64_t D, int64_t F,
+                          int dt, const int32_t* goff, int32_t* gblk, int64_t rows_total,
+                          const Ffn2Epi& epi, hipStream_t st) {
+    GemmParams p = {};
+    p.A = H; p.B = W2; p.M = k; p.N = D; p.K = F; p.groups = E;
+    p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
+    p.goff = goff; p.gblk = gblk;
+    p.epi_general = 1;
+    p.epi_gate = epi.gate;
+    p.epi_keep = epi.keep;
+    p.epi_res = epi.res;
+    p.xr = epi.xr;
+    p.xo = epi.xo;
+    if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
+    return run_dma64<KIND_FFN2, 256, 4, 2, true>(p, gblk, rows_total, st);
 }
 
 }  // namespace base

@@ -149,6 +149,56 @@ BASE_DEV void dma_epilogue_rows(const GemmParams& p, f32x16_t (&acc)[TM][TN], co
     }
 }
 
+// FFN2 epilogue of the layer variants (same accumulator layout as above):
+// y = g (R + C) + c2 h[t] with the choices of GemmParams' epi_* fields,
+// written to out[t] or to the grouped row xo[row0 + row].
+template <int TM, int TN>
+BASE_DEV void dma_epilogue_general(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                                   int64_t mw, int64_t nw, int lane, const int32_t (&trow)[TM],
+                                   const float (&gate)[TM]) {
+    const bool vec = (p.N & 3) == 0;
+    const int64_t cb = nw + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = mw + i * 32 + (lane & 31);
+        if (m >= tl.rows) continue;
+        const int64_t t = trow[i];
+        const float g = gate[i];
+        const float c2 = p.epi_keep == 0 ? 1.0f : (p.epi_keep == 1 ? 1.0f - g : 0.0f);
+        const bool need_h = c2 != 0.0f || p.epi_res == 1;
+        const uint16_t* hrow = (const uint16_t*)p.h + t * p.N;
+        const uint16_t* rrow = (p.epi_res == 2) ? (const uint16_t*)p.xr + (tl.row0 + m) * p.N : hrow;
+        uint16_t* orow = p.xo ? (uint16_t*)p.xo + (tl.row0 + m) * p.N : (uint16_t*)p.out + t * p.N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = cb + j * 32 + 8 * q;
+                if (vec) {
+                    if (n >= p.N) continue;
+                    f32x4_t hv = {0.0f, 0.0f, 0.0f, 0.0f}, rv = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if (need_h) hv = __builtin_convertvector(*(const bf16x4_t*)(hrow + n), f32x4_t);
+                    if (p.epi_res == 1) rv = hv;
+                    else if (p.epi_res == 2)
+                        rv = __builtin_convertvector(*(const bf16x4_t*)(rrow + n), f32x4_t);
+                    f32x4_t y;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) y[c] = fmaf(g, rv[c] + acc[i][j][4 * q + c], c2 * hv[c]);
+                    *(bf16x4_t*)(orow + n) = __builtin_convertvector(y, bf16x4_t);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (n + c >= p.N) continue;
+                        const float hv = need_h ? bf16_to_f32(hrow[n + c]) : 0.0f;
+                        const float rv = p.epi_res == 1 ? hv
+                                         : (p.epi_res == 2 ? bf16_to_f32(rrow[n + c]) : 0.0f);
+                        orow[n + c] = f32_to_bf16(fmaf(g, rv + acc[i][j][4 * q + c], c2 * hv));
+                    }
+                }
+            }
+    }
+}
+
 template <int Kind, int TM, int TN>
 BASE_DEV void dma_epilogue(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
                            int64_t mw, int64_t nw, int lane, const int32_t (&trow)[TM],
@@ -172,7 +222,8 @@ BASE_DEV char* dma64_stage() {
 // so 16 consecutive rows (one ds_read_b128 pass) hit 16 distinct bank groups.
 BASE_DEV int swz8(int r) { return (r >> 1) & 7; }
 
-template <int Kind, int BN, int WM, int WN>
+// GEN: the FFN2 epilogue of the layer variants instead of eq. 1's
+template <int Kind, int BN, int WM, int WN, bool GEN = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams p) {
     static_assert(Kind == KIND_FFN1 || Kind == KIND_FFN2, "expert products only");
     constexpr int BM = 256, BK = 64, NT = WM * WN * 64;
@@ -204,7 +255,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
         const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
         if (Kind == KIND_FFN2 && m < tl.rows) {
             trow[i] = p.perm[tl.row0 + m];
-            gate[i] = sigmoid_f32(p.s_in[(int64_t)trow[i] * p.E + g]);
+            gate[i] = (GEN && p.epi_gate) ? 1.0f : sigmoid_f32(p.s_in[(int64_t)trow[i] * p.E + g]);
         }
     }
 
@@ -219,7 +270,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
         const int64_t m = m0 + row;
         asrc[j] = nullptr;
         if (m < tl.rows) {
-            const int64_t src = (Kind == KIND_FFN1) ? p.perm[tl.row0 + m] : tl.row0 + m;
+            const int64_t src = (Kind == KIND_FFN1 && p.perm) ? p.perm[tl.row0 + m] : tl.row0 + m;
             asrc[j] = A + src * p.K + c * 8;
         }
     }
@@ -315,5 +366,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
         step(kt + 1, dma64_stage<1>(), dma64_stage<0>());
     }
     wait_vmcnt<0>();
-    dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
+    if (GEN && Kind == KIND_FFN2)
+        dma_epilogue_general<TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
+    else
+        dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
 }

@@ -30,7 +30,8 @@ hipError_t launch_affinity(const void* h, const void* w, float* s, int64_t T,
 // the grouped order) or ragged (group e owns rows goff[e] .. goff[e+1]-1,
 // rows_total = goff[E]; gblk is E+1 ints of scratch for the launch's block
 // map).
-// H[r, :] = act(h[perm[r], :] W1_e^T) for every row r of group e (bf16 or fp32 H)
+// H[r, :] = act(h[perm[r], :] W1_e^T) for every row r of group e (bf16 or fp32 H);
+// with perm == nullptr the rows of h are already grouped: act(h[r, :] W1_e^T)
 hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1,
                        void* H, int64_t E, int64_t k, int64_t D, int64_t F,
                        int dt, int act, const int32_t* goff, int32_t* gblk,
@@ -41,6 +42,34 @@ hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2,
                        int64_t k, int64_t D, int64_t F, int dt,
                        const int32_t* goff, int32_t* gblk, int64_t rows_total,
                        hipStream_t st);
+
+// Generalised second product (layer variants): with C = H W2_e^T and
+// t = perm[r], y = g (R + C) + c2 h[t, :] where
+//   g  = sigmoid(s[t, e]) (gate == 0) or 1 (gate == 1),
+//   c2 = 1 (keep == 0), 1 - g (keep == 1) or 0 (keep == 2),
+//   R  = 0 (res == 0), h[t, :] (res == 1) or xr[r, :] (res == 2, grouped rows);
+// y goes to out[t, :], or to the grouped row xo[r, :] when xo != nullptr.
+// (Eq. 1 is gate 0, keep 0, res 0, scattered.) xr may equal xo.
+struct Ffn2Epi {
+    int gate, keep, res;
+    const void* xr;
+    void* xo;
+};
+hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2,
+                          const float* s, const void* h, void* out, int64_t E,
+                          int64_t k, int64_t D, int64_t F, int dt,
+                          const int32_t* goff, int32_t* gblk, int64_t rows_total,
+                          const Ffn2Epi& epi, hipStream_t st);
+
+// ---- layernorm.hip
+// Y[r, :] = LN(X[r, :]) * gamma[e] + beta[e] over D, e = assign[perm[r]] the
+// row's expert, with X[r, :] = x[perm[r], :] (gather != 0) or x[r, :]
+// (grouped rows). gamma / beta: E x D fp32 or nullptr (ones / zeros). The
+// statistics are fp32; Y has dtype dt.
+hipError_t launch_layernorm(const void* x, int gather, const int32_t* perm,
+                            const int32_t* assign, const float* gamma,
+                            const float* beta, double eps, void* Y, int64_t T,
+                            int64_t E, int64_t D, int dt, hipStream_t st);
 
 // ---- route.hip
 hipError_t launch_scan_init(ScoreScan* scan, hipStream_t st);

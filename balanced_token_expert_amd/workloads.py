@@ -28,6 +28,8 @@ import numpy as np
 # tensor ids inside a workload's seed space
 TID_H, TID_W, TID_W1, TID_W2, TID_AUX = 0, 1, 2, 3, 4
 ROW_CHUNK = 2048  # token rows per generator chunk
+BLOCK_CHUNK = 100000  # chunk offset of an expert's feed-forward block
+LN_CHUNK = 200000     # chunk offset of the layer-norm parameters (TID_AUX)
 
 
 @dataclass(frozen=True)
@@ -143,6 +145,30 @@ def gen_w2(wl: Workload, expert: int, rep: int = 0) -> np.ndarray:
     """Expert ``expert``'s second FFN matrix (D x F, [out, in]), N(0, 1/F)."""
     rng = _rng(wl, rep, TID_W2, expert)
     return _store(_normal(rng, (wl.D, wl.F), 1.0 / np.sqrt(wl.F)), wl.dtype)
+
+
+def gen_block_w1(wl: Workload, block: int, expert: int, rep: int = 0) -> np.ndarray:
+    """First matrix of feed-forward block ``block`` of an expert (F x D);
+    block 0 is ``gen_w1``."""
+    rng = _rng(wl, rep, TID_W1, block * BLOCK_CHUNK + expert)
+    return _store(_normal(rng, (wl.F, wl.D), 1.0 / np.sqrt(wl.D)), wl.dtype)
+
+
+def gen_block_w2(wl: Workload, block: int, expert: int, rep: int = 0) -> np.ndarray:
+    """Second matrix of feed-forward block ``block`` of an expert (D x F);
+    block 0 is ``gen_w2``."""
+    rng = _rng(wl, rep, TID_W2, block * BLOCK_CHUNK + expert)
+    return _store(_normal(rng, (wl.D, wl.F), 1.0 / np.sqrt(wl.F)), wl.dtype)
+
+
+def gen_ln(wl: Workload, block: int, rep: int = 0):
+    """Layer-norm scales and shifts of block ``block`` for every expert (two
+    E x D fp32 arrays): 1 + 0.1 N(0,1) and 0.1 N(0,1), away from the identity
+    initialisation so that both take part."""
+    rng = _rng(wl, rep, TID_AUX, LN_CHUNK + block)
+    g = (1.0 + 0.1 * rng.standard_normal((wl.E, wl.D))).astype(np.float32)
+    b = (0.1 * rng.standard_normal((wl.E, wl.D))).astype(np.float32)
+    return g, b
 
 
 def _skew_rows(wl: Workload, rep: int) -> np.ndarray:

@@ -114,7 +114,8 @@ typedef enum {
     BASE_OP_AFFINITY = 0,
     BASE_OP_AUCTION = 1,
     BASE_OP_GREEDY = 2,
-    BASE_OP_LAYER = 3
+    BASE_OP_LAYER = 3,
+    BASE_OP_LAYER_EX = 4 /* base_layer_forward_ex: LAYER plus two T x D buffers */
 } base_op;
 
 size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F,
@@ -209,12 +210,56 @@ int base_layer_forward(const void *h, const void *w, const void *W1,
                        int32_t *perm, void *out, base_auction_stats *stats,
                        void *ws, size_t ws_bytes, base_stream_t stream);
 
+/* Layer variants (base_layer_forward_ex). The pages note two places where
+ * the released code differs from eq. 1: it mixes with a convex blend,
+ * y = g f(x) + (1 - g) x, g = sigmoid(s[t][a_t]) (page "Paper vs code",
+ * mixing equation), and its experts are residual internally; sec. 4.1 makes
+ * each expert a stack of feed-forward blocks, each with layer norm, a
+ * projection to the hidden width, the activation, a projection back and a
+ * residual connection:  x <- x + W2_n act(W1_n LN_n(x)),  n = 0 .. N-1. */
+typedef enum { BASE_MIX_RESIDUAL = 0, BASE_MIX_CONVEX = 1 } base_mix;
+
+typedef struct {
+    int32_t mix;       /* BASE_MIX_RESIDUAL: y = g f(x) + x (eq. 1);
+                          BASE_MIX_CONVEX: y = g f(x) + (1 - g) x */
+    int32_t sublayers; /* 0: f(x) = W2 act(W1 x) as in base_layer_forward;
+                          N in 1..64: f = N blocks of sec. 4.1 (above) */
+    double ln_eps;     /* layer-norm epsilon (>= 0; N >= 1 only) */
+    const float *ln_gamma; /* DEVICE, N x E x D fp32 layer-norm scales, or
+                              NULL for ones */
+    const float *ln_beta;  /* DEVICE, N x E x D fp32 layer-norm shifts, or
+                              NULL for zeros */
+} base_layer_opts;
+
+/*
+ * base_layer_forward_ex -- base_layer_forward with the layer variants above
+ * (`opts` is a HOST pointer, NULL = residual mix, plain experts).
+ *   With sublayers = N >= 1, W1 is N x E x F x D and W2 is N x E x D x F
+ *   (block-major), and each block's layer norm uses the population variance
+ *   over D, fp32 statistics, fp32 gamma / beta of the token's expert; the
+ *   block input and the normalised rows are stored in dtype dt (bf16: the
+ *   running block output is rounded to bf16 after each block). The gate is
+ *   the fp32 affinity of the chosen expert, as in base_layer_forward.
+ *   Everything else (routing modes, outputs, errors) is as base_layer_forward.
+ *   Extra error: INVALID_ARG for an unknown mix, sublayers outside [0, 64],
+ *   or ln_eps < 0.
+ *   ws: scratch of base_workspace_bytes(BASE_OP_LAYER_EX, T, E, D, F, dt).
+ */
+int base_layer_forward_ex(const void *h, const void *w, const void *W1,
+                          const void *W2, int64_t T, int64_t E, int64_t D,
+                          int64_t F, int dt, int act, int mode,
+                          base_auction_cfg cfg, int32_t *assign, float *scores,
+                          int32_t *perm, void *out, base_auction_stats *stats,
+                          const base_layer_opts *opts, void *ws,
+                          size_t ws_bytes, base_stream_t stream);
+
 /*
  * base_set_phase_events -- optional tracing. When `events` is non-NULL, every
  * later base_layer_forward call on this host thread records n (<= 6) HIP
  * events (hipEvent_t, created by the caller) on its stream: [0] before the
  * affinity product, [1] after it, [2] after routing and grouping, [3] after
- * the first expert product, [4] after the second (the end), [5] = [4]. The
+ * the first expert product (base_layer_forward_ex with blocks: after the
+ * last block's first product), [4] at the end, [5] = [4]. The
  * caller reads durations with hipEventElapsedTime. NULL turns tracing off.
  * Returns BASE_ERR_INVALID_ARG if n is outside [0, 6].
  */

@@ -116,3 +116,23 @@ def test_greedy_and_affinity_host_errors(lib):
     assert lib.base_affinity(FAKE, FAKE, None, 12, 3, 8, 1, None) == api.BASE_ERR_INVALID_ARG
     assert lib.base_affinity(FAKE, FAKE, FAKE, 12, 3, 12, 1, None) == api.BASE_ERR_UNSUPPORTED
     assert lib.base_affinity(FAKE, FAKE, FAKE, 12, 3, 8, 4, None) == api.BASE_ERR_INVALID_ARG
+
+
+def test_layer_ex_host_errors(lib):
+    good = api.cfg(1.0, 1e-4, 10.0, 0)
+    T, E, D, F = 12, 3, 8, 16
+    lay = api.base_workspace_bytes(api.BASE_OP_LAYER, T, E, D, F, api.BASE_BF16)
+    lay_ex = api.base_workspace_bytes(api.BASE_OP_LAYER_EX, T, E, D, F, api.BASE_BF16)
+    assert lay_ex >= lay + 2 * T * D * 2
+
+    def call(mix=0, sub=1, eps=1e-5, ws=1 << 30, T=T):
+        o = api.LayerOpts(mix, sub, eps, None, None)
+        return lib.base_layer_forward_ex(FAKE, FAKE, FAKE, FAKE, T, E, D, F, 1, 1, 0, good, FAKE,
+                                         None, None, FAKE, None, ctypes.byref(o), FAKE, ws, None)
+
+    assert call(mix=2) == api.BASE_ERR_INVALID_ARG
+    assert call(sub=-1) == api.BASE_ERR_INVALID_ARG
+    assert call(sub=65) == api.BASE_ERR_INVALID_ARG
+    assert call(eps=-1.0) == api.BASE_ERR_INVALID_ARG
+    assert call(ws=lay) == api.BASE_ERR_INVALID_ARG        # needs the LAYER_EX workspace
+    assert call(T=10) == api.BASE_ERR_INDIVISIBLE
