@@ -199,6 +199,61 @@ def greedy_layer(hd, wd, W1d, W2d, act, T, E, reps=5):
             "largest_group": int(counts.max()), "empty_experts": int((counts == 0).sum())}
 
 
+def layer_variants(wl, hd, wd, W1d, W2d, act, c, reps=5):
+    """base_layer_forward_ex on the same inputs and balanced routing: the
+    released code's convex mix with plain experts, and experts of one and two
+    sec. 4.1 blocks (layer norm, up, activation, down, residual). Block 0
+    uses the layer's expert matrices; the second block reuses them (the
+    values do not change the work). Median ms of the whole call and of the
+    expert part (grouping done -> output written, library phase events)."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    dt = api.BASE_BF16 if wl.dtype == "bf16" else api.BASE_F32
+    bufs = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+                scores=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+                out=torch.empty_like(hd), stats=api.new_stats(),
+                ws=api.workspace(api.BASE_OP_LAYER_EX, T, E, D, F, dt))
+    lnp = [W.gen_ln(wl, b) for b in range(2)]
+    gam = torch.from_numpy(np.stack([g for g, _ in lnp])).cuda()
+    bet = torch.from_numpy(np.stack([b for _, b in lnp])).cuda()
+    W1x2, W2x2 = torch.stack([W1d, W1d]), torch.stack([W2d, W2d])
+    cases = {"convex_plain": dict(mix=api.BASE_MIX_CONVEX, sublayers=0, W1=W1d, W2=W2d),
+             "convex_blocks1_ln": dict(mix=api.BASE_MIX_CONVEX, sublayers=1, W1=W1d[None],
+                                       W2=W2d[None], ln_gamma=gam[:1], ln_beta=bet[:1]),
+             "convex_blocks2_ln": dict(mix=api.BASE_MIX_CONVEX, sublayers=2, W1=W1x2, W2=W2x2,
+                                       ln_gamma=gam, ln_beta=bet)}
+    ev = HipEvents(6 * reps)
+    res = {}
+    for name, kw in cases.items():
+        kw = dict(kw)
+        W1v, W2v = kw.pop("W1"), kw.pop("W2")
+
+        def call():
+            api.base_layer_forward_ex(hd, wd, W1v, W2v, act, api.BASE_ROUTE_BALANCED, c, **kw,
+                                      **bufs)
+        call()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            api.base_set_phase_events(ev.block(6 * i), 6)
+            call()
+        torch.cuda.synchronize()
+        api.base_set_phase_events(None, 0)
+        tot = [ev.ms(6 * i, 6 * i + 4) for i in range(reps)]
+        exp = [ev.ms(6 * i + 2, 6 * i + 4) for i in range(reps)]
+        st = api.read_stats(bufs["stats"])
+        res[name] = {"ms": round(float(np.median(tot)), 4),
+                     "tokens_per_s": round(T / (np.median(tot) * 1e-3), 1),
+                     "expert_ms": round(float(np.median(exp)), 4),
+                     "expert_tflops": round(2.0 * 2 * T * D * F * max(kw["sublayers"], 1)
+                                            / (np.median(exp) * 1e-3) / 1e12, 1),
+                     "status": st.status}
+    del W1x2, W2x2
+    return res
+
+
 def auction_solve(reps=10):
     """Auction solve ms on the mixture workload (device-resident fp32 scores)."""
     import torch
@@ -272,6 +327,7 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-auction", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -384,6 +440,8 @@ def main():
                            "uniform_share": round(1.0 / E, 5)},
            "roofline": roof, "wall_s_timed": round(wall, 3)}
     res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
+    if not args.no_variants:
+        res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c)
     if not args.no_auction:
         res["auction_solve_ms"] = auction_solve()
     if not args.no_cpu_baseline:

@@ -25,6 +25,13 @@ CASES = [
     dict(T=1536, E=4, D=320, F=520, dtype="bf16", act="gelu", kind="iid", mix=1, sub=2, ln=True),
     dict(T=1536, E=4, D=320, F=520, dtype="bf16", act="relu", kind="skew", mix=0, sub=2, ln=False),
     dict(T=2048, E=8, D=256, F=512, dtype="bf16", act="gelu", kind="mixture", mix=1, sub=3, ln=True),
+    # layer-norm row widths: 2, 4, 8 and 16 register chunks of 8 per lane
+    # with ragged chunk tails, and a row too long to keep in registers
+    dict(T=512, E=4, D=776, F=64, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=True),
+    dict(T=512, E=4, D=1032, F=64, dtype="bf16", act="gelu", kind="iid", mix=0, sub=2, ln=True),
+    dict(T=512, E=4, D=2056, F=64, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=False),
+    dict(T=256, E=2, D=4104, F=32, dtype="bf16", act="gelu", kind="iid", mix=0, sub=2, ln=True),
+    dict(T=256, E=2, D=8200, F=32, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=True),
 ]
 MODES = [api.BASE_ROUTE_BALANCED, api.BASE_ROUTE_GIVEN, api.BASE_ROUTE_GREEDY]
 
