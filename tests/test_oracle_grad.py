@@ -1,0 +1,118 @@
+"""Pins of the oracle's layer gradients (oracle/grad.py) against things other
+than themselves: central finite differences of the pinned forward
+(layer_forward_ex), torch.autograd over torch.nn modules in fp64 (an
+independent differentiation), and structural cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.grad import act_grad, layer_backward
+
+RNG = np.random.default_rng(11)
+
+
+def _inputs(T=12, E=3, D=5, F=7, ragged=False):
+    h = RNG.standard_normal((T, D))
+    w = RNG.standard_normal((E, D)) * 0.7
+    W1 = RNG.standard_normal((E, F, D)) * D ** -0.5
+    W2 = RNG.standard_normal((E, D, F)) * F ** -0.5
+    if ragged:
+        a = RNG.integers(0, E, T)
+        a[:E] = np.arange(E)
+        a[0] = 0  # keep expert E-1 reachable but the groups uneven
+    else:
+        a = RNG.permutation(np.repeat(np.arange(E), T // E))
+    dy = RNG.standard_normal((T, D))
+    return h, w, W1, W2, a, dy
+
+
+def _loss(h, w, W1, W2, a, act, dy, mix):
+    y = oracle.layer_forward_ex(h, w, W1, W2, a, act, mix=mix)
+    return float((dy * y).sum())
+
+
+@pytest.mark.parametrize("mix", ["residual", "convex"])
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_gradients_match_finite_differences(mix, act, ragged):
+    h, w, W1, W2, a, dy = _inputs(ragged=ragged)
+    dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, act, dy, mix=mix)
+    E = w.shape[0]
+    num = {"h": np.zeros_like(h), "w": np.zeros_like(w), "W1": np.zeros_like(W1),
+           "W2": np.zeros_like(W2)}
+    step = 1e-6
+    params = {"h": h, "w": w, "W1": W1, "W2": W2}
+    for name, arr in params.items():
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + step
+            lp = _loss(h, w, W1, W2, a, act, dy, mix)
+            arr[idx] = keep - step
+            lm = _loss(h, w, W1, W2, a, act, dy, mix)
+            arr[idx] = keep
+            num[name][idx] = (lp - lm) / (2 * step)
+    got = {"h": dh, "w": dw, "W1": np.stack([dW1[e] for e in range(E)]),
+           "W2": np.stack([dW2[e] for e in range(E)])}
+    for name in params:
+        err = np.abs(got[name] - num[name]).max()
+        assert err < 1e-7 * max(1.0, np.abs(num[name]).max()), (name, err)
+
+
+@pytest.mark.parametrize("mix", ["residual", "convex"])
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_gradients_match_torch_autograd(mix, act):
+    """The layer rebuilt from torch.nn.functional pieces in fp64; torch's
+    autograd differentiates it independently of the hand-written chain rule."""
+    T, E, D, F = 64, 4, 16, 40
+    h, w, W1, W2, a, dy = _inputs(T, E, D, F)
+    th, tw, tW1, tW2 = (torch.tensor(x, requires_grad=True) for x in (h, w, W1, W2))
+    y = torch.zeros(T, D, dtype=torch.float64)
+    tact = torch.relu if act == "relu" else torch.nn.functional.gelu
+    for e in range(E):
+        rows = torch.from_numpy(np.nonzero(a == e)[0])
+        x = th[rows]
+        g = torch.sigmoid(x @ tw[e])[:, None]
+        f = torch.nn.functional.linear(tact(torch.nn.functional.linear(x, tW1[e])), tW2[e])
+        y = y.index_put((rows,), g * f + (x if mix == "residual" else (1 - g) * x))
+    (y * torch.from_numpy(dy)).sum().backward()
+    dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, act, dy, mix=mix)
+    assert np.allclose(dh, th.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dw, tw.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(np.stack([dW1[e] for e in range(E)]), tW1.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(np.stack([dW2[e] for e in range(E)]), tW2.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_act_grad_special_values():
+    z = np.array([-3.0, -1e-300, 0.0, 1e-300, 2.0])
+    assert np.array_equal(act_grad(z, "relu"), [0.0, 0.0, 0.0, 1.0, 1.0])
+    # GELU'(0) = Phi(0) = 1/2; GELU' -> 1 far right, -> 0 far left
+    g = act_grad(np.array([0.0, 40.0, -40.0]), "gelu")
+    assert g[0] == 0.5 and abs(g[1] - 1.0) < 1e-15 and abs(g[2]) < 1e-15
+
+
+def test_zero_second_projection():
+    """W2 = 0: the expert output and the first matrix's gradient vanish; with
+    the residual mix dh = dy exactly and the gate gets nothing; with the
+    convex mix the gate still learns from -dy . x."""
+    h, w, W1, W2, a, dy = _inputs()
+    W2 = np.zeros_like(W2)
+    dh, dw, dW1, dW2g = layer_backward(h, w, W1, W2, a, "gelu", dy, mix="residual")
+    assert np.array_equal(dh, dy)
+    assert not np.any(dw)
+    assert all(not np.any(dW1[e]) for e in dW1)
+    assert any(np.any(dW2g[e]) for e in dW2g)
+    dh, dw, _, _ = layer_backward(h, w, W1, W2, a, "gelu", dy, mix="convex")
+    g = oracle.sigmoid((h * w[a]).sum(axis=1))[:, None]
+    dl = g[:, 0] * (1 - g[:, 0]) * -(dy * h).sum(axis=1)
+    assert np.allclose(dh, (1 - g) * dy + dl[:, None] * w[a], rtol=0, atol=1e-14)
+
+
+def test_zero_upstream_gradient_and_empty_expert():
+    h, w, W1, W2, a, dy = _inputs(T=12, E=4)
+    a = np.where(a == 3, 0, a)  # expert 3 gets no token
+    dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, "relu", np.zeros_like(dy))
+    assert not np.any(dh) and not np.any(dw)
+    assert all(not np.any(dW1[e]) and not np.any(dW2[e]) for e in range(4))
+    dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, "relu", dy)
+    assert not np.any(dw[3]) and not np.any(dW1[3]) and not np.any(dW2[3])
