@@ -24,10 +24,11 @@ BASE_ACT_RELU, BASE_ACT_GELU = 0, 1
 BASE_ROUTE_BALANCED, BASE_ROUTE_GREEDY, BASE_ROUTE_GIVEN = 0, 1, 2
 BASE_OP_AFFINITY, BASE_OP_AUCTION, BASE_OP_GREEDY, BASE_OP_LAYER = 0, 1, 2, 3
 BASE_OP_LAYER_EX = 4
+BASE_OP_LAYER_BWD = 5
 BASE_MIX_RESIDUAL, BASE_MIX_CONVEX = 0, 1
 EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
             "base_assign_auction", "base_route_greedy", "base_layer_forward",
-            "base_layer_forward_ex", "base_set_phase_events")
+            "base_layer_forward_ex", "base_layer_backward", "base_set_phase_events")
 STATS_BYTES = 8 + 16 * 8 * 2
 
 
@@ -74,9 +75,11 @@ def load(path: str = LIB_PATH):
     lib.base_layer_forward_ex.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, i32,
                                           AuctionCfg, P, P, P, P, P, ctypes.POINTER(LayerOpts),
                                           P, ctypes.c_size_t, P]
+    lib.base_layer_backward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, P, P, P, P, P,
+                                        P, P, P, ctypes.POINTER(LayerOpts), P, ctypes.c_size_t, P]
     lib.base_set_phase_events.argtypes = [P, i32]
     for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
-              "base_layer_forward_ex", "base_set_phase_events"):
+              "base_layer_forward_ex", "base_layer_backward", "base_set_phase_events"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -259,6 +262,32 @@ def base_layer_forward_ex(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = Non
                                       _stream(stream))
     _check(rc, "base_layer_forward_ex")
     return {"out": out, "assign": assign, "scores": scores, "perm": perm, "stats": stats}
+
+
+def base_layer_backward(h, w, W1, W2, act: int, assign, scores, dy, mix: int = 0, dh=None,
+                        dw=None, dW1=None, dW2=None, stats=None, ws=None, stream=None):
+    """Gradients of the plain-expert layer for the upstream gradient dy, the
+    assignment fixed; returns dict(dh, dw, dW1, dW2, stats), each gradient
+    in the dtype of h."""
+    _dev(h, w, W1, W2, assign, scores, dy, dh, dw, dW1, dW2)
+    T, D = h.shape
+    E = w.shape[0]
+    F = W1.shape[1]
+    dev = h.device
+    dt = _dt(h)
+    dh = torch.empty_like(h) if dh is None else dh
+    dw = torch.empty_like(w) if dw is None else dw
+    dW1 = torch.empty_like(W1) if dW1 is None else dW1
+    dW2 = torch.empty_like(W2) if dW2 is None else dW2
+    stats = new_stats(dev) if stats is None else stats
+    ws = workspace(BASE_OP_LAYER_BWD, T, E, D, F, dt, device=dev) if ws is None else ws
+    opts = LayerOpts(int(mix), 0, 1e-5, None, None)
+    rc = load().base_layer_backward(_ptr(h), _ptr(w), _ptr(W1), _ptr(W2), T, E, D, F, dt, act,
+                                    _ptr(assign), _ptr(scores), _ptr(dy), _ptr(dh), _ptr(dw),
+                                    _ptr(dW1), _ptr(dW2), _ptr(stats), ctypes.byref(opts),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "base_layer_backward")
+    return {"dh": dh, "dw": dw, "dW1": dW1, "dW2": dW2, "stats": stats}
 
 
 def base_set_phase_events(events, n: int):

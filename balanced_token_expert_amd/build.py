@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbase_layer.so")
-SOURCES = ["gemm.hip", "route.hip", "auction.hip", "layernorm.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "route.hip", "auction.hip", "layernorm.hip", "grad.hip", "api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # keep the compiler from forming packed fp32 math (v_pk_*_f32)

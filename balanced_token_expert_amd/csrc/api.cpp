@@ -15,13 +15,15 @@ constexpr int64_t kMaxT = int64_t(1) << 24;  // int32 token ids and offsets
 constexpr int64_t kMaxE = 1024;              // auction keeps E prices per lane group
 constexpr int kMaxPhases = 64;
 constexpr int kMaxSublayers = 64;
+constexpr int64_t kMaxBwdWidth = int64_t(1) << 20;  // D, F of base_layer_backward
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout shared by base_workspace_bytes and the entry points.
 struct Layout {
     size_t scan = 0, stats = 0, prices = 0, scores = 0, perm = 0, offsets = 0, hidden = 0,
-           auction = 0, permws = 0, assign = 0, gblk = 0, xbuf = 0, ybuf = 0, total = 0;
+           auction = 0, permws = 0, assign = 0, gblk = 0, xbuf = 0, ybuf = 0, xg = 0, dyg = 0,
+           zbuf = 0, gubuf = 0, dzbuf = 0, part = 0, dl = 0, total = 0;
 };
 
 Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
@@ -37,6 +39,22 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
     }
     take(L.scan, sizeof(ScoreScan));
     take(L.stats, sizeof(AucStatsDev));
+    if (op == BASE_OP_LAYER_BWD) {
+        const size_t b = dt == BASE_BF16 ? 2 : 4;
+        take(L.perm, (size_t)T * 4);
+        take(L.offsets, (size_t)(E + 1) * 4);
+        take(L.gblk, (size_t)(E + 1) * 4);
+        take(L.permws, perm_ws_bytes(T, E));
+        take(L.xg, (size_t)T * D * b);    // token rows, grouped
+        take(L.dyg, (size_t)T * D * b);   // upstream gradient rows, grouped
+        take(L.zbuf, (size_t)T * F * b);  // pre-activations Z
+        take(L.gubuf, (size_t)T * F * b); // gate * act(Z)
+        take(L.dzbuf, (size_t)T * F * b); // dZ
+        take(L.part, (size_t)T * bwd_nparts(F, dt == BASE_BF16) * 4);
+        take(L.dl, (size_t)T * 4);        // gate-logit gradients
+        L.total = off;
+        return L;
+    }
     if (op == BASE_OP_GREEDY) {
         take(L.perm, (size_t)T * 4);
         take(L.offsets, (size_t)(E + 1) * 4);
@@ -222,8 +240,10 @@ int base_set_phase_events(void** events, int n) {
 }
 
 size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dtype) {
-    if (T <= 0 || E <= 0 || op < 0 || op > BASE_OP_LAYER_EX) return 0;
-    if ((op == BASE_OP_LAYER || op == BASE_OP_LAYER_EX) && (F <= 0 || D <= 0)) return 0;
+    if (T <= 0 || E <= 0 || op < 0 || op > BASE_OP_LAYER_BWD) return 0;
+    if ((op == BASE_OP_LAYER || op == BASE_OP_LAYER_EX || op == BASE_OP_LAYER_BWD) &&
+        (F <= 0 || D <= 0))
+        return 0;
     return layout(op, T, E, D, F, dtype).total;
 }
 
@@ -299,6 +319,69 @@ int base_layer_forward_ex(const void* h, const void* w, const void* W1, const vo
     const base_layer_opts dflt = {BASE_MIX_RESIDUAL, 0, 1e-5, nullptr, nullptr};
     return layer_forward(h, w, W1, W2, T, E, D, F, dt, act, mode, cfg, assign, scores, perm, out,
                          stats, opts ? opts : &dflt, ws, ws_bytes, stream);
+}
+
+int base_layer_backward(const void* h, const void* w, const void* W1, const void* W2, int64_t T,
+                        int64_t E, int64_t D, int64_t F, int dt, int act, const int32_t* assign,
+                        const float* scores, const void* dy, void* dh, void* dw, void* dW1,
+                        void* dW2, base_auction_stats* stats, const base_layer_opts* opts,
+                        void* ws, size_t ws_bytes, base_stream_t stream) {
+    if (!h || !w || !W1 || !W2 || !assign || !scores || !dy || !dh || !dw || !dW1 || !dW2)
+        return BASE_ERR_INVALID_ARG;
+    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
+    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
+    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
+    const int mix = opts ? opts->mix : BASE_MIX_RESIDUAL;
+    if (mix != BASE_MIX_RESIDUAL && mix != BASE_MIX_CONVEX) return BASE_ERR_INVALID_ARG;
+    if (opts && opts->sublayers != 0) return BASE_ERR_UNSUPPORTED;
+    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
+    // the backward products address a tile's operands with 32-bit offsets
+    if (D > kMaxBwdWidth || F > kMaxBwdWidth) return BASE_ERR_UNSUPPORTED;
+    if (dt == BASE_BF16 &&
+        (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) || misaligned(W1) ||
+         misaligned(W2) || misaligned(dy) || misaligned(dh) || misaligned(dW1) || misaligned(dW2)))
+        return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(BASE_OP_LAYER_BWD, T, E, D, F, dt);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
+    int32_t* pm = (int32_t*)(W + L.perm);
+    int32_t* offs = (int32_t*)(W + L.offsets);
+    int32_t* gblk = (int32_t*)(W + L.gblk);
+    void* Xg = W + L.xg;
+    void* dYg = W + L.dyg;
+    void* Z = W + L.zbuf;
+    void* gU = W + L.gubuf;
+    void* dZ = W + L.dzbuf;
+    float* part = (float*)(W + L.part);
+    float* dl = (float*)(W + L.dl);
+    const int64_t np = bwd_nparts(F, dt == BASE_BF16);
+
+    mark(0, st);
+    // expert groups of the given assignment (any sizes; ids outside [0, E)
+    // are reported through stats->status)
+    hipError_t e = launch_stats_reset(sd, st);
+    if (e == hipSuccess)
+        e = launch_perm(assign, T, E, pm, offs, nullptr, 0, &sd->status, W + L.permws, st);
+    if (e == hipSuccess) e = launch_gather2(h, dy, pm, Xg, dYg, T, D, dt, st);
+    if (e == hipSuccess)
+        e = launch_bwd_z(Xg, W1, pm, scores, Z, gU, T, E, D, F, dt, act, offs, gblk, st);
+    mark(1, st);
+    if (e == hipSuccess)
+        e = launch_bwd_v(dYg, W2, pm, scores, Z, dZ, part, T, E, D, F, dt, act, offs, gblk, st);
+    if (e == hipSuccess)
+        e = launch_gate_grad(part, np, Xg, dYg, pm, offs, scores, mix, dl, T, E, D, dt, st);
+    mark(2, st);
+    if (e == hipSuccess) e = launch_bwd_w(dYg, gU, D, F, E, offs, dW2, dt, st);
+    mark(3, st);
+    if (e == hipSuccess) e = launch_bwd_w(dZ, Xg, F, D, E, offs, dW1, dt, st);
+    mark(4, st);
+    if (e == hipSuccess)
+        e = launch_bwd_x(dZ, W1, pm, scores, dYg, w, dl, mix, dh, T, E, D, F, dt, offs, gblk, st);
+    if (e == hipSuccess) e = launch_centroid_grad(dl, Xg, offs, dw, E, D, dt, st);
+    mark(5, st);
+    return hip_rc(e);
 }
 
 }  // extern "C"

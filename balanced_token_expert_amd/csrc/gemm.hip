@@ -21,7 +21,14 @@
 
 namespace base {
 
-enum { KIND_AFF = 0, KIND_FFN1 = 1, KIND_FFN2 = 2 };
+enum { KIND_AFF = 0, KIND_FFN1 = 1, KIND_FFN2 = 2,
+       // backward products of the layer, per expert group (grouped rows):
+       KIND_BZ = 3,  // Z = X W1^T; stores Z and gate * act(Z)
+       KIND_BV = 4,  // V = dY W2 (W2 read k-major); stores dZ = gate V act'(Z)
+                     // and per-row partial sums of V act(Z)
+       KIND_BX = 5,  // dX = dZ W1 (W1 read k-major); dh[t] = dX + c dY + dl w_e
+       KIND_BW = 6   // dW_g = P_g^T Q_g over the group's rows (both k-major)
+};
 
 struct GemmParams {
     const void* A;          // bf16 bits or fp32, rows of length K
@@ -47,6 +54,18 @@ struct GemmParams {
     int epi_general, epi_gate, epi_keep, epi_res;
     const void* xr;
     void* xo;
+    // backward products. An operand "read k-major" is stored as rows of k
+    // with M (or N) contiguous: element (m, k) at A[k * lda + m] (B: ldb).
+    int64_t lda, ldb;
+    const int32_t* kgoff;   // BW: group g sums rows [kgoff[g], kgoff[g+1]) (null: K each)
+    const void* zin;        // BV: saved pre-activations Z, grouped rows of length N
+    void* gu;               // BZ: gate * act(Z), grouped rows
+    const void* dyg;        // BX: grouped upstream gradient rows (length N)
+    const void* wc;         // BX: centroids, E x N
+    const float* dl;        // BX: gate-logit gradient of each grouped row
+    float* part;            // BV: partial sums of V . act(Z), nparts per grouped row
+    int64_t nparts;
+    int mix;                // BX: 0 residual (c = 1), 1 convex (c = 1 - gate)
 };
 
 // The tile a block computes: group g, tile (tm, tn), and the group's rows
@@ -390,6 +409,112 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
+// fp32 backward products: 64 x 64 tiles, exact fp32 FMAs, the epilogues of
+// the bf16 path with fp32 storage. Operands read k-major are staged with M
+// (N) contiguous, so both layouts load coalesced.
+template <int Kind>
+__global__ __launch_bounds__(256) void gemm_f32_bwd_kernel(GemmParams p) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    constexpr bool AT = Kind == KIND_BW;
+    constexpr bool BT = Kind == KIND_BV || Kind == KIND_BX || Kind == KIND_BW;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[BK][BN + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    Tile tl;
+    if (!locate_tile<BM, BN>(p, blockIdx.x, tl)) return;
+    const int64_t g = tl.g;
+    const int64_t m0 = tl.tm * BM, n0 = tl.tn * BN;
+    const float* A = (const float*)p.A;
+    const float* B = (const float*)p.B + g * p.b_gstride;
+    int64_t kbeg = 0, Kc = p.K;
+    if (Kind == KIND_BW) {
+        kbeg = p.kgoff ? p.kgoff[g] : g * p.K;
+        Kc = p.kgoff ? p.kgoff[g + 1] - kbeg : p.K;
+    }
+    // k-major staging: thread -> (k = tid / 16, 4 consecutive m / n);
+    // m/n-major staging: thread -> (row = tid / 4, 4 consecutive k)
+    const int lr = tid >> 2, lk = (tid & 3) * 4;
+    const int tk = tid >> 4, tc = (tid & 15) * 4;
+    float acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < Kc; k0 += BK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (AT) {
+                const int64_t k = k0 + tk, m = m0 + tc + q;
+                As[tk][tc + q] = (k < Kc && m < tl.rows) ? A[(kbeg + k) * p.lda + m] : 0.0f;
+            } else {
+                const int64_t k = k0 + lk + q, m = m0 + lr;
+                As[lk + q][lr] = (k < Kc && m < tl.rows) ? A[(tl.row0 + m) * p.K + k] : 0.0f;
+            }
+            if (BT) {
+                const int64_t k = k0 + tk, n = n0 + tc + q;
+                Bs[tk][tc + q] = (k < Kc && n < p.N) ? B[(kbeg + k) * p.ldb + n] : 0.0f;
+            } else {
+                const int64_t k = k0 + lk + q, n = n0 + lr;
+                Bs[lk + q][lr] = (k < Kc && n < p.N) ? B[n * p.K + k] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty * 4 + i;
+        const bool rowok = m < tl.rows;
+        const int64_t row = tl.row0 + m;
+        int64_t t = 0;
+        float gate = 0.0f;
+        if (Kind != KIND_BW && rowok) {
+            t = p.perm[row];
+            gate = sigmoid_f32(p.s_in[t * p.E + g]);
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx * 4 + j;
+            if (!rowok || n >= p.N) continue;
+            const float v = acc[i][j];
+            if (Kind == KIND_BZ) {
+                ((float*)p.H)[row * p.N + n] = v;
+                ((float*)p.gu)[row * p.N + n] = gate * apply_act(v, p.act);
+            } else if (Kind == KIND_BV) {
+                const float z = ((const float*)p.zin)[row * p.N + n];
+                const float u = apply_act(z, p.act);
+                const float du = p.act ? 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+                                             z * expf(-0.5f * z * z) * 0.39894228040143268f
+                                       : (z > 0.0f ? 1.0f : 0.0f);
+                psum = fmaf(v, u, psum);
+                ((float*)p.H)[row * p.N + n] = gate * v * du;
+            } else if (Kind == KIND_BX) {
+                const float cx = p.mix ? 1.0f - gate : 1.0f;
+                ((float*)p.out)[t * p.N + n] =
+                    fmaf(p.dl[row], ((const float*)p.wc)[g * p.N + n],
+                         fmaf(cx, ((const float*)p.dyg)[row * p.N + n], v));
+            } else {
+                ((float*)p.H)[row * p.N + n] = v;
+            }
+        }
+        if (Kind == KIND_BV) {
+            // the 16 threads of a row are 16 consecutive lanes
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 64);
+            if (tx == 0 && rowok) p.part[row * p.nparts + tl.tn] = psum;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int Kind, int BM, int BN, int WM, int WN>
@@ -422,6 +547,16 @@ static hipError_t run_dma64(const GemmParams& p, int32_t* gblk, int64_t rows_tot
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_dma64_kernel<Kind, BN, WM, WN, GEN>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int Kind>
+static hipError_t run_f32_bwd(const GemmParams& p, int32_t* gblk, int64_t rows_total,
+                              hipStream_t st) {
+    const int64_t tiles = grid_blocks<64, 64>(p, gblk, rows_total, st);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_f32_bwd_kernel<Kind>, dim3((unsigned)tiles), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -483,6 +618,57 @@ hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2, co
     p.xo = epi.xo;
     if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
     return run_dma64<KIND_FFN2, 256, 4, 2, true>(p, gblk, rows_total, st);
+}
+
+// ---- backward products (ragged groups: group e owns rows goff[e] ..
+// goff[e+1]-1 of the grouped order; T = goff[E])
+
+int64_t bwd_nparts(int64_t F, int dt) { return dt == 0 ? (F + 63) / 64 : (F + 255) / 256 * 2; }
+
+hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, const float* s,
+                        void* Z, void* gU, int64_t T, int64_t E, int64_t D, int64_t F, int dt,
+                        int act, const int32_t* goff, int32_t* gblk, hipStream_t st) {
+    GemmParams p = {};
+    p.A = Xg; p.B = W1; p.M = T / E; p.N = F; p.K = D; p.groups = E;
+    p.perm = perm; p.b_gstride = F * D; p.s_in = s; p.E = E; p.H = Z; p.gu = gU; p.act = act;
+    p.goff = goff; p.gblk = gblk;
+    if (dt == 0) return run_f32_bwd<KIND_BZ>(p, gblk, T, st);
+    return run_dma64<KIND_BZ, 256, 4, 2>(p, gblk, T, st);
+}
+
+hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, const float* s,
+                        const void* Z, void* dZ, float* part, int64_t T, int64_t E, int64_t D,
+                        int64_t F, int dt, int act, const int32_t* goff, int32_t* gblk,
+                        hipStream_t st) {
+    GemmParams p = {};
+    p.A = dYg; p.B = W2; p.M = T / E; p.N = F; p.K = D; p.groups = E;
+    p.perm = perm; p.b_gstride = D * F; p.ldb = F; p.s_in = s; p.E = E; p.zin = Z; p.H = dZ;
+    p.part = part; p.nparts = bwd_nparts(F, dt); p.act = act;
+    p.goff = goff; p.gblk = gblk;
+    if (dt == 0) return run_f32_bwd<KIND_BV>(p, gblk, T, st);
+    return run_dma64<KIND_BV, 256, 4, 2>(p, gblk, T, st);
+}
+
+hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, const float* s,
+                        const void* dYg, const void* w, const float* dl, int mix, void* dh,
+                        int64_t T, int64_t E, int64_t D, int64_t F, int dt, const int32_t* goff,
+                        int32_t* gblk, hipStream_t st) {
+    GemmParams p = {};
+    p.A = dZ; p.B = W1; p.M = T / E; p.N = D; p.K = F; p.groups = E;
+    p.perm = perm; p.b_gstride = F * D; p.ldb = D; p.s_in = s; p.E = E; p.dyg = dYg; p.wc = w;
+    p.dl = dl; p.mix = mix; p.out = dh;
+    p.goff = goff; p.gblk = gblk;
+    if (dt == 0) return run_f32_bwd<KIND_BX>(p, gblk, T, st);
+    return run_dma64<KIND_BX, 256, 4, 2>(p, gblk, T, st);
+}
+
+hipError_t launch_bwd_w(const void* P, const void* Q, int64_t M, int64_t N, int64_t E,
+                        const int32_t* goff, void* dW, int dt, hipStream_t st) {
+    GemmParams p = {};
+    p.A = P; p.B = Q; p.M = M; p.N = N; p.K = 0; p.groups = E;
+    p.lda = M; p.ldb = N; p.kgoff = goff; p.H = dW;
+    if (dt == 0) return run_f32_bwd<KIND_BW>(p, nullptr, 0, st);
+    return run_dma64<KIND_BW, 256, 4, 2>(p, nullptr, 0, st);
 }
 
 }  // namespace base

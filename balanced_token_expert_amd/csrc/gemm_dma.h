@@ -15,6 +15,16 @@
 // chunk per half wave) free of LDS bank conflicts. Lanes whose row or K range
 // lies outside the operand load a 16-byte block of zeros.
 //
+// Operands of the backward products may be stored "k-major" instead (rows of
+// k with M or N contiguous, e.g. W2 read as W2^T, or token rows summed over
+// in a weight gradient). Such a stage holds 64 k-rows of 256 values (512
+// bytes, 32 chunks; chunk c of row r at c ^ swz_t(r)), filled by the same
+// 16-byte DMA, and its fragments come from two ds_read_b64_tr_b16 per
+// 32 x 16 fragment: within each 16-lane group, the lane that supplies row
+// r0 + j, columns 4a .. 4a+3 hands element b of them to lane 4a + b, so lane
+// l ends up with 4 consecutive k of column l % 32 (rows 8 (l / 32) .. + 3 and
+// + 4 .. + 7 over the two reads), the layout the MFMA takes.
+//
 // The MFMAs take the weight fragment as their first operand, so each
 // accumulator holds C transposed: a lane owns one output row and runs of 4
 // consecutive columns. The epilogue then writes 8-byte pieces of rows and
@@ -26,6 +36,25 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 BASE_DEV void dma16(const void* src, char* dst) {
     __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// The same 16-byte DMA through a raw buffer descriptor: a byte offset at or
+// past the descriptor's size (kOob included) loads zeros.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+// The arguments are uniform; readfirstlane tells the compiler so, which keeps
+// the descriptor in scalar registers (else each load gets a waterfall loop).
+BASE_DEV buf_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void* b = (void*)(((uint64_t)hi << 32) | lo);
+    // 0x00020000: the descriptor word 3 of raw dword buffers on gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(b, 0, (int)n, 0x00020000);
+}
+BASE_DEV void dma16_buf(buf_rsrc_t r, uint32_t voff, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, (int)voff, 0, 0, 0);
 }
 
 // s_waitcnt through the builtin rather than inline asm, so that the
@@ -222,10 +251,135 @@ BASE_DEV char* dma64_stage() {
 // so 16 consecutive rows (one ds_read_b128 pass) hit 16 distinct bank groups.
 BASE_DEV int swz8(int r) { return (r >> 1) & 7; }
 
+// k-major stages (32 chunks per row): the rows one transpose read touches,
+// r0 + 0..3 (first half wave) and r0 + 8..11 (second half), land in distinct
+// 64-byte bank groups.
+BASE_DEV int swz_t(int r) { return ((r & 3) << 2) | ((r & 8) << 1); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 32 x 16 fragment of a k-major stage: rows k .. k+3 and k+4 .. k+7 from the
+// lane's address (the second read 4 rows = 2048 bytes further)
+BASE_DEV bf16x8_t tr_frag(const char* a) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 4 * 512));
+    const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// GELU (the A&S 7.1.26 form above) and its derivative Phi(x) + x phi(x),
+// sharing the exp: e^(-z^2) with z = |x| / sqrt 2 is e^(-x^2 / 2).
+BASE_DEV void gelu_grad_as7126(float x, float& u, float& du) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float q = fmaf(t, 1.061405429f, -1.453152027f);
+    q = fmaf(t, q, 1.421413741f);
+    q = fmaf(t, q, -0.284496736f);
+    q = fmaf(t, q, 0.254829592f);
+    q *= t;
+    const float ex = __builtin_amdgcn_exp2f(-(z * z) * 1.44269504088896341f);
+    const float tail = q * ex;
+    const float two_phi = x >= 0.0f ? 2.0f - tail : tail;
+    u = 0.5f * x * two_phi;
+    du = fmaf(x * ex, 0.39894228040143268f, 0.5f * two_phi);
+}
+
+BASE_DEV void act_grad(float x, int act, float& u, float& du) {
+    if (act) {
+        gelu_grad_as7126(x, u, du);
+    } else {
+        u = fmaxf(x, 0.0f);
+        du = x > 0.0f ? 1.0f : 0.0f;
+    }
+}
+
+// Epilogue of the backward products (accumulator layout as above; rows are
+// grouped rows, or output rows of dW for BW). wpart: this wave's column of
+// the BV partial sums.
+template <int Kind, int TM, int TN>
+BASE_DEV void dma_epilogue_bwd(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                               int64_t mw, int64_t nw, int lane, const int32_t (&trow)[TM],
+                               const float (&gate)[TM], int64_t wpart) {
+    const int64_t cb = nw + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = mw + i * 32 + (lane & 31);
+        const bool rowok = m < tl.rows;
+        const int64_t row = tl.row0 + m;
+        const float g = gate[i];
+        float psum = 0.0f;
+        float cx = 1.0f, dlr = 0.0f;
+        if (Kind == KIND_BX && rowok) {
+            cx = p.mix ? 1.0f - g : 1.0f;
+            dlr = p.dl[row];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = cb + j * 32 + 8 * q;
+                // N % 8 == 0: a run of 4 is wholly inside or outside
+                if (!rowok || n >= p.N) continue;
+                f32x4_t y;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[c] = acc[i][j][4 * q + c];
+                if (Kind == KIND_BZ) {
+                    f32x4_t gu;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        float u, du;
+                        act_grad(y[c], p.act, u, du);
+                        gu[c] = g * u;
+                    }
+                    *(bf16x4_t*)((uint16_t*)p.H + row * p.N + n) = __builtin_convertvector(y, bf16x4_t);
+                    *(bf16x4_t*)((uint16_t*)p.gu + row * p.N + n) = __builtin_convertvector(gu, bf16x4_t);
+                } else if (Kind == KIND_BV) {
+                    const f32x4_t z = __builtin_convertvector(
+                        *(const bf16x4_t*)((const uint16_t*)p.zin + row * p.N + n), f32x4_t);
+                    f32x4_t dz;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        float u, du;
+                        act_grad(z[c], p.act, u, du);
+                        psum = fmaf(y[c], u, psum);
+                        dz[c] = g * y[c] * du;
+                    }
+                    *(bf16x4_t*)((uint16_t*)p.H + row * p.N + n) = __builtin_convertvector(dz, bf16x4_t);
+                } else if (Kind == KIND_BX) {
+                    const f32x4_t d = __builtin_convertvector(
+                        *(const bf16x4_t*)((const uint16_t*)p.dyg + row * p.N + n), f32x4_t);
+                    const f32x4_t wv = __builtin_convertvector(
+                        *(const bf16x4_t*)((const uint16_t*)p.wc + tl.g * p.N + n), f32x4_t);
+                    f32x4_t o;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) o[c] = fmaf(dlr, wv[c], fmaf(cx, d[c], y[c]));
+                    *(bf16x4_t*)((uint16_t*)p.out + (int64_t)trow[i] * p.N + n) =
+                        __builtin_convertvector(o, bf16x4_t);
+                } else {
+                    *(bf16x4_t*)((uint16_t*)p.H + row * p.N + n) = __builtin_convertvector(y, bf16x4_t);
+                }
+            }
+        if (Kind == KIND_BV) {
+            psum += __shfl_xor(psum, 32, 64);
+            if (lane < 32 && rowok) p.part[row * p.nparts + wpart] = psum;
+        }
+    }
+}
+
 // GEN: the FFN2 epilogue of the layer variants instead of eq. 1's
 template <int Kind, int BN, int WM, int WN, bool GEN = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams p) {
-    static_assert(Kind == KIND_FFN1 || Kind == KIND_FFN2, "expert products only");
+    static_assert(Kind != KIND_AFF, "expert products only");
+    // operands read k-major (see above): A for the weight gradients, B for
+    // every backward product but the recomputation of Z
+    constexpr bool AT = Kind == KIND_BW;
+    constexpr bool BT = Kind == KIND_BV || Kind == KIND_BX || Kind == KIND_BW;
+    constexpr bool ROWTOK = Kind == KIND_FFN2 || Kind == KIND_BZ || Kind == KIND_BV ||
+                            Kind == KIND_BX;  // rows need their token and gate
+    static_assert(!BT || BN == 256, "k-major stages are 256 wide");
+    constexpr bool BWD = Kind >= KIND_BZ;
     constexpr int BM = 256, BK = 64, NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -245,6 +399,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
     const int64_t m0 = tl.tm * BM, n0 = tl.tn * BN;
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* B = (const uint16_t*)p.B + g * p.b_gstride;
+    // the K range: a weight gradient sums its group's rows
+    int64_t kbeg = 0, Kc = p.K;
+    if (Kind == KIND_BW) {
+        kbeg = p.kgoff ? p.kgoff[g] : g * p.K;
+        Kc = p.kgoff ? p.kgoff[g + 1] - kbeg : p.K;
+    }
 
     int32_t trow[TM];
     float gate[TM];
@@ -253,38 +413,125 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
         trow[i] = 0;
         gate[i] = 0.0f;
         const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (Kind == KIND_FFN2 && m < tl.rows) {
+        if (ROWTOK && m < tl.rows) {
             trow[i] = p.perm[tl.row0 + m];
             gate[i] = (GEN && p.epi_gate) ? 1.0f : sigmoid_f32(p.s_in[(int64_t)trow[i] * p.E + g]);
         }
     }
 
-    const uint16_t* asrc[AI];
-    const uint16_t* bsrc[BI];
-    int akc[AI], bkc[BI];
+    // forward products, per DMA slot: source of the stage's first step
+    // (null: zeros) and its k offset inside a step
+    const uint16_t* asrc[BWD ? 1 : AI];
+    const uint16_t* bsrc[BWD ? 1 : BI];
+    int akc[BWD ? 1 : AI], bkc[BWD ? 1 : BI];
+    // backward products (every operand row grouped, none gathered): the
+    // slots load through a buffer descriptor rebuilt each step, so a slot's
+    // source is a 32-bit byte offset (one register) and the descriptor's
+    // bound turns rows past the operand, and k-rows past the step's window,
+    // into zeros; a column block past M / N carries an out-of-range marker.
+    uint32_t aoff[BWD ? AI : 1], boff[BWD ? BI : 1];
+    // the k of slot j inside a step: k-major operands the row, others the
+    // chunk's first k
+    auto slot_k = [&](bool kmaj, int wj) -> int {
+        const int slot = wj * 64 + lane;
+        if (kmaj) return slot >> 5;
+        return (((slot % CPR) ^ swz8(slot / CPR)) * 8);
+    };
+    if constexpr (BWD) {
 #pragma unroll
-    for (int j = 0; j < AI; ++j) {
-        const int slot = (wave * AI + j) * 64 + lane;
-        const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
-        akc[j] = c * 8;
-        const int64_t m = m0 + row;
-        asrc[j] = nullptr;
-        if (m < tl.rows) {
-            const int64_t src = (Kind == KIND_FFN1 && p.perm) ? p.perm[tl.row0 + m] : tl.row0 + m;
-            asrc[j] = A + src * p.K + c * 8;
+        for (int j = 0; j < AI; ++j) {
+            const int slot = (wave * AI + j) * 64 + lane;
+            if (AT) {
+                const int row = slot >> 5, c = (slot & 31) ^ swz_t(row);
+                aoff[j] = (m0 + 8 * c < tl.rows) ? (uint32_t)(row * p.lda + 8 * c) * 2u : kOob;
+            } else {
+                const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+                aoff[j] = (uint32_t)(row * p.K + c * 8) * 2u;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            const int slot = (wave * BI + j) * 64 + lane;
+            if (BT) {
+                const int row = slot >> 5, c = (slot & 31) ^ swz_t(row);
+                boff[j] = (n0 + 8 * c < p.N) ? (uint32_t)(row * p.ldb + 8 * c) * 2u : kOob;
+            } else {
+                const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+                boff[j] = (uint32_t)(row * p.K + c * 8) * 2u;
+            }
+        }
+    } else {
+        // expert products of the forward pass: a pointer per slot (A rows
+        // may be gathered through perm)
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            const int slot = (wave * AI + j) * 64 + lane;
+            const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+            akc[j] = c * 8;
+            const int64_t m = m0 + row;
+            asrc[j] = nullptr;
+            if (m < tl.rows) {
+                const int64_t src = (Kind == KIND_FFN1 && p.perm) ? p.perm[tl.row0 + m] : tl.row0 + m;
+                asrc[j] = A + src * p.K + c * 8;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            const int slot = (wave * BI + j) * 64 + lane;
+            const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+            bkc[j] = c * 8;
+            const int64_t n = n0 + row;
+            bsrc[j] = (n < p.N) ? B + n * p.K + c * 8 : nullptr;
         }
     }
-#pragma unroll
-    for (int j = 0; j < BI; ++j) {
-        const int slot = (wave * BI + j) * 64 + lane;
-        const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
-        bkc[j] = c * 8;
-        const int64_t n = n0 + row;
-        bsrc[j] = (n < p.N) ? B + n * p.K + c * 8 : nullptr;
-    }
+    // 32-bit copies of the sizes the backward descriptors are built from
+    const int kc32 = (int)Kc, k32 = (int)p.K, lda32 = (int)p.lda, ldb32 = (int)p.ldb;
+    const int rows32 = (int)tl.rows, m032 = (int)m0, n32 = (int)p.N, n032 = (int)n0;
     const void* zero = (const void*)&g_zero16;
     auto issue = [&](int64_t kt, char* st) {
         const int64_t k0 = kt * BK;
+        if constexpr (BWD) {
+            // descriptors of this step: k-major operands cover the step's
+            // (up to) 64 k-rows from column m0 / n0 on; the others the tile's
+            // valid rows from k0 on (their k tail is masked per slot)
+            // 32-bit min / max only (the launcher keeps every size below
+            // 2^21): branches here would merge paths inside the K loop and
+            // cost the compiler its tracking of which stage the DMAs write
+            const int k0i = (int)k0;
+            const int kv = min(max(kc32 - k0i, 0), BK);
+            int an, bn;
+            const uint16_t *ab, *bb;
+            if (AT) {
+                ab = A + (kbeg + k0) * p.lda + m0;
+                an = max(kv * lda32 + (rows32 - m032) - lda32, 0);
+            } else {
+                ab = A + (tl.row0 + m0) * p.K + k0;
+                an = max(min(rows32 - m032, BM) * k32 - k0i, 0);
+            }
+            if (BT) {
+                bb = B + (kbeg + k0) * p.ldb + n0;
+                bn = max(kv * ldb32 + (n32 - n032) - ldb32, 0);
+            } else {
+                bb = B + n0 * p.K + k0;
+                bn = max(min(n32 - n032, BN) * k32 - k0i, 0);
+            }
+            an *= 2;
+            bn *= 2;
+            const buf_rsrc_t ra = make_rsrc(ab, (uint32_t)an), rb = make_rsrc(bb, (uint32_t)bn);
+#pragma unroll
+            for (int j = 0; j < AI; ++j) {
+                uint32_t v = aoff[j];
+                if (!AT && k0 + slot_k(false, wave * AI + j) >= Kc) v = kOob;
+                dma16_buf(ra, v, st + (wave * AI + j) * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < BI; ++j) {
+                uint32_t v = boff[j];
+                if (!BT && k0 + slot_k(false, wave * BI + j) >= Kc) v = kOob;
+                dma16_buf(rb, v, st + A_BYTES + (wave * BI + j) * 1024);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const void* src = (asrc[j] && k0 + akc[j] < p.K) ? (const void*)(asrc[j] + k0) : zero;
@@ -303,6 +550,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
     const int sx = swz8(lane & 31);
     const int arow0 = (wm * WTM + (lane & 31)) * ROWB;
     const int brow0 = A_BYTES + (wn * WTN + (lane & 31)) * ROWB;
+    // k-major fragments: the lane's byte offset for the wave's first
+    // fragment (first row, chunk and byte within it). Fragment i starts 4 i
+    // chunks further; the swizzle XORs chunk bits 2..4 and leaves bits 0..1
+    // (the lane's place inside the fragment), so its offset is the first one
+    // XOR 64 i bytes.
+    int atoff = 0, btoff = 0;
+    {
+        const int r0 = 8 * (lane >> 5) + ((lane & 15) >> 2);
+        const int sw = swz_t(r0);
+        const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        const int byte = r0 * 512 + 8 * (lane & 1);
+        static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BM == 256, "fragment chunk bits");
+        if (AT) atoff = byte + (((((wm * WTM) >> 3) ^ sw) | low) << 4);
+        if (BT) btoff = A_BYTES + byte + (((((wn * WTN) >> 3) ^ sw) | low) << 4);
+    }
 
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -313,7 +575,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // K steps of 64, padded to an even count (zero blocks past K)
-    const int64_t nk = ((p.K + 2 * BK - 1) / (2 * BK)) * 2;
+    const int64_t nk = ((Kc + 2 * BK - 1) / (2 * BK)) * 2;
     // wait for the step about to be read (the only one in flight) and for
     // every wave's reads of the stage refilled next
     auto ready = [&]() {
@@ -327,9 +589,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
     auto load_sub = [&](const char* st, int s, bf16x8_t (&fa_)[TM], bf16x8_t (&fb_)[TN]) {
         const int co = ((2 * s + (lane >> 5)) ^ sx) * 16;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa_[i] = *(const bf16x8_t*)(st + arow0 + co + i * 32 * ROWB);
+        for (int i = 0; i < TM; ++i)
+            fa_[i] = AT ? tr_frag(st + (atoff ^ (64 * i)) + 16 * s * 512)
+                        : *(const bf16x8_t*)(st + arow0 + co + i * 32 * ROWB);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb_[j] = *(const bf16x8_t*)(st + brow0 + co + j * 32 * ROWB);
+        for (int j = 0; j < TN; ++j)
+            fb_[j] = BT ? tr_frag(st + (btoff ^ (64 * j)) + 16 * s * 512)
+                        : *(const bf16x8_t*)(st + brow0 + co + j * 32 * ROWB);
     };
     auto mfma_sub = [&](const bf16x8_t (&fa_)[TM], const bf16x8_t (&fb_)[TN]) {
 #pragma unroll
@@ -366,7 +632,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
         step(kt + 1, dma64_stage<1>(), dma64_stage<0>());
     }
     wait_vmcnt<0>();
-    if (GEN && Kind == KIND_FFN2)
+    if constexpr (Kind >= KIND_BZ)
+        dma_epilogue_bwd<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate,
+                                       tl.tn * WN + wn);
+    else if constexpr (GEN && Kind == KIND_FFN2)
         dma_epilogue_general<TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
     else
         dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);

@@ -61,6 +61,44 @@ hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2,
                           const int32_t* goff, int32_t* gblk, int64_t rows_total,
                           const Ffn2Epi& epi, hipStream_t st);
 
+// ---- backward products (gemm.hip). Rows are grouped (row r of group e is
+// token perm[r]); group e owns rows goff[e] .. goff[e+1]-1, T = goff[E];
+// gblk: E+1 ints of scratch. Gate g_r = sigmoid(s[perm[r], e]).
+// Z = Xg W1_e^T and gU = g act(Z), both T x F.
+hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, const float* s,
+                        void* Z, void* gU, int64_t T, int64_t E, int64_t D, int64_t F, int dt,
+                        int act, const int32_t* goff, int32_t* gblk, hipStream_t st);
+// V = dYg W2_e (T x F); dZ = g V act'(Z); part[r * bwd_nparts(F, dt) + j]
+// = partial sums over column blocks of V . act(Z)
+int64_t bwd_nparts(int64_t F, int dt);
+hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, const float* s,
+                        const void* Z, void* dZ, float* part, int64_t T, int64_t E, int64_t D,
+                        int64_t F, int dt, int act, const int32_t* goff, int32_t* gblk,
+                        hipStream_t st);
+// dh[perm[r]] = (dZ W1_e)[r] + c dYg[r] + dl[r] w_e, c = 1 (mix 0) or 1 - g
+hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, const float* s,
+                        const void* dYg, const void* w, const float* dl, int mix, void* dh,
+                        int64_t T, int64_t E, int64_t D, int64_t F, int dt, const int32_t* goff,
+                        int32_t* gblk, hipStream_t st);
+// dW_e = P_e^T Q_e: P rows of length M, Q rows of length N, summed over the
+// rows of group e; dW is E x M x N. M % 8 == N % 8 == 0 for bf16.
+hipError_t launch_bwd_w(const void* P, const void* Q, int64_t M, int64_t N, int64_t E,
+                        const int32_t* goff, void* dW, int dt, hipStream_t st);
+
+// ---- grad.hip
+// Xg[r] = h[perm[r]], dYg[r] = dy[perm[r]] (rows of D values of dtype dt)
+hipError_t launch_gather2(const void* h, const void* dy, const int32_t* perm, void* Xg,
+                          void* dYg, int64_t T, int64_t D, int dt, hipStream_t st);
+// dl[r] = g (1 - g) dg with dg = sum of the row's nparts partials, minus
+// dYg[r] . Xg[r] for the convex mix; g = sigmoid(s[perm[r], e]), e the
+// group of r
+hipError_t launch_gate_grad(const float* part, int64_t nparts, const void* Xg, const void* dYg,
+                            const int32_t* perm, const int32_t* goff, const float* s, int mix,
+                            float* dl, int64_t T, int64_t E, int64_t D, int dt, hipStream_t st);
+// dw[e] = sum over the rows r of group e of dl[r] Xg[r]
+hipError_t launch_centroid_grad(const float* dl, const void* Xg, const int32_t* goff, void* dw,
+                                int64_t E, int64_t D, int dt, hipStream_t st);
+
 // ---- layernorm.hip
 // Y[r, :] = LN(X[r, :]) * gamma[e] + beta[e] over D, e = assign[perm[r]] the
 // row's expert, with X[r, :] = x[perm[r], :] (gather != 0) or x[r, :]

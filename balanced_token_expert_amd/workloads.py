@@ -26,7 +26,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids inside a workload's seed space
-TID_H, TID_W, TID_W1, TID_W2, TID_AUX = 0, 1, 2, 3, 4
+TID_H, TID_W, TID_W1, TID_W2, TID_AUX, TID_DY = 0, 1, 2, 3, 4, 5
 ROW_CHUNK = 2048  # token rows per generator chunk
 BLOCK_CHUNK = 100000  # chunk offset of an expert's feed-forward block
 LN_CHUNK = 200000     # chunk offset of the layer-norm parameters (TID_AUX)
@@ -210,6 +210,22 @@ def gen_tokens(wl: Workload, rep: int = 0, rows: Optional[slice] = None,
         elif wl.kind == "skew":
             m = skew[lo:hi]
             z[m] = anchor[None, :] + np.float32(np.sqrt(0.1)) * z[m]
+        a, b = max(lo, r0), min(hi, r1)
+        out[a - r0:b - r0] = z[a - lo:b - lo]
+    return _store(out, wl.dtype)
+
+
+def gen_dy(wl: Workload, rep: int = 0, rows: Optional[slice] = None) -> np.ndarray:
+    """Upstream gradient of the layer output (T x D, or a contiguous row
+    range): N(0, 1) entries in the workload's dtype, drawn per row chunk."""
+    r0 = 0 if rows is None or rows.start is None else rows.start
+    r1 = wl.T if rows is None or rows.stop is None else rows.stop
+    assert 0 <= r0 <= r1 <= wl.T
+    out = np.empty((r1 - r0, wl.D), dtype=np.float32)
+    c0, c1 = r0 // ROW_CHUNK, (r1 + ROW_CHUNK - 1) // ROW_CHUNK
+    for c in range(c0, c1):
+        lo, hi = c * ROW_CHUNK, min(wl.T, (c + 1) * ROW_CHUNK)
+        z = _rng(wl, rep, TID_DY, c).standard_normal((hi - lo, wl.D), dtype=np.float32)
         a, b = max(lo, r0), min(hi, r1)
         out[a - r0:b - r0] = z[a - lo:b - lo]
     return _store(out, wl.dtype)

@@ -115,7 +115,8 @@ typedef enum {
     BASE_OP_AUCTION = 1,
     BASE_OP_GREEDY = 2,
     BASE_OP_LAYER = 3,
-    BASE_OP_LAYER_EX = 4 /* base_layer_forward_ex: LAYER plus two T x D buffers */
+    BASE_OP_LAYER_EX = 4, /* base_layer_forward_ex: LAYER plus two T x D buffers */
+    BASE_OP_LAYER_BWD = 5 /* base_layer_backward */
 } base_op;
 
 size_t base_workspace_bytes(int op, int64_t T, int64_t E, int64_t D, int64_t F,
@@ -254,12 +255,56 @@ int base_layer_forward_ex(const void *h, const void *w, const void *W1,
                           size_t ws_bytes, base_stream_t stream);
 
 /*
+ * base_layer_backward -- gradients of the plain-expert layer (sublayers = 0)
+ * for an upstream gradient dy of its output, with the assignment held fixed:
+ * the affinities that chose the experts carry no gradient and the centroids
+ * learn through the sigmoid gate only (BASE Layers sec. 3.1, learning the
+ * centroids through the gate; page "Paper vs code", gradient into routing:
+ * the released code scores under no_grad). For token t in expert e = a_t,
+ * x = h_t, z = W1_e x, u = act(z), c = W2_e u, g = sigmoid(scores[t][e]):
+ *   dW2_e = sum_t g dy u^T,  dz = g (W2_e^T dy) * act'(z),  dW1_e = sum_t dz x^T
+ *   dg = dy . c (eq. 1) or dy . (c - x) (convex),  dl = g (1 - g) dg
+ *   dh_t = W1_e^T dz + dy (eq. 1) or (1 - g) dy (convex) + dl w_e
+ *   dw_e = sum_t dl x
+ *   h, w, W1, W2, dt, act: as given to the forward call. assign: the T
+ *   expert ids it used (DEVICE; any group sizes, e.g. greedy routing).
+ *   scores: DEVICE T x E fp32, the affinities the forward gated with (its
+ *   `scores` output). dy: DEVICE T x D (dtype dt), original token order.
+ *   opts: HOST, NULL or with sublayers == 0 (mix selects eq. 1 or convex).
+ *   Outputs (DEVICE, dtype dt, overwritten): dh T x D (original order),
+ *   dw E x D, dW1 E x F x D, dW2 E x D x F. An expert with no token gets
+ *   zero gradients.
+ *   Precision: bf16 products with fp32 accumulation; the saved
+ *   pre-activations, gate * act, dz and the grouped rows of h and dy are
+ *   stored as bf16 (fp32 for dt = F32); gate sums in fp32.
+ *   stats: device pointer or NULL. Device-side error: stats->status =
+ *   BASE_ERR_UNBALANCED when an id of assign lies outside [0, E) (the
+ *   gradients are then undefined).
+ *   Errors: INVALID_ARG as base_layer_forward (null pointer, sizes, dtype,
+ *   act, mix, workspace); UNSUPPORTED for sublayers != 0, D or F above
+ *   2^20, and the bf16 layout limits of base_layer_forward (plus dy, dh,
+ *   dW1, dW2 16-byte aligned). Phase events (base_set_phase_events): [0] start, [1] after
+ *   the grouping and Z, [2] after dz and dl, [3] after dW2, [4] after dW1,
+ *   [5] at the end.
+ *   ws: scratch of base_workspace_bytes(BASE_OP_LAYER_BWD, T, E, D, F, dt).
+ */
+int base_layer_backward(const void *h, const void *w, const void *W1,
+                        const void *W2, int64_t T, int64_t E, int64_t D,
+                        int64_t F, int dt, int act, const int32_t *assign,
+                        const float *scores, const void *dy, void *dh,
+                        void *dw, void *dW1, void *dW2,
+                        base_auction_stats *stats, const base_layer_opts *opts,
+                        void *ws, size_t ws_bytes, base_stream_t stream);
+
+/*
  * base_set_phase_events -- optional tracing. When `events` is non-NULL, every
- * later base_layer_forward call on this host thread records n (<= 6) HIP
+ * later base_layer_forward(_ex) and base_layer_backward call on this host
+ * thread records n (<= 6) HIP
  * events (hipEvent_t, created by the caller) on its stream: [0] before the
  * affinity product, [1] after it, [2] after routing and grouping, [3] after
  * the first expert product (base_layer_forward_ex with blocks: after the
- * last block's first product), [4] at the end, [5] = [4]. The
+ * last block's first product), [4] at the end, [5] = [4] (the backward
+ * call's six points are listed with it). The
  * caller reads durations with hipEventElapsedTime. NULL turns tracing off.
  * Returns BASE_ERR_INVALID_ARG if n is outside [0, 6].
  */

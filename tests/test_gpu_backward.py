@@ -1,0 +1,154 @@
+"""Parity of base_layer_backward against the oracle's fp64 gradients
+(oracle.layer_backward), with the gate taken from the scores the GPU's
+affinity product gave. Shapes span several 256-wide tiles with ragged ends
+in every dimension the backward products tile (rows of a group, D, F, and
+the k = tokens-per-expert sum of the weight gradients); assignments are
+balanced, ragged, or leave an expert empty; both mixes, both activations.
+Tolerances: 1e-5 (fp32), 2e-2 (bf16) max-abs relative per gradient.
+
+At the large workload's full size (T = 65536, E = 128, D = 2048, F = 8192,
+the configuration the benchmark times), a few experts' gradients are
+checked against the oracle computed for those experts only."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from balanced_token_expert_amd import api
+from balanced_token_expert_amd import workloads as W
+from tests.gpu_util import dev_to_f64, f64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # T, E, D, F, dtype, act, kind, mix, assignment
+    dict(T=512, E=8, D=64, F=256, dtype="f32", act="relu", kind="iid", mix=0, asg="balanced"),
+    dict(T=600, E=6, D=72, F=96, dtype="f32", act="gelu", kind="mixture", mix=1, asg="ragged"),
+    dict(T=1536, E=4, D=320, F=520, dtype="bf16", act="gelu", kind="iid", mix=0, asg="balanced"),
+    dict(T=1536, E=4, D=320, F=520, dtype="bf16", act="gelu", kind="iid", mix=1, asg="ragged"),
+    dict(T=2048, E=8, D=256, F=512, dtype="bf16", act="relu", kind="mixture", mix=1,
+         asg="balanced"),
+    dict(T=1000, E=5, D=264, F=200, dtype="bf16", act="gelu", kind="iid", mix=0, asg="empty"),
+    dict(T=3000, E=3, D=136, F=784, dtype="bf16", act="relu", kind="skew", mix=0, asg="ragged"),
+]
+
+
+def _assignment(T, E, how, seed):
+    rng = np.random.default_rng(seed)
+    if how == "balanced":
+        return rng.permutation(np.repeat(np.arange(E), T // E)).astype(np.int32)
+    if how == "empty":  # expert E-1 gets nothing, the rest ragged
+        return rng.integers(0, E - 1, T).astype(np.int32)
+    # ragged: skewed group sizes, every expert present
+    p = np.arange(1, E + 1, dtype=np.float64) ** 2
+    a = rng.choice(E, size=T, p=p / p.sum()).astype(np.int32)
+    a[:E] = np.arange(E)
+    return a
+
+
+def _run(wl, host, a, mix, dev=None):
+    dev = dev or {k: to_dev(v, wl.dtype) for k, v in host.items()}
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    s = api.base_affinity(dev["h"], dev["w"])
+    assign = torch.from_numpy(a).cuda()
+    r = api.base_layer_backward(dev["h"], dev["w"], dev["W1"], dev["W2"], act, assign, s,
+                                dev["dy"], mix=mix)
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    return r, s.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_backward_parity(ci):
+    c = CASES[ci]
+    wl = W.custom(c["T"], c["E"], c["D"], c["F"], dtype=c["dtype"], act=c["act"],
+                  kind=c["kind"], wid=960 + ci)
+    host = W.gen_all(wl)
+    host["dy"] = W.gen_dy(wl)
+    a = _assignment(wl.T, wl.E, c["asg"], ci)
+    r, s = _run(wl, host, a, c["mix"])
+    mix = "convex" if c["mix"] else "residual"
+    dh, dw, dW1, dW2 = oracle.layer_backward(
+        f64(host["h"], wl.dtype), f64(host["w"], wl.dtype), f64(host["W1"], wl.dtype),
+        f64(host["W2"], wl.dtype), a, wl.act, f64(host["dy"], wl.dtype), mix=mix, s=s)
+    tol = 1e-5 if wl.dtype == "f32" else 2e-2
+    got = {"dh": dev_to_f64(r["dh"]), "dw": dev_to_f64(r["dw"]),
+           "dW1": dev_to_f64(r["dW1"]), "dW2": dev_to_f64(r["dW2"])}
+    ref = {"dh": dh, "dw": dw, "dW1": np.stack([dW1[e] for e in range(wl.E)]),
+           "dW2": np.stack([dW2[e] for e in range(wl.E)])}
+    errs = {k: rel_err(got[k], ref[k]) for k in got}
+    print(ci, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    if c["asg"] == "empty":
+        # no token: exactly zero gradients for the expert and its centroid
+        assert not got["dW1"][-1].any() and not got["dW2"][-1].any() and not got["dw"][-1].any()
+
+
+def test_backward_zero_upstream_gradient_is_zero():
+    wl = W.custom(1024, 4, 256, 512, dtype="bf16", act="gelu", kind="iid", wid=975)
+    host = W.gen_all(wl)
+    host["dy"] = np.zeros((wl.T, wl.D), dtype=host["h"].dtype)
+    r, _ = _run(wl, host, _assignment(wl.T, wl.E, "balanced", 1), 1)
+    for k in ("dh", "dw", "dW1", "dW2"):
+        assert not r[k].float().abs().max().item(), k
+
+
+def test_backward_out_of_range_id_reported():
+    wl = W.custom(512, 4, 64, 128, dtype="bf16", act="relu", kind="iid", wid=976)
+    host = W.gen_all(wl)
+    host["dy"] = W.gen_dy(wl)
+    dev = {k: to_dev(v, wl.dtype) for k, v in host.items()}
+    a = _assignment(wl.T, wl.E, "balanced", 2)
+    a[7] = wl.E  # outside [0, E)
+    s = api.base_affinity(dev["h"], dev["w"])
+    r = api.base_layer_backward(dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_RELU,
+                                torch.from_numpy(a).cuda(), s, dev["dy"])
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == api.BASE_ERR_UNBALANCED
+
+
+def test_backward_full_size_sampled_experts():
+    """The large workload at full size: every gradient of three experts (and
+    their tokens' dh rows, their centroids' dw rows) against the oracle."""
+    wl = W.workload(5)
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    with ThreadPoolExecutor(16) as ex:
+        w = W.gen_centroids(wl)
+        h = np.concatenate(list(ex.map(
+            lambda r0: W.gen_tokens(wl, rows=slice(r0, min(T, r0 + 4096)), centroids=w),
+            range(0, T, 4096))))
+        dy = np.concatenate(list(ex.map(
+            lambda r0: W.gen_dy(wl, rows=slice(r0, min(T, r0 + 4096))), range(0, T, 4096))))
+        W1 = list(ex.map(lambda e: W.gen_w1(wl, e), range(E)))
+        W2 = list(ex.map(lambda e: W.gen_w2(wl, e), range(E)))
+    dev = {"h": to_dev(h, wl.dtype), "w": to_dev(w, wl.dtype), "dy": to_dev(dy, wl.dtype)}
+    dev["W1"] = torch.empty((E, F, D), dtype=torch.bfloat16, device="cuda")
+    dev["W2"] = torch.empty((E, D, F), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        dev["W1"][e].copy_(to_dev(W1[e], wl.dtype))
+        dev["W2"][e].copy_(to_dev(W2[e], wl.dtype))
+    # the balanced assignment of the benchmark's forward
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=500 * T)
+    fwd = api.base_layer_forward(dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_GELU,
+                                 api.BASE_ROUTE_BALANCED, c)
+    torch.cuda.synchronize()
+    assert api.read_stats(fwd["stats"]).status == 0
+    r = api.base_layer_backward(dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_GELU,
+                                fwd["assign"], fwd["scores"], dev["dy"])
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    a = fwd["assign"].cpu().numpy()
+    experts = [0, 77, E - 1]
+    rows = np.nonzero(np.isin(a, experts))[0]
+    s = fwd["scores"].cpu().numpy().astype(np.float64)
+    dh, dw, dW1, dW2 = oracle.layer_backward(
+        f64(h, wl.dtype), f64(w, wl.dtype), lambda e: f64(W1[e], wl.dtype),
+        lambda e: f64(W2[e], wl.dtype), a, wl.act, f64(dy, wl.dtype), s=s, experts=experts)
+    assert rel_err(dev_to_f64(r["dh"][torch.from_numpy(rows).cuda()]), dh[rows]) <= 2e-2
+    for e in experts:
+        assert rel_err(dev_to_f64(r["dw"][e]), dw[e]) <= 2e-2, e
+        assert rel_err(dev_to_f64(r["dW1"][e]), dW1[e]) <= 2e-2, e
+        assert rel_err(dev_to_f64(r["dW2"][e]), dW2[e]) <= 2e-2, e
