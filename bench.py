@@ -254,6 +254,49 @@ def layer_variants(wl, hd, wd, W1d, W2d, act, c, reps=5):
     return res
 
 
+def layer_backward(wl, hd, wd, W1d, W2d, act, lay, reps=5):
+    """base_layer_backward on the same inputs, with the assignment and the
+    scores of the last balanced forward step and a seeded upstream gradient
+    (eq. 1's residual mix). Median ms of the whole call and of its phases
+    (library phase events): grouping + Z = X W1^T, dZ and the gate gradient
+    (V = dY W2), dW2, dW1, and dX + dh + dw; each product is 2 T D F flops."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    dt = api.BASE_BF16 if wl.dtype == "bf16" else api.BASE_F32
+    with ThreadPoolExecutor(16) as ex:
+        dy = np.concatenate(list(ex.map(lambda r0: W.gen_dy(wl, rows=slice(r0, min(T, r0 + 4096))),
+                                        range(0, T, 4096))))
+    dyd = to_dev(dy, wl.dtype)
+    out = dict(dh=torch.empty_like(hd), dw=torch.empty_like(wd), dW1=torch.empty_like(W1d),
+               dW2=torch.empty_like(W2d), stats=api.new_stats(),
+               ws=api.workspace(api.BASE_OP_LAYER_BWD, T, E, D, F, dt))
+
+    def call():
+        api.base_layer_backward(hd, wd, W1d, W2d, act, lay["assign"], lay["scores"], dyd, **out)
+    call()
+    torch.cuda.synchronize()
+    ev = HipEvents(6 * reps)
+    for i in range(reps):
+        api.base_set_phase_events(ev.block(6 * i), 6)
+        call()
+    torch.cuda.synchronize()
+    api.base_set_phase_events(None, 0)
+    names = ("group_z", "dz_gate", "dW2", "dW1", "dx_dw")
+    ph = {n: float(np.median([ev.ms(6 * i + j, 6 * i + j + 1) for i in range(reps)]))
+          for j, n in enumerate(names)}
+    tot = float(np.median([ev.ms(6 * i, 6 * i + 5) for i in range(reps)]))
+    flop = 2.0 * T * D * F
+    st = api.read_stats(out["stats"])
+    del out
+    return {"ms": round(tot, 4), "tokens_per_s": round(T / (tot * 1e-3), 1),
+            "tflops": round(5 * flop / (tot * 1e-3) / 1e12, 1),
+            "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+            "phase_tflops": {k: round(flop / (v * 1e-3) / 1e12, 1) for k, v in ph.items()},
+            "mix": "residual", "status": st.status}
+
+
 def auction_solve(reps=10):
     """Auction solve ms on the mixture workload (device-resident fp32 scores)."""
     import torch
@@ -328,6 +371,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-auction", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -440,6 +484,8 @@ def main():
                            "uniform_share": round(1.0 / E, 5)},
            "roofline": roof, "wall_s_timed": round(wall, 3)}
     res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
+    if not args.no_backward:
+        res["layer_backward"] = layer_backward(wl, hd, wd, W1d, W2d, act, lay)
     if not args.no_variants:
         res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c)
     if not args.no_auction:
