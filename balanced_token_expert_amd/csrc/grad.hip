@@ -95,28 +95,61 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* part, int64
     }
 }
 
-// block (x, e): columns 512 x .. 512 x + 511 of dw[e], two per thread
+// block (x, e): columns 256 x .. 256 x + 255 of dw[e]. Wave w sums the
+// rows goff[e] + w, + 4, ...; lane l owns columns 4 l .. 4 l + 3 (one 8-byte
+// bf16 or 16-byte fp32 load per row), so each wave streams whole 512-byte
+// (1 KB) row pieces. The four waves' sums meet in LDS in a fixed order.
 template <int DT>
 __global__ __launch_bounds__(256) void centroid_grad_kernel(const float* dl, const void* Xg,
                                                             const int32_t* goff, void* dw,
-                                                            int64_t D) {
+                                                            int64_t D, int vec) {
+    __shared__ float red[4][256];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t e = blockIdx.y;
-    const int64_t d = (int64_t)blockIdx.x * 512 + 2 * threadIdx.x;
-    if (d >= D) return;
-    const bool two = d + 1 < D;
+    const int64_t d0 = (int64_t)blockIdx.x * 256 + 4 * lane;
     const int64_t r0 = goff[e], r1 = goff[e + 1];
-    float a0 = 0.0f, a1 = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) {
-        const float c = dl[r];
-        a0 = fmaf(c, ld_elem<DT>(Xg, r * D + d), a0);
-        if (two) a1 = fmaf(c, ld_elem<DT>(Xg, r * D + d + 1), a1);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (d0 < D) {
+        if (vec) {  // d0 + 3 < D: D % 4 == 0 (fp32) or D % 8 == 0 (bf16)
+#pragma unroll 4
+            for (int64_t r = r0 + wv; r < r1; r += 4) {
+                const float c = dl[r];
+                float x[4];
+                if (DT) {
+                    const uint2 u = *(const uint2*)((const uint16_t*)Xg + r * D + d0);
+                    x[0] = __uint_as_float(u.x << 16);
+                    x[1] = __uint_as_float(u.x & 0xffff0000u);
+                    x[2] = __uint_as_float(u.y << 16);
+                    x[3] = __uint_as_float(u.y & 0xffff0000u);
+                } else {
+                    const float4 v = *(const float4*)((const float*)Xg + r * D + d0);
+                    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = fmaf(c, x[i], a[i]);
+            }
+        } else {
+            for (int64_t r = r0 + wv; r < r1; r += 4) {
+                const float c = dl[r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (d0 + i < D) a[i] = fmaf(c, ld_elem<DT>(Xg, r * D + d0 + i), a[i]);
+            }
+        }
     }
-    if (DT) {
-        ((uint16_t*)dw)[e * D + d] = f32_to_bf16(a0);
-        if (two) ((uint16_t*)dw)[e * D + d + 1] = f32_to_bf16(a1);
-    } else {
-        ((float*)dw)[e * D + d] = a0;
-        if (two) ((float*)dw)[e * D + d + 1] = a1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wv][4 * lane + i] = a[i];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t d = d0 + i;
+            if (d >= D) continue;
+            const int j = 4 * lane + i;
+            const float v = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
+            if (DT) ((uint16_t*)dw)[e * D + d] = f32_to_bf16(v);
+            else ((float*)dw)[e * D + d] = v;
+        }
     }
 }
 
@@ -154,11 +187,16 @@ hipError_t launch_gate_grad(const float* part, int64_t nparts, const void* Xg, c
 
 hipError_t launch_centroid_grad(const float* dl, const void* Xg, const int32_t* goff, void* dw,
                                 int64_t E, int64_t D, int dt, hipStream_t st) {
-    const dim3 grid((unsigned)((D + 511) / 512), (unsigned)E);
+    const dim3 grid((unsigned)((D + 255) / 256), (unsigned)E);
+    // whole 4-column pieces load as one vector when every row start allows
+    const int vec = dt ? (D % 8 == 0 && ((uintptr_t)Xg & 7) == 0)
+                       : (D % 4 == 0 && ((uintptr_t)Xg & 15) == 0);
     if (dt)
-        hipLaunchKernelGGL(centroid_grad_kernel<1>, grid, dim3(256), 0, st, dl, Xg, goff, dw, D);
+        hipLaunchKernelGGL(centroid_grad_kernel<1>, grid, dim3(256), 0, st, dl, Xg, goff, dw, D,
+                           vec);
     else
-        hipLaunchKernelGGL(centroid_grad_kernel<0>, grid, dim3(256), 0, st, dl, Xg, goff, dw, D);
+        hipLaunchKernelGGL(centroid_grad_kernel<0>, grid, dim3(256), 0, st, dl, Xg, goff, dw, D,
+                           vec);
     return hipGetLastError();
 }
 
