@@ -66,6 +66,7 @@ struct GemmParams {
     float* part;            // BV: partial sums of V . act(Z), nparts per grouped row
     int64_t nparts;
     int mix;                // BX: 0 residual (c = 1), 1 convex (c = 1 - gate)
+    int a_bytes;            // persistent FFN1 with gathered rows: bytes of h (< 2^31)
 };
 
 // The tile a block computes: group g, tile (tm, tn), and the group's rows
@@ -550,6 +551,45 @@ static hipError_t run_dma64(const GemmParams& p, int32_t* gblk, int64_t rows_tot
     return hipGetLastError();
 }
 
+// Persistent launch of the backward products: one block per CU (a block
+// holds 128 KB of LDS stages and 512 threads of 256 registers, so a CU runs
+// one at a time), a multiple of 8 so every XCD gets the same number.
+static int64_t cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            c > 0)
+            n = c;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// The persistent kernel addresses a step's operands with 32-bit offsets:
+// widths up to 2^20 and, for rows gathered through perm, all of h below 2^31
+// bytes. Larger problems take the one-tile-per-block kernel.
+static bool pers_fits(int64_t K, int64_t N, int64_t gathered_bytes) {
+    const int64_t lim = int64_t(1) << 20;
+    return K <= lim && N <= lim && gathered_bytes < (int64_t(1) << 31);
+}
+
+template <int Kind, bool GEN = false, bool GATHER = false>
+static hipError_t run_pers(const GemmParams& p, int32_t* gblk, int64_t rows_total,
+                           hipStream_t st) {
+    const int64_t tiles = grid_blocks<256, 256>(p, gblk, rows_total, st);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    int64_t grid = (cu_count() + 7) / 8 * 8;
+    const int64_t t8 = (tiles + 7) / 8 * 8;
+    if (grid > t8) grid = t8;
+    hipLaunchKernelGGL((gemm_bf16_pers_kernel<Kind, 4, 2, GEN, GATHER>), dim3((unsigned)grid),
+                       dim3(512), 0, st, p, tiles);
+    return hipGetLastError();
+}
+
 template <int Kind>
 static hipError_t run_f32_bwd(const GemmParams& p, int32_t* gblk, int64_t rows_total,
                               hipStream_t st) {
@@ -587,6 +627,12 @@ hipError_t launch_ffn1(const void* h, const int32_t* perm, const void* W1, void*
     p.perm = perm; p.b_gstride = F * D; p.H = H; p.act = act;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32<KIND_FFN1>(p, gblk, rows_total, st);
+    const int64_t hb = perm ? rows_total * D * 2 : 0;
+    if (pers_fits(D, F, hb)) {
+        p.a_bytes = (int)hb;
+        return perm ? run_pers<KIND_FFN1, false, true>(p, gblk, rows_total, st)
+                    : run_pers<KIND_FFN1>(p, gblk, rows_total, st);
+    }
     return run_dma64<KIND_FFN1, 256, 4, 2>(p, gblk, rows_total, st);
 }
 
@@ -599,6 +645,7 @@ hipError_t launch_ffn2(const void* H, const int32_t* perm, const void* W2, const
     p.perm = perm; p.b_gstride = D * F; p.s_in = s; p.E = E; p.h = h; p.out = out;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
+    if (pers_fits(F, D, 0)) return run_pers<KIND_FFN2>(p, gblk, rows_total, st);
     return run_dma64<KIND_FFN2, 256, 4, 2>(p, gblk, rows_total, st);
 }
 
@@ -617,6 +664,7 @@ hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2, co
     p.xr = epi.xr;
     p.xo = epi.xo;
     if (dt == 0) return run_f32<KIND_FFN2>(p, gblk, rows_total, st);
+    if (pers_fits(F, D, 0)) return run_pers<KIND_FFN2, true>(p, gblk, rows_total, st);
     return run_dma64<KIND_FFN2, 256, 4, 2, true>(p, gblk, rows_total, st);
 }
 
@@ -633,7 +681,7 @@ hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, con
     p.perm = perm; p.b_gstride = F * D; p.s_in = s; p.E = E; p.H = Z; p.gu = gU; p.act = act;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32_bwd<KIND_BZ>(p, gblk, T, st);
-    return run_dma64<KIND_BZ, 256, 4, 2>(p, gblk, T, st);
+    return run_pers<KIND_BZ>(p, gblk, T, st);
 }
 
 hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, const float* s,
@@ -646,7 +694,7 @@ hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, co
     p.part = part; p.nparts = bwd_nparts(F, dt); p.act = act;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32_bwd<KIND_BV>(p, gblk, T, st);
-    return run_dma64<KIND_BV, 256, 4, 2>(p, gblk, T, st);
+    return run_pers<KIND_BV>(p, gblk, T, st);
 }
 
 hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, const float* s,
@@ -659,7 +707,7 @@ hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, con
     p.dl = dl; p.mix = mix; p.out = dh;
     p.goff = goff; p.gblk = gblk;
     if (dt == 0) return run_f32_bwd<KIND_BX>(p, gblk, T, st);
-    return run_dma64<KIND_BX, 256, 4, 2>(p, gblk, T, st);
+    return run_pers<KIND_BX>(p, gblk, T, st);
 }
 
 hipError_t launch_bwd_w(const void* P, const void* Q, int64_t M, int64_t N, int64_t E,
@@ -668,7 +716,7 @@ hipError_t launch_bwd_w(const void* P, const void* Q, int64_t M, int64_t N, int6
     p.A = P; p.B = Q; p.M = M; p.N = N; p.K = 0; p.groups = E;
     p.lda = M; p.ldb = N; p.kgoff = goff; p.H = dW;
     if (dt == 0) return run_f32_bwd<KIND_BW>(p, nullptr, 0, st);
-    return run_dma64<KIND_BW, 256, 4, 2>(p, nullptr, 0, st);
+    return run_pers<KIND_BW>(p, nullptr, 0, st);
 }
 
 }  // namespace base

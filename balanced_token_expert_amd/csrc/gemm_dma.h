@@ -640,3 +640,304 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma64_kernel(GemmParams
     else
         dma_epilogue<Kind, TM, TN>(p, acc, tl, m0 + wm * WTM, n0 + wn * WTN, lane, trow, gate);
 }
+
+// Persistent form of the expert products: one block per CU walks a run of
+// tiles (each XCD owns a contiguous run of the logical tiles; its blocks take
+// every (blocks per XCD)-th one, so the tiles in flight on an XCD are
+// neighbours that share operand tiles in its L2). The last two K steps of a
+// tile issue the DMAs of the next tile's first two steps, so when its K loop
+// ends the registers already hold the next tile's first fragments and its
+// epilogue runs while the next tile's first loads are in flight. A slot's
+// 32-bit offset inside a step's window does not depend on the tile (the
+// per-step buffer descriptor carries the tile), except for the first
+// forward product's rows gathered through perm: their offsets from the
+// start of h are loaded for the next tile while the current one runs, and
+// a row past its group loads zeros. Rows past a group, the k
+// tail of an operand with k contiguous, and k-rows past the step's window
+// read zeros; columns past M / N of a k-major operand read the start of the
+// next k-row of the same tensor (zeros past its end), which only reaches
+// accumulator rows / columns the epilogue discards.
+BASE_DEV int uni32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+BASE_DEV int64_t uni64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// GATHER: the first forward product with its rows gathered through perm
+template <int Kind, int WM, int WN, bool GEN = false, bool GATHER = false>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pers_kernel(GemmParams p, int64_t ntiles) {
+    static_assert(Kind != KIND_AFF, "expert products");
+    static_assert(!GATHER || Kind == KIND_FFN1, "only the first forward product gathers");
+    constexpr bool AT = Kind == KIND_BW;
+    constexpr bool BT = Kind == KIND_BV || Kind == KIND_BX || Kind == KIND_BW;
+    constexpr bool ROWTOK = Kind != KIND_BW && Kind != KIND_FFN1;
+    constexpr bool gather = GATHER;
+    constexpr int BM = 256, BN = 256, BK = 64, NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int ROWB = BK * 2, CPR = ROWB / 16;
+    constexpr int A_BYTES = BM * ROWB;
+    constexpr int AI = BM * CPR / NT, BI = BN * CPR / NT;
+    static_assert(AI >= 1 && BI >= 1 && TM >= 1 && TN >= 1, "tile shape");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // the launch covers ntiles logical tiles (ragged groups: the block map's
+    // own count)
+    const int64_t nt = p.goff ? (int64_t)p.gblk[p.groups] : ntiles;
+    const int64_t xcd = blockIdx.x & 7, bper = gridDim.x >> 3;
+    const int64_t per = nt >> 3, rem = nt & 7;
+    const int64_t t0 = xcd * per + (xcd < rem ? xcd : rem);
+    const int64_t t_end = t0 + per + (xcd < rem ? 1 : 0);
+    int64_t lid = t0 + (blockIdx.x >> 3);
+
+    struct TS {
+        Tile t;
+        int64_t kbeg;
+        int Kc, nk, ok;
+    };
+    auto tile_at = [&](int64_t l) -> TS {
+        TS s;
+        s.t = Tile{0, 0, 0, 0, 0};
+        s.kbeg = 0;
+        s.Kc = 0;
+        s.nk = 0;
+        s.ok = l < t_end && locate_tile<BM, BN>(p, l, s.t);
+        if (s.ok) {
+            s.Kc = (int)p.K;
+            if (Kind == KIND_BW) {
+                s.kbeg = p.kgoff ? p.kgoff[s.t.g] : s.t.g * p.K;
+                s.Kc = p.kgoff ? (int)(p.kgoff[s.t.g + 1] - s.kbeg) : (int)p.K;
+            }
+            // at least two steps (an empty group runs two zero steps): the
+            // last two steps of every tile load the next tile's first two
+            s.nk = s.Kc > 0 ? ((s.Kc + 2 * BK - 1) / (2 * BK)) * 2 : 2;
+        }
+        // uniform by construction; readfirstlane keeps them in scalar
+        // registers, so choosing between this tile and the next one inside
+        // the K loop is a scalar select, not a branch or a vector select
+        s.t.g = uni64(s.t.g);
+        s.t.tm = uni64(s.t.tm);
+        s.t.tn = uni64(s.t.tn);
+        s.t.row0 = uni64(s.t.row0);
+        s.t.rows = uni64(s.t.rows);
+        s.kbeg = uni64(s.kbeg);
+        s.Kc = uni32(s.Kc);
+        s.nk = uni32(s.nk);
+        s.ok = uni32(s.ok);
+        return s;
+    };
+    TS cur = tile_at(lid);
+    if (!cur.ok) return;
+    TS nxt = tile_at(lid + bper);
+
+    uint32_t aoff[AI], boff[BI], agn[AI];
+    // k offset of a k-contiguous slot: with an even number of slots per wave,
+    // slot j's row is 8 (wave AI + j) + lane / 8 and its chunk
+    // (lane % 8) ^ (lane / 16) ^ 4 (j % 2), so one register serves all j
+    static_assert(AI % 2 == 0 && BI % 2 == 0 && CPR == 8, "slot chunk pattern");
+    const int kc0 = ((lane & 7) ^ (lane >> 4)) * 8;
+#pragma unroll
+    for (int j = 0; j < AI; ++j) {
+        const int slot = (wave * AI + j) * 64 + lane;
+        if (AT) {
+            const int row = slot >> 5, c = (slot & 31) ^ swz_t(row);
+            aoff[j] = (uint32_t)(row * p.lda + 8 * c) * 2u;
+        } else {
+            const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+            aoff[j] = (uint32_t)(row * p.K + c * 8) * 2u;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int slot = (wave * BI + j) * 64 + lane;
+        if (BT) {
+            const int row = slot >> 5, c = (slot & 31) ^ swz_t(row);
+            boff[j] = (uint32_t)(row * p.ldb + 8 * c) * 2u;
+        } else {
+            const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+            boff[j] = (uint32_t)(row * p.K + c * 8) * 2u;
+        }
+    }
+    // gathered rows: byte offsets from the start of h of tile s's slots
+    // (kOob past the group)
+    auto gather_offs = [&](const TS& s, uint32_t (&o)[AI]) {
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            const int slot = (wave * AI + j) * 64 + lane;
+            const int row = slot / CPR, c = (slot % CPR) ^ swz8(row);
+            const int64_t m = s.t.tm * BM + row;
+            o[j] = kOob;
+            if (s.ok && m < s.t.rows)
+                o[j] = (uint32_t)((int64_t)p.perm[s.t.row0 + m] * p.K + c * 8) * 2u;
+        }
+    };
+    if (gather) {
+        gather_offs(cur, aoff);
+        gather_offs(nxt, agn);
+    }
+    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* Bp = (const uint16_t*)p.B;
+    const int k32 = (int)p.K, lda32 = (int)p.lda, ldb32 = (int)p.ldb;
+
+    // DMAs of step k0 / BK of tile s into stage st (a tile that does not
+    // exist loads zeros)
+    auto issue = [&](const TS& s, bool sn, int k0, char* st) {
+        const int kv = min(max(s.Kc - k0, 0), BK);
+        const int m0 = (int)(s.t.tm * BM), n0 = (int)(s.t.tn * BN);
+        const uint16_t* B = Bp + s.t.g * p.b_gstride;
+        int an, bn;
+        const uint16_t *ab, *bb;
+        if (AT) {
+            ab = A + (s.kbeg + k0) * p.lda + m0;
+            an = max(kv * lda32 - m0, 0);
+        } else if (gather) {
+            ab = A + k0;  // the whole of h (its size fits 32 bits: checked at launch)
+            an = max(p.a_bytes / 2 - k0, 0);
+        } else {
+            ab = A + (s.t.row0 + m0) * p.K + k0;
+            an = max(min((int)s.t.rows - m0, BM) * k32 - k0, 0);
+        }
+        if (BT) {
+            bb = B + (s.kbeg + k0) * p.ldb + n0;
+            bn = max(kv * ldb32 - n0, 0);
+        } else {
+            bb = B + (int64_t)n0 * p.K + k0;
+            bn = max(min((int)p.N - n0, BN) * k32 - k0, 0);
+        }
+        if (!s.ok) an = bn = 0;
+        const buf_rsrc_t ra = make_rsrc(ab, (uint32_t)an * 2u), rb = make_rsrc(bb, (uint32_t)bn * 2u);
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            uint32_t v = (gather && sn) ? agn[j] : aoff[j];
+            if (!AT && k0 + (kc0 ^ (32 * (j & 1))) >= s.Kc) v = kOob;
+            dma16_buf(ra, v, st + (wave * AI + j) * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            uint32_t v = boff[j];
+            if (!BT && k0 + (kc0 ^ (32 * (j & 1))) >= s.Kc) v = kOob;
+            dma16_buf(rb, v, st + A_BYTES + (wave * BI + j) * 1024);
+        }
+    };
+
+    int32_t trow[TM];
+    float gate[TM];
+    auto rows_of = [&](const TS& s, int32_t (&tr)[TM], float (&ga)[TM]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            tr[i] = 0;
+            ga[i] = 0.0f;
+            const int64_t m = s.t.tm * BM + wm * WTM + i * 32 + (lane & 31);
+            if (ROWTOK && s.ok && m < s.t.rows) {
+                tr[i] = p.perm[s.t.row0 + m];
+                ga[i] = (GEN && p.epi_gate) ? 1.0f
+                                            : sigmoid_f32(p.s_in[(int64_t)tr[i] * p.E + s.t.g]);
+            }
+        }
+    };
+    rows_of(cur, trow, gate);
+
+    int atoff = 0, btoff = 0;
+    {
+        const int r0 = 8 * (lane >> 5) + ((lane & 15) >> 2);
+        const int sw = swz_t(r0);
+        const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        const int byte = r0 * 512 + 8 * (lane & 1);
+        if (AT) atoff = byte + (((((wm * WTM) >> 3) ^ sw) | low) << 4);
+        if (BT) btoff = A_BYTES + byte + (((((wn * WTN) >> 3) ^ sw) | low) << 4);
+    }
+    const int sx = swz8(lane & 31);
+    const int arow0 = (wm * WTM + (lane & 31)) * ROWB;
+    const int brow0 = A_BYTES + (wn * WTN + (lane & 31)) * ROWB;
+
+    f32x16_t acc[TM][TN];
+    auto ready = [&]() {
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+    };
+    bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+    auto load_sub = [&](const char* st, int s, bf16x8_t (&fa_)[TM], bf16x8_t (&fb_)[TN]) {
+        const int co = ((2 * s + (lane >> 5)) ^ sx) * 16;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa_[i] = AT ? tr_frag(st + (atoff ^ (64 * i)) + 16 * s * 512)
+                        : *(const bf16x8_t*)(st + arow0 + co + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb_[j] = BT ? tr_frag(st + (btoff ^ (64 * j)) + 16 * s * 512)
+                        : *(const bf16x8_t*)(st + brow0 + co + j * 32 * ROWB);
+    };
+    auto mfma_sub = [&](const bf16x8_t (&fa_)[TM], const bf16x8_t (&fb_)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
+    };
+    // step kt of the current tile in stage `cs`; refills `cs` with step
+    // kt + 2 of this tile or, in the last two steps, of the next tile
+    auto step = [&](int kt, char* cs, char* ns) {
+        load_sub(cs, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a0, b0);
+        load_sub(cs, 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a1, b1);
+        load_sub(cs, 3, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a0, b0);
+        ready();
+        const bool to_next = kt + 2 >= cur.nk;
+        issue(to_next ? nxt : cur, to_next, (to_next ? kt + 2 - cur.nk : kt + 2) * BK, cs);
+        load_sub(ns, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_sub(a1, b1);
+    };
+
+    issue(cur, false, 0, dma64_stage<0>());
+    issue(cur, false, BK, dma64_stage<1>());
+    ready();
+    load_sub(dma64_stage<0>(), 0, a0, b0);
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int kt = 0; kt < cur.nk; kt += 2) {
+            step(kt, dma64_stage<0>(), dma64_stage<1>());
+            step(kt + 1, dma64_stage<1>(), dma64_stage<0>());
+        }
+        int32_t trn[TM];
+        float gan[TM];
+        rows_of(nxt, trn, gan);
+        const int64_t mw = cur.t.tm * BM + wm * WTM, nw = cur.t.tn * BN + wn * WTN;
+        if constexpr (Kind >= KIND_BZ)
+            dma_epilogue_bwd<Kind, TM, TN>(p, acc, cur.t, mw, nw, lane, trow, gate,
+                                           cur.t.tn * WN + wn);
+        else if constexpr (GEN && Kind == KIND_FFN2)
+            dma_epilogue_general<TM, TN>(p, acc, cur.t, mw, nw, lane, trow, gate);
+        else
+            dma_epilogue<Kind, TM, TN>(p, acc, cur.t, mw, nw, lane, trow, gate);
+        if (!nxt.ok) break;
+        cur = nxt;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            trow[i] = trn[i];
+            gate[i] = gan[i];
+        }
+        lid += bper;
+        nxt = tile_at(lid + bper);
+        if (gather) {
+#pragma unroll
+            for (int j = 0; j < AI; ++j) aoff[j] = agn[j];
+            gather_offs(nxt, agn);
+        }
+    }
+    wait_vmcnt<0>();
+}
