@@ -13,7 +13,9 @@ before timing starts.
 Also reported: the auction solve time on the mixture workload (T=16384,
 E=128, D=1024, eps 1.0 -> 1e-4), the per-phase kernel times (HIP events
 recorded by the library on its stream), the roofline of the dominant kernel,
-and the CPU oracle timed on a bounded sample of the same work.
+the CPU oracle timed on a bounded sample of the same work, and, outside the
+step, the greedy-mode layer, the layer variants (convex mix, layer-norm
+blocks) and the backward pass on the same inputs.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2]
 """
@@ -49,10 +51,10 @@ FETCH_SCALE = 1.99995
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "e24a68db278f7feb79e8f56226b2ec2ee4f7c0266f83c5114b6a1e944e9e8062",
-             2397259.8, 1188216.9),
-    "ffn2": ("large_t64k_e128_d2048", "e24a68db278f7feb79e8f56226b2ec2ee4f7c0266f83c5114b6a1e944e9e8062",
-             2785302.6, 307358.4),
+    "ffn1": ("large_t64k_e128_d2048", "af9b9994a1710ab22d17f64e3aa06ba2688655061a9e290f410473ac871a2ac9",
+             2504070.4, 1184542.8),
+    "ffn2": ("large_t64k_e128_d2048", "af9b9994a1710ab22d17f64e3aa06ba2688655061a9e290f410473ac871a2ac9",
+             2857225.9, 362473.3),
 }
 
 
