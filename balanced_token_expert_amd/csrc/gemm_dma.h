@@ -295,6 +295,129 @@ BASE_DEV void act_grad(float x, int act, float& u, float& du) {
     }
 }
 
+// Staged stores of 32 rows (set i) of a wave's 64 x 128 output block (bf16):
+// out[j][q] holds row 32 i + lane % 32, columns 32 j + 8 q + 4 (lane / 32)
+// .. + 3. Written directly, each store instruction puts 16 bytes into each
+// of 32 rows, and HBM writes of outputs with long rows ran 1.7-2.4x the
+// bytes stored (lines left L2 partly written). Here the 32 rows go through
+// the wave's 4 KB of LDS one 64-column half at a time (16-byte chunk c of
+// row r at chunk c ^ (r % 8): one write instruction covers 32 rows in the
+// fewest bank cycles) and come back as whole 128-byte row pieces: each store
+// instruction writes 8 rows x 128 bytes, i.e. whole lines. The code has no
+// divergent branch: every lane takes part in every LDS exchange, and the
+// stores go through a buffer descriptor of the block (dst: its row 0,
+// column 0; rows ld elements apart; its size ends at the last row that
+// exists), so rows past the block and columns at or past ncols are dropped
+// by the descriptor's bound (an exec-masked LDS exchange here once had a
+// read moved inside the masked region by the compiler).
+__shared__ __attribute__((aligned(16))) char g_epi[8 * 4096];
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// val(j, q) gives out[j][q] (computed just before its half is staged, so
+// only half a row set of packed values is live at a time).
+template <int TN, class Val>
+BASE_DEV void store_rows_staged(char* lds, int lane, int i, Val&& val, buf_rsrc_t dst, int64_t ld,
+                                int64_t ncols) {
+    static_assert(TN == 4, "128 columns per wave");
+    const int lr = lane & 31;
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+        uint2 o[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[jj][q] = val(2 * jh + jj, q);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(uint2*)(lds + lr * 128 + (((4 * jj + q) ^ (lr & 7)) << 4) + 8 * (lane >> 5)) =
+                    o[jj][q];
+        // one wave owns the buffer and its LDS operations run in order
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int r = 8 * s + (lane >> 3), c = lane & 7;
+            const uint4 v = *(const uint4*)(lds + r * 128 + ((c ^ (r & 7)) << 4));
+            const int64_t col = 64 * jh + 8 * c;
+            const uint32_t off = col < ncols ? (uint32_t)(((32 * i + r) * ld + col) * 2) : kOob;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), dst, (int)off, 0, 0);
+        }
+    }
+}
+
+BASE_DEV uint2 pack_bf16x4(f32x4_t y) {
+    return __builtin_bit_cast(uint2, __builtin_convertvector(y, bf16x4_t));
+}
+
+// Descriptor of a wave's block of grouped rows of length ld: its row 0,
+// column 0, sized to end at its last existing row (the launcher keeps
+// 64 ld * 2 below 2^31).
+BASE_DEV buf_rsrc_t block_rsrc(const void* base, const Tile& tl, int64_t mw, int64_t nw,
+                               int64_t ld) {
+    const int64_t vr = tl.rows - mw < 0 ? 0 : (tl.rows - mw > 64 ? 64 : tl.rows - mw);
+    return make_rsrc((const uint16_t*)base + (tl.row0 + mw) * ld + nw, (uint32_t)(vr * ld * 2));
+}
+
+// Epilogue of the weight gradients: plain bf16 rows of dW, stored through
+// LDS in whole row pieces (store_rows_staged). Large workload: dW2 3.83 ->
+// 3.08 ms and dW1 3.51 -> 3.19 ms against direct 8-byte stores.
+template <int TM, int TN>
+BASE_DEV void dma_epilogue_bw(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                              int64_t mw, int64_t nw, int lane) {
+    char* lds = g_epi + (threadIdx.x >> 6) * 4096;
+    const buf_rsrc_t dst = block_rsrc(p.H, tl, mw, nw, p.N);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        store_rows_staged<TN>(
+            lds, lane, i,
+            [&](int j, int q) {
+                f32x4_t y;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[c] = acc[i][j][4 * q + c];
+                return pack_bf16x4(y);
+            },
+            dst, p.N, p.N - nw);
+}
+
+// The recomputation of Z: stores Z and g act(Z) with the same staged stores
+// (large workload: 3.17 -> 2.63 ms). V -> dZ keeps direct stores: holding
+// the Z values it reads beside the staged ones spilled registers and made it
+// a third slower.
+template <int TM, int TN>
+BASE_DEV void dma_epilogue_z(const GemmParams& p, f32x16_t (&acc)[TM][TN], const Tile& tl,
+                             int64_t mw, int64_t nw, int lane, const float (&gate)[TM]) {
+    char* lds = g_epi + (threadIdx.x >> 6) * 4096;
+    const buf_rsrc_t zr = block_rsrc(p.H, tl, mw, nw, p.N);
+    const buf_rsrc_t ur = block_rsrc(p.gu, tl, mw, nw, p.N);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const float g = gate[i];
+        store_rows_staged<TN>(
+            lds, lane, i,
+            [&](int j, int q) {
+                f32x4_t y;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[c] = acc[i][j][4 * q + c];
+                return pack_bf16x4(y);
+            },
+            zr, p.N, p.N - nw);
+        store_rows_staged<TN>(
+            lds, lane, i,
+            [&](int j, int q) {
+                f32x4_t gu;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float u, du;
+                    act_grad(acc[i][j][4 * q + c], p.act, u, du);
+                    gu[c] = g * u;
+                }
+                return pack_bf16x4(gu);
+            },
+            ur, p.N, p.N - nw);
+    }
+}
+
 // Epilogue of the backward products (accumulator layout as above; rows are
 // grouped rows, or output rows of dW for BW). wpart: this wave's column of
 // the BV partial sums.
@@ -917,7 +1040,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pers_kernel(GemmParams 
         float gan[TM];
         rows_of(nxt, trn, gan);
         const int64_t mw = cur.t.tm * BM + wm * WTM, nw = cur.t.tn * BN + wn * WTN;
-        if constexpr (Kind >= KIND_BZ)
+        if constexpr (Kind == KIND_BW)
+            dma_epilogue_bw<TM, TN>(p, acc, cur.t, mw, nw, lane);
+        else if constexpr (Kind == KIND_BZ)
+            dma_epilogue_z<TM, TN>(p, acc, cur.t, mw, nw, lane, gate);
+        else if constexpr (Kind >= KIND_BZ)
             dma_epilogue_bwd<Kind, TM, TN>(p, acc, cur.t, mw, nw, lane, trow, gate,
                                            cur.t.tn * WN + wn);
         else if constexpr (GEN && Kind == KIND_FFN2)
