@@ -47,14 +47,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99995
+FETCH_SCALE = 1.99994
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "af9b9994a1710ab22d17f64e3aa06ba2688655061a9e290f410473ac871a2ac9",
-             2504070.4, 1184542.8),
-    "ffn2": ("large_t64k_e128_d2048", "af9b9994a1710ab22d17f64e3aa06ba2688655061a9e290f410473ac871a2ac9",
-             2857225.9, 362473.3),
+    "ffn1": ("large_t64k_e128_d2048", "6215bae84037b15243817fc404ff29739007b83152358865214246d628a80510",
+             2504547.9, 1181926.9),
+    "ffn2": ("large_t64k_e128_d2048", "6215bae84037b15243817fc404ff29739007b83152358865214246d628a80510",
+             2848111.6, 362500.9),
 }
 
 
