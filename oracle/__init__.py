@@ -22,7 +22,9 @@ from .reference import (  # noqa: F401
     expert_ffn, gelu, sigmoid, dual_value, eps_cs_violation, objective,
     counts_of, layer_norm, expert_blocks, layer_forward_ex,
 )
-from .grad import act_grad, layer_backward  # noqa: F401
+from .grad import (  # noqa: F401
+    act_grad, layer_backward, layer_backward_ex, layer_norm_backward,
+)
 from .solvers import (  # noqa: F401
     auction, hungarian, cycle_cancel, min_cycle_gap, exact_assignment,
     OracleError,

@@ -20,15 +20,16 @@ and for an upstream gradient dy of y:
 
 Library primitives used as steps: numpy.matmul (fp64), scipy.special.erf.
 Parity: pinned by central finite differences of the pinned forward
-(``layer_forward_ex``), by torch.autograd in fp64 over torch.nn modules, and
-by structural cases (tests/test_oracle_grad.py).
+(``layer_forward_ex``, with and without layer-norm blocks), by torch.autograd
+in fp64 over torch.nn modules (Linear, LayerNorm), and by structural cases
+(tests/test_oracle_grad.py).
 """
 from __future__ import annotations
 
 import numpy as np
 from scipy.special import erf
 
-from .reference import _act, sigmoid
+from .reference import _act, layer_norm, sigmoid
 
 
 def act_grad(z, act: str) -> np.ndarray:
@@ -93,3 +94,94 @@ def layer_backward(h, w, W1, W2, a, act: str, dy, mix: str = "residual", s=None,
         dh[rows] = dz @ w1 + keep + dl[:, None] * w[e][None, :]
         dw[e] = dl @ x
     return dh, dw, dW1, dW2
+
+
+def layer_norm_backward(x, gamma, dy, eps: float = 1e-5):
+    """Gradients of y = (x - mean) / sqrt(var + eps) * gamma + beta over the
+    last axis (population variance) for an upstream dy: returns (dx, dgamma,
+    dbeta) with dgamma, dbeta summed over the rows. gamma None means ones.
+    With xh the normalised rows and g = dy * gamma:
+    dx = rstd (g - mean(g) - xh mean(g xh))."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    D = x.shape[-1]
+    mu = x.mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xh = (x - mu) * rstd
+    gm = np.ones(D) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    g = dy * gm
+    dx = rstd * (g - g.mean(axis=-1, keepdims=True) - xh * (g * xh).mean(axis=-1, keepdims=True))
+    return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
+
+
+def layer_backward_ex(h, w, W1, W2, a, act: str, dy, mix: str = "residual", sublayers: int = 0,
+                      gamma=None, beta=None, ln_eps: float = 1e-5, s=None, experts=None):
+    """Gradients of sum(dy * y) for ``layer_forward_ex`` with the assignment
+    fixed. sublayers = 0 is ``layer_backward``. With N >= 1 sec. 4.1 blocks
+    per expert (x_{n+1} = x_n + W2_n act(W1_n LN_n(x_n)), f = x_N), the
+    upstream of the blocks is dx_N = g dy, dg = dy . x_N (residual) or
+    dy . (x_N - x_0) (convex), and each block, last first, adds
+    LN_n'(W1_n^T dz_n) to the residual path, dz_n = (W2_n^T dx_{n+1}) act'.
+
+    W1, W2 indexed [n][e] (or callables (n, e)); gamma, beta N x E x D or
+    None. Returns (dh, dw, dW1, dW2, dgamma, dbeta): dh, dw as in
+    layer_backward; dW1, dW2 dicts (n, e) -> matrix; dgamma, dbeta dicts
+    (n, e) -> D-vector, the gradients of each layer norm's scale and shift
+    (at gamma = 1, beta = 0 when they are not given)."""
+    if sublayers == 0:
+        dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, act, dy, mix=mix, s=s,
+                                          experts=experts)
+        return dh, dw, dW1, dW2, {}, {}
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    a = np.asarray(a, dtype=np.int64)
+    T, D = h.shape
+    E = w.shape[0]
+    if mix not in ("residual", "convex"):
+        raise ValueError(f"unknown mix {mix!r}")
+    dh = np.full((T, D), np.nan)
+    dw = np.full((E, D), np.nan)
+    dW1, dW2, dgam, dbet = {}, {}, {}, {}
+    todo = range(E) if experts is None else experts
+    for e in todo:
+        rows = np.nonzero(a == e)[0]
+        x0 = h[rows]
+        d_y = dy[rows]
+        l = x0 @ w[e] if s is None else np.asarray(s, dtype=np.float64)[rows, e]
+        g = sigmoid(l)[:, None]
+        w1s = [np.asarray(W1(n, e) if callable(W1) else W1[n][e], dtype=np.float64)
+               for n in range(sublayers)]
+        w2s = [np.asarray(W2(n, e) if callable(W2) else W2[n][e], dtype=np.float64)
+               for n in range(sublayers)]
+        gs = [None if gamma is None else np.asarray(gamma[n][e], dtype=np.float64)
+              for n in range(sublayers)]
+        bs = [None if beta is None else np.asarray(beta[n][e], dtype=np.float64)
+              for n in range(sublayers)]
+        # forward, keeping each block's input
+        xs = [x0]
+        for n in range(sublayers):
+            yn = layer_norm(xs[-1], gs[n], bs[n], ln_eps)
+            xs.append(xs[-1] + _act(yn @ w1s[n].T, act) @ w2s[n].T)
+        xN = xs[-1]
+        if mix == "residual":
+            dg = (d_y * xN).sum(axis=1)
+            keep = d_y
+        else:
+            dg = (d_y * (xN - x0)).sum(axis=1)
+            keep = (1.0 - g) * d_y
+        dx = g * d_y
+        for n in reversed(range(sublayers)):
+            xn = xs[n]
+            yn = layer_norm(xn, gs[n], bs[n], ln_eps)
+            z = yn @ w1s[n].T
+            u = _act(z, act)
+            dW2[(n, e)] = dx.T @ u
+            dz = (dx @ w2s[n]) * act_grad(z, act)
+            dW1[(n, e)] = dz.T @ yn
+            dxn, dgam[(n, e)], dbet[(n, e)] = layer_norm_backward(xn, gs[n], dz @ w1s[n], ln_eps)
+            dx = dx + dxn
+        dl = (g[:, 0] * (1.0 - g[:, 0])) * dg
+        dh[rows] = dx + keep + dl[:, None] * w[e][None, :]
+        dw[e] = dl @ x0
+    return dh, dw, dW1, dW2, dgam, dbet

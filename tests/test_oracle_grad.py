@@ -116,3 +116,104 @@ def test_zero_upstream_gradient_and_empty_expert():
     assert all(not np.any(dW1[e]) and not np.any(dW2[e]) for e in range(4))
     dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, "relu", dy)
     assert not np.any(dw[3]) and not np.any(dW1[3]) and not np.any(dW2[3])
+
+
+# ---------------------------------------------------------------- sec. 4.1 blocks
+
+def test_layer_norm_backward_matches_torch():
+    x = RNG.standard_normal((13, 24)) * 2.0 + 1.0
+    g, b = 1.0 + 0.2 * RNG.standard_normal(24), 0.2 * RNG.standard_normal(24)
+    dy = RNG.standard_normal((13, 24))
+    tx, tg, tb = (torch.tensor(v, requires_grad=True) for v in (x, g, b))
+    y = torch.nn.functional.layer_norm(tx, (24,), tg, tb, eps=1e-5)
+    (y * torch.from_numpy(dy)).sum().backward()
+    dx, dg, db = oracle.layer_norm_backward(x, g, dy, 1e-5)
+    assert np.allclose(dx, tx.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dg, tg.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(db, tb.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def _block_inputs(T=10, E=2, D=6, F=8, N=2):
+    h = RNG.standard_normal((T, D))
+    w = RNG.standard_normal((E, D)) * 0.7
+    W1 = RNG.standard_normal((N, E, F, D)) * D ** -0.5
+    W2 = RNG.standard_normal((N, E, D, F)) * F ** -0.5
+    gam = 1.0 + 0.2 * RNG.standard_normal((N, E, D))
+    bet = 0.2 * RNG.standard_normal((N, E, D))
+    a = RNG.permutation(np.repeat(np.arange(E), T // E))
+    dy = RNG.standard_normal((T, D))
+    return h, w, W1, W2, gam, bet, a, dy
+
+
+@pytest.mark.parametrize("mix", ["residual", "convex"])
+@pytest.mark.parametrize("act,N", [("relu", 1), ("gelu", 2)])
+def test_block_gradients_match_finite_differences(mix, act, N):
+    h, w, W1, W2, gam, bet, a, dy = _block_inputs(N=N)
+    E = w.shape[0]
+
+    def loss():
+        y = oracle.layer_forward_ex(h, w, W1, W2, a, act, mix=mix, sublayers=N, gamma=gam,
+                                    beta=bet, ln_eps=1e-5)
+        return float((dy * y).sum())
+
+    dh, dw, dW1, dW2, dga, dbe = oracle.layer_backward_ex(h, w, W1, W2, a, act, dy, mix=mix,
+                                                          sublayers=N, gamma=gam, beta=bet)
+    got = {"h": dh, "w": dw,
+           "W1": np.stack([np.stack([dW1[(n, e)] for e in range(E)]) for n in range(N)]),
+           "W2": np.stack([np.stack([dW2[(n, e)] for e in range(E)]) for n in range(N)]),
+           "gam": np.stack([np.stack([dga[(n, e)] for e in range(E)]) for n in range(N)]),
+           "bet": np.stack([np.stack([dbe[(n, e)] for e in range(E)]) for n in range(N)])}
+    params = {"h": h, "w": w, "W1": W1, "W2": W2, "gam": gam, "bet": bet}
+    step = 1e-6
+    for name, arr in params.items():
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + step
+            lp = loss()
+            arr[idx] = keep - step
+            lm = loss()
+            arr[idx] = keep
+            num[idx] = (lp - lm) / (2 * step)
+        err = np.abs(got[name] - num).max()
+        assert err < 2e-7 * max(1.0, np.abs(num).max()), (name, err)
+
+
+@pytest.mark.parametrize("mix", ["residual", "convex"])
+def test_block_gradients_match_torch_modules(mix):
+    """Two blocks built from torch.nn.LayerNorm / Linear / GELU per expert."""
+    T, E, D, F, N = 32, 2, 12, 20, 2
+    h, w, W1, W2, gam, bet, a, dy = _block_inputs(T, E, D, F, N)
+    th, tw = torch.tensor(h, requires_grad=True), torch.tensor(w, requires_grad=True)
+    mods = {}
+    for n in range(N):
+        for e in range(E):
+            ln = torch.nn.LayerNorm(D, eps=1e-5, dtype=torch.float64)
+            up = torch.nn.Linear(D, F, bias=False, dtype=torch.float64)
+            down = torch.nn.Linear(F, D, bias=False, dtype=torch.float64)
+            with torch.no_grad():
+                ln.weight.copy_(torch.from_numpy(gam[n, e]))
+                ln.bias.copy_(torch.from_numpy(bet[n, e]))
+                up.weight.copy_(torch.from_numpy(W1[n, e]))
+                down.weight.copy_(torch.from_numpy(W2[n, e]))
+            mods[(n, e)] = (ln, up, down)
+    y = torch.zeros(T, D, dtype=torch.float64)
+    for e in range(E):
+        rows = torch.from_numpy(np.nonzero(a == e)[0])
+        x0 = th[rows]
+        g = torch.sigmoid(x0 @ tw[e])[:, None]
+        x = x0
+        for n in range(N):
+            ln, up, down = mods[(n, e)]
+            x = x + down(torch.nn.functional.gelu(up(ln(x))))
+        y = y.index_put((rows,), g * x + (x0 if mix == "residual" else (1 - g) * x0))
+    (y * torch.from_numpy(dy)).sum().backward()
+    dh, dw, dW1, dW2, dga, dbe = oracle.layer_backward_ex(h, w, W1, W2, a, "gelu", dy, mix=mix,
+                                                          sublayers=N, gamma=gam, beta=bet)
+    assert np.allclose(dh, th.grad.numpy(), rtol=0, atol=1e-11)
+    assert np.allclose(dw, tw.grad.numpy(), rtol=0, atol=1e-11)
+    for (n, e), (ln, up, down) in mods.items():
+        assert np.allclose(dW1[(n, e)], up.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dW2[(n, e)], down.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dga[(n, e)], ln.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dbe[(n, e)], ln.bias.grad.numpy(), rtol=0, atol=1e-11)
