@@ -23,7 +23,7 @@ from .reference import (  # noqa: F401
     counts_of, layer_norm, expert_blocks, layer_forward_ex,
 )
 from .grad import (  # noqa: F401
-    act_grad, layer_backward, layer_backward_ex, layer_norm_backward,
+    act_grad, layer_backward, layer_backward_ex, layer_norm_backward, stored,
 )
 from .solvers import (  # noqa: F401
     auction, hungarian, cycle_cancel, min_cycle_gap, exact_assignment,

@@ -114,8 +114,27 @@ def layer_norm_backward(x, gamma, dy, eps: float = 1e-5):
     return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
 
 
+def stored(x, store=None) -> np.ndarray:
+    """x as a kernel that computes in fp32 and keeps the result in ``store``
+    holds it: None keeps fp64; "f32" rounds to the nearest fp32; "bf16"
+    rounds to the nearest fp32 and then to the nearest bfloat16 (8 bits of
+    significand, ties to even; overflow goes to infinity)."""
+    x = np.asarray(x, dtype=np.float64)
+    if store is None:
+        return x
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    if store == "f32":
+        return x32.astype(np.float64)
+    if store != "bf16":
+        raise ValueError(f"unknown storage type {store!r}")
+    b = x32.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def layer_backward_ex(h, w, W1, W2, a, act: str, dy, mix: str = "residual", sublayers: int = 0,
-                      gamma=None, beta=None, ln_eps: float = 1e-5, s=None, experts=None):
+                      gamma=None, beta=None, ln_eps: float = 1e-5, s=None, experts=None,
+                      store=None):
     """Gradients of sum(dy * y) for ``layer_forward_ex`` with the assignment
     fixed. sublayers = 0 is ``layer_backward``. With N >= 1 sec. 4.1 blocks
     per expert (x_{n+1} = x_n + W2_n act(W1_n LN_n(x_n)), f = x_N), the
@@ -127,7 +146,15 @@ def layer_backward_ex(h, w, W1, W2, a, act: str, dy, mix: str = "residual", subl
     None. Returns (dh, dw, dW1, dW2, dgamma, dbeta): dh, dw as in
     layer_backward; dW1, dW2 dicts (n, e) -> matrix; dgamma, dbeta dicts
     (n, e) -> D-vector, the gradients of each layer norm's scale and shift
-    (at gamma = 1, beta = 0 when they are not given)."""
+    (at gamma = 1, beta = 0 when they are not given).
+
+    ``store`` ("bf16", "f32" or None): the blocks' forward state -- each
+    block's input x_n, its layer-norm output and act(z) -- is taken at its
+    value after a store in that type (``stored``), the rest in fp64. ReLU's
+    derivative is a 0/1 decision on the sign of z; with the state kept in
+    bf16, z moves by bf16 rounding and decisions near z = 0 follow the
+    precision the state was kept in, so a comparison with a bf16 kernel takes
+    them from the same rounded state."""
     if sublayers == 0:
         dh, dw, dW1, dW2 = layer_backward(h, w, W1, W2, a, act, dy, mix=mix, s=s,
                                           experts=experts)
@@ -159,10 +186,11 @@ def layer_backward_ex(h, w, W1, W2, a, act: str, dy, mix: str = "residual", subl
         bs = [None if beta is None else np.asarray(beta[n][e], dtype=np.float64)
               for n in range(sublayers)]
         # forward, keeping each block's input
-        xs = [x0]
+        xs = [stored(x0, store)]
         for n in range(sublayers):
-            yn = layer_norm(xs[-1], gs[n], bs[n], ln_eps)
-            xs.append(xs[-1] + _act(yn @ w1s[n].T, act) @ w2s[n].T)
+            yn = stored(layer_norm(xs[-1], gs[n], bs[n], ln_eps), store)
+            un = stored(_act(yn @ w1s[n].T, act), store)
+            xs.append(stored(xs[-1] + un @ w2s[n].T, store))
         xN = xs[-1]
         if mix == "residual":
             dg = (d_y * xN).sum(axis=1)
@@ -173,9 +201,9 @@ def layer_backward_ex(h, w, W1, W2, a, act: str, dy, mix: str = "residual", subl
         dx = g * d_y
         for n in reversed(range(sublayers)):
             xn = xs[n]
-            yn = layer_norm(xn, gs[n], bs[n], ln_eps)
+            yn = stored(layer_norm(xn, gs[n], bs[n], ln_eps), store)
             z = yn @ w1s[n].T
-            u = _act(z, act)
+            u = stored(_act(z, act), store)
             dW2[(n, e)] = dx.T @ u
             dz = (dx @ w2s[n]) * act_grad(z, act)
             dW1[(n, e)] = dz.T @ yn

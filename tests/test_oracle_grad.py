@@ -217,3 +217,76 @@ def test_block_gradients_match_torch_modules(mix):
         assert np.allclose(dW2[(n, e)], down.weight.grad.numpy(), rtol=0, atol=1e-11)
         assert np.allclose(dga[(n, e)], ln.weight.grad.numpy(), rtol=0, atol=1e-11)
         assert np.allclose(dbe[(n, e)], ln.bias.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_stored_matches_torch_casts():
+    """``stored`` against torch's own fp32 and bfloat16 conversions: random
+    magnitudes over many binades, exact ties of both parities, values just
+    off a tie, tiny and huge values (overflow to infinity)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-60, 60, 20000))
+    ties = (np.arange(1, 2001, dtype=np.float64) * 2 + 1) * 2.0 ** -8  # odd multiples of 2^-8
+    near = np.concatenate([ties * (1 + 2.0 ** -20), ties * (1 - 2.0 ** -20)])
+    special = np.array([0.0, -0.0, 1e-40, -1e-40, 3.4e38, -3.4e38, 65504.0, 1.0 + 2.0 ** -8])
+    x = np.concatenate([x, ties, -ties, near, special])
+    t = torch.from_numpy(x)
+    want_f32 = t.to(torch.float32).to(torch.float64).numpy()
+    want_bf16 = t.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.stored(x, "f32"), want_f32)
+    assert np.array_equal(oracle.stored(x, "bf16"), want_bf16)
+    assert oracle.stored(x) is not None and np.array_equal(oracle.stored(x), x)
+
+
+@pytest.mark.parametrize("mix", ["residual", "convex"])
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_stored_block_gradients_match_straight_through_torch(mix, act):
+    """store="bf16": torch.nn modules with each block's input, layer-norm
+    output and activation replaced in the forward by its bfloat16 value
+    (torch's cast) while the gradient passes through unchanged -- the
+    gradient of the blocks evaluated at the rounded state."""
+    T, E, D, F, N = 32, 2, 12, 20, 2
+    h, w, W1, W2, gam, bet, a, dy = _block_inputs(T, E, D, F, N)
+
+    def st(x):
+        r = x.detach().to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        return x + (r - x).detach()
+
+    fn = torch.nn.functional.relu if act == "relu" else torch.nn.functional.gelu
+    th, tw = torch.tensor(h, requires_grad=True), torch.tensor(w, requires_grad=True)
+    mods = {}
+    for n in range(N):
+        for e in range(E):
+            ln = torch.nn.LayerNorm(D, eps=1e-5, dtype=torch.float64)
+            up = torch.nn.Linear(D, F, bias=False, dtype=torch.float64)
+            down = torch.nn.Linear(F, D, bias=False, dtype=torch.float64)
+            with torch.no_grad():
+                ln.weight.copy_(torch.from_numpy(gam[n, e]))
+                ln.bias.copy_(torch.from_numpy(bet[n, e]))
+                up.weight.copy_(torch.from_numpy(W1[n, e]))
+                down.weight.copy_(torch.from_numpy(W2[n, e]))
+            mods[(n, e)] = (ln, up, down)
+    y = torch.zeros(T, D, dtype=torch.float64)
+    for e in range(E):
+        rows = torch.from_numpy(np.nonzero(a == e)[0])
+        x0 = th[rows]
+        g = torch.sigmoid(x0 @ tw[e])[:, None]
+        x = st(x0)
+        for n in range(N):
+            ln, up, down = mods[(n, e)]
+            x = st(x + down(st(fn(up(st(ln(x)))))))
+        y = y.index_put((rows,), g * x + (x0 if mix == "residual" else (1 - g) * x0))
+    (y * torch.from_numpy(dy)).sum().backward()
+    dh, dw, dW1, dW2, dga, dbe = oracle.layer_backward_ex(h, w, W1, W2, a, act, dy, mix=mix,
+                                                          sublayers=N, gamma=gam, beta=bet,
+                                                          store="bf16")
+    assert np.allclose(dh, th.grad.numpy(), rtol=0, atol=1e-11)
+    assert np.allclose(dw, tw.grad.numpy(), rtol=0, atol=1e-11)
+    for (n, e), (ln, up, down) in mods.items():
+        assert np.allclose(dW1[(n, e)], up.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dW2[(n, e)], down.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dga[(n, e)], ln.weight.grad.numpy(), rtol=0, atol=1e-11)
+        assert np.allclose(dbe[(n, e)], ln.bias.grad.numpy(), rtol=0, atol=1e-11)
+    # and the rounding does move the result (the pin is not vacuous)
+    dh0 = oracle.layer_backward_ex(h, w, W1, W2, a, act, dy, mix=mix, sublayers=N, gamma=gam,
+                                   beta=bet)[0]
+    assert np.abs(dh0 - dh).max() > 1e-6
