@@ -28,7 +28,8 @@ BASE_OP_LAYER_BWD = 5
 BASE_MIX_RESIDUAL, BASE_MIX_CONVEX = 0, 1
 EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
             "base_assign_auction", "base_route_greedy", "base_layer_forward",
-            "base_layer_forward_ex", "base_layer_backward", "base_set_phase_events")
+            "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
+            "base_workspace_bytes_ex", "base_set_phase_events")
 STATS_BYTES = 8 + 16 * 8 * 2
 
 
@@ -77,9 +78,15 @@ def load(path: str = LIB_PATH):
                                           P, ctypes.c_size_t, P]
     lib.base_layer_backward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, P, P, P, P, P,
                                         P, P, P, ctypes.POINTER(LayerOpts), P, ctypes.c_size_t, P]
+    lib.base_layer_backward_ex.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, i32, P, P, P, P,
+                                           P, P, P, P, P, P, ctypes.POINTER(LayerOpts), P,
+                                           ctypes.c_size_t, P]
+    lib.base_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i64, i32, i32]
+    lib.base_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.base_set_phase_events.argtypes = [P, i32]
     for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
-              "base_layer_forward_ex", "base_layer_backward", "base_set_phase_events"):
+              "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
+              "base_set_phase_events"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -288,6 +295,49 @@ def base_layer_backward(h, w, W1, W2, act: int, assign, scores, dy, mix: int = 0
                                     _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "base_layer_backward")
     return {"dh": dh, "dw": dw, "dW1": dW1, "dW2": dW2, "stats": stats}
+
+
+def base_workspace_bytes_ex(op: int, T: int, E: int, D: int, F: int, dtype: int,
+                            sublayers: int) -> int:
+    return int(load().base_workspace_bytes_ex(op, T, E, D, F, dtype, sublayers))
+
+
+def base_layer_backward_ex(h, w, W1, W2, act: int, assign, scores, dy, mix: int = 0,
+                           sublayers: int = 0, ln_gamma=None, ln_beta=None, ln_eps: float = 1e-5,
+                           dh=None, dw=None, dW1=None, dW2=None, dgamma=None, dbeta=None,
+                           want_ln_grads=True, stats=None, ws=None, stream=None):
+    """base_layer_backward for the layer variants: W1 / W2 as for
+    base_layer_forward_ex; returns dict(dh, dw, dW1, dW2, dgamma, dbeta,
+    stats) (dgamma / dbeta N x E x D fp32 when sublayers >= 1)."""
+    _dev(h, w, W1, W2, assign, scores, dy, dh, dw, dW1, dW2, ln_gamma, ln_beta, dgamma, dbeta)
+    T, D = h.shape
+    E = w.shape[0]
+    F = W1.shape[-2]
+    dev = h.device
+    dt = _dt(h)
+    dh = torch.empty_like(h) if dh is None else dh
+    dw = torch.empty_like(w) if dw is None else dw
+    dW1 = torch.empty_like(W1) if dW1 is None else dW1
+    dW2 = torch.empty_like(W2) if dW2 is None else dW2
+    if sublayers >= 1 and want_ln_grads:
+        shape = (sublayers, E, D)
+        dgamma = torch.empty(shape, dtype=torch.float32, device=dev) if dgamma is None else dgamma
+        dbeta = torch.empty(shape, dtype=torch.float32, device=dev) if dbeta is None else dbeta
+    stats = new_stats(dev) if stats is None else stats
+    if ws is None:
+        n = base_workspace_bytes_ex(BASE_OP_LAYER_BWD, T, E, D, F, dt, sublayers)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    opts = LayerOpts(int(mix), int(sublayers), float(ln_eps),
+                     None if ln_gamma is None else ln_gamma.data_ptr(),
+                     None if ln_beta is None else ln_beta.data_ptr())
+    rc = load().base_layer_backward_ex(_ptr(h), _ptr(w), _ptr(W1), _ptr(W2), T, E, D, F, dt, act,
+                                       _ptr(assign), _ptr(scores), _ptr(dy), _ptr(dh), _ptr(dw),
+                                       _ptr(dW1), _ptr(dW2), _ptr(dgamma), _ptr(dbeta),
+                                       _ptr(stats), ctypes.byref(opts), _ptr(ws), ws.numel(),
+                                       _stream(stream))
+    _check(rc, "base_layer_backward_ex")
+    return {"dh": dh, "dw": dw, "dW1": dW1, "dW2": dW2, "dgamma": dgamma, "dbeta": dbeta,
+            "stats": stats}
 
 
 def base_set_phase_events(events, n: int):

@@ -23,10 +23,12 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
     size_t scan = 0, stats = 0, prices = 0, scores = 0, perm = 0, offsets = 0, hidden = 0,
            auction = 0, permws = 0, assign = 0, gblk = 0, xbuf = 0, ybuf = 0, xg = 0, dyg = 0,
-           zbuf = 0, gubuf = 0, dzbuf = 0, part = 0, dl = 0, total = 0;
+           zbuf = 0, gubuf = 0, dzbuf = 0, part = 0, dl = 0, xs = 0, dxa = 0, dxo = 0, dyn = 0,
+           lnst = 0, total = 0;
 };
 
-Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
+// (op BASE_OP_LAYER_BWD with nsub >= 1: the backward of layer-norm blocks)
+Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt, int nsub = 0) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t& slot, size_t bytes) {
@@ -52,6 +54,14 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt) {
         take(L.dzbuf, (size_t)T * F * b); // dZ
         take(L.part, (size_t)T * bwd_nparts(F, dt == BASE_BF16) * 4);
         take(L.dl, (size_t)T * 4);        // gate-logit gradients
+        if (nsub >= 1) {
+            take(L.xs, (size_t)(nsub + 1) * T * D * b);  // each block's input, then x_N
+            take(L.dxa, (size_t)T * D * 4);   // upstream gradient of a block, fp32
+            take(L.dxo, (size_t)T * D * b);   // the same as an operand
+            take(L.dyn, (size_t)T * D * b);   // gradient of a block's normalised rows
+            take(L.lnst, (size_t)T * 8);      // per-row mean and rstd
+            take(L.ybuf, (size_t)T * D * b);  // normalised rows
+        }
         L.total = off;
         return L;
     }
@@ -215,6 +225,144 @@ static int layer_forward(const void* h, const void* w, const void* W1, const voi
     return hip_rc(e);
 }
 
+// Shared body of base_layer_backward (plain experts) and
+// base_layer_backward_ex (also experts of layer-norm blocks).
+static int layer_backward(const void* h, const void* w, const void* W1, const void* W2, int64_t T,
+                          int64_t E, int64_t D, int64_t F, int dt, int act, const int32_t* assign,
+                          const float* scores, const void* dy, void* dh, void* dw, void* dW1,
+                          void* dW2, float* dgamma, float* dbeta, base_auction_stats* stats,
+                          const base_layer_opts* opts, void* ws, size_t ws_bytes,
+                          base_stream_t stream) {
+    if (!h || !w || !W1 || !W2 || !assign || !scores || !dy || !dh || !dw || !dW1 || !dW2)
+        return BASE_ERR_INVALID_ARG;
+    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
+    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
+    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
+    const int mix = opts ? opts->mix : BASE_MIX_RESIDUAL;
+    const int nsub = opts ? opts->sublayers : 0;
+    if (mix != BASE_MIX_RESIDUAL && mix != BASE_MIX_CONVEX) return BASE_ERR_INVALID_ARG;
+    if (nsub < 0 || nsub > kMaxSublayers) return BASE_ERR_INVALID_ARG;
+    if (nsub > 0 && !(opts->ln_eps >= 0)) return BASE_ERR_INVALID_ARG;
+    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
+    // the backward products address a tile's operands with 32-bit offsets
+    if (D > kMaxBwdWidth || F > kMaxBwdWidth) return BASE_ERR_UNSUPPORTED;
+    if (dt == BASE_BF16 &&
+        (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) || misaligned(W1) ||
+         misaligned(W2) || misaligned(dy) || misaligned(dh) || misaligned(dW1) || misaligned(dW2)))
+        return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(BASE_OP_LAYER_BWD, T, E, D, F, dt, nsub);
+    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
+    int32_t* pm = (int32_t*)(W + L.perm);
+    int32_t* offs = (int32_t*)(W + L.offsets);
+    int32_t* gblk = (int32_t*)(W + L.gblk);
+    void* Xg = W + L.xg;
+    void* dYg = W + L.dyg;
+    void* Z = W + L.zbuf;
+    void* gU = W + L.gubuf;
+    void* dZ = W + L.dzbuf;
+    float* part = (float*)(W + L.part);
+    float* dl = (float*)(W + L.dl);
+    const int64_t np = bwd_nparts(F, dt == BASE_BF16);
+    const size_t b = dt == BASE_BF16 ? 2 : 4;
+
+    mark(0, st);
+    // expert groups of the given assignment (any sizes; ids outside [0, E)
+    // are reported through stats->status)
+    hipError_t e = launch_stats_reset(sd, st);
+    if (e == hipSuccess)
+        e = launch_perm(assign, T, E, pm, offs, nullptr, 0, &sd->status, W + L.permws, st);
+    if (nsub == 0) {
+        if (e == hipSuccess) e = launch_gather2(h, dy, pm, Xg, dYg, T, D, dt, st);
+        if (e == hipSuccess)
+            e = launch_bwd_z(Xg, W1, pm, scores, Z, gU, T, E, D, F, dt, act, offs, gblk, 0, st);
+        mark(1, st);
+        if (e == hipSuccess)
+            e = launch_bwd_v(dYg, W2, pm, scores, Z, dZ, part, T, E, D, F, dt, act, offs, gblk, 0,
+                             st);
+        if (e == hipSuccess)
+            e = launch_gate_grad(part, np, Xg, dYg, pm, offs, scores, mix, dl, T, E, D, dt, st);
+        mark(2, st);
+        if (e == hipSuccess) e = launch_bwd_w(dYg, gU, D, F, E, offs, dW2, dt, st);
+        mark(3, st);
+        if (e == hipSuccess) e = launch_bwd_w(dZ, Xg, F, D, E, offs, dW1, dt, st);
+        mark(4, st);
+        if (e == hipSuccess)
+            e = launch_bwd_x(dZ, W1, pm, scores, dYg, w, dl, mix, dh, T, E, D, F, dt, offs, gblk,
+                             nullptr, st);
+        if (e == hipSuccess) e = launch_centroid_grad(dl, Xg, offs, dw, E, D, dt, st);
+        mark(5, st);
+        return hip_rc(e);
+    }
+
+    // experts of nsub layer-norm blocks (sec. 4.1): run the blocks forward on
+    // the grouped rows, keeping every block's input x_n (x_0 = h's rows), then
+    // take the blocks back, last first, on the upstream g dy
+    char* xs = W + L.xs;
+    auto X = [&](int n) -> void* { return xs + (size_t)n * T * D * b; };
+    float* dXa = (float*)(W + L.dxa);
+    void* dXo = W + L.dxo;
+    void* dYn = W + L.dyn;
+    float* lnst = (float*)(W + L.lnst);
+    void* Y = W + L.ybuf;
+    const int64_t k = T / E;  // unused with ragged groups, which all launches here use
+    auto ga = [&](int n) -> const float* {
+        return opts->ln_gamma ? opts->ln_gamma + (size_t)n * E * D : nullptr;
+    };
+    auto be = [&](int n) -> const float* {
+        return opts->ln_beta ? opts->ln_beta + (size_t)n * E * D : nullptr;
+    };
+    auto w1 = [&](int n) { return (const char*)W1 + (size_t)n * E * F * D * b; };
+    auto w2 = [&](int n) { return (const char*)W2 + (size_t)n * E * D * F * b; };
+    if (e == hipSuccess) e = launch_gather2(h, dy, pm, X(0), dYg, T, D, dt, st);
+    for (int n = 0; n < nsub && e == hipSuccess; ++n) {
+        e = launch_layernorm(X(n), 0, pm, assign, ga(n), be(n), opts->ln_eps, Y, T, E, D, dt, st);
+        if (e == hipSuccess)
+            e = launch_ffn1(Y, nullptr, w1(n), gU, E, k, D, F, dt, act, offs, gblk, T, st);
+        const Ffn2Epi epi = {1, 2, 2, X(n), X(n + 1)};  // x_{n+1} = x_n + C, grouped
+        if (e == hipSuccess)
+            e = launch_ffn2_ex(gU, pm, w2(n), scores, h, nullptr, E, k, D, F, dt, offs, gblk, T,
+                               epi, st);
+    }
+    mark(1, st);
+    if (e == hipSuccess)
+        e = launch_block_gate(X(0), X(nsub), dYg, pm, offs, scores, mix, dXa, dXo, dl, T, E, D, dt,
+                              st);
+    mark(2, st);
+    for (int n = nsub - 1; n >= 0 && e == hipSuccess; --n) {
+        e = launch_layernorm(X(n), 0, pm, assign, ga(n), be(n), opts->ln_eps, Y, T, E, D, dt, st);
+        if (e == hipSuccess)  // Z and act(Z) (gate 1: dX already holds g)
+            e = launch_bwd_z(Y, w1(n), pm, scores, Z, gU, T, E, D, F, dt, act, offs, gblk, 1, st);
+        if (e == hipSuccess)
+            e = launch_bwd_v(dXo, w2(n), pm, scores, Z, dZ, part, T, E, D, F, dt, act, offs, gblk,
+                             1, st);
+        if (e == hipSuccess)
+            e = launch_bwd_w(dXo, gU, D, F, E, offs, (char*)dW2 + (size_t)n * E * D * F * b, dt,
+                             st);
+        if (e == hipSuccess)
+            e = launch_bwd_w(dZ, Y, F, D, E, offs, (char*)dW1 + (size_t)n * E * F * D * b, dt, st);
+        if (e == hipSuccess)
+            e = launch_bwd_x(dZ, w1(n), pm, scores, dYg, w, dl, mix, dh, T, E, D, F, dt, offs,
+                             gblk, dYn, st);
+        if (e == hipSuccess)
+            e = launch_ln_backward(X(n), dYn, ga(n), offs, opts->ln_eps, dXa, dXo, lnst, T, E, D,
+                                   dt, st);
+        if (e == hipSuccess)
+            e = launch_ln_param_grad(X(n), dYn, lnst, offs,
+                                     dgamma ? dgamma + (size_t)n * E * D : nullptr,
+                                     dbeta ? dbeta + (size_t)n * E * D : nullptr, E, D, dt, st);
+    }
+    mark(3, st);
+    mark(4, st);
+    if (e == hipSuccess)
+        e = launch_finish_dh(dXa, dYg, dl, w, pm, offs, scores, mix, dh, T, E, D, dt, st);
+    if (e == hipSuccess) e = launch_centroid_grad(dl, X(0), offs, dw, E, D, dt, st);
+    mark(5, st);
+    return hip_rc(e);
+}
+
 extern "C" {
 
 const char* base_strerror(int code) {
@@ -326,62 +474,27 @@ int base_layer_backward(const void* h, const void* w, const void* W1, const void
                         const float* scores, const void* dy, void* dh, void* dw, void* dW1,
                         void* dW2, base_auction_stats* stats, const base_layer_opts* opts,
                         void* ws, size_t ws_bytes, base_stream_t stream) {
-    if (!h || !w || !W1 || !W2 || !assign || !scores || !dy || !dh || !dw || !dW1 || !dW2)
-        return BASE_ERR_INVALID_ARG;
-    if (T <= 0 || E <= 0 || D <= 0 || F <= 0 || E > T) return BASE_ERR_INVALID_ARG;
-    if (dt != BASE_F32 && dt != BASE_BF16) return BASE_ERR_INVALID_ARG;
-    if (act != BASE_ACT_RELU && act != BASE_ACT_GELU) return BASE_ERR_INVALID_ARG;
-    const int mix = opts ? opts->mix : BASE_MIX_RESIDUAL;
-    if (mix != BASE_MIX_RESIDUAL && mix != BASE_MIX_CONVEX) return BASE_ERR_INVALID_ARG;
     if (opts && opts->sublayers != 0) return BASE_ERR_UNSUPPORTED;
-    if (T > kMaxT || E > kMaxE) return BASE_ERR_UNSUPPORTED;
-    // the backward products address a tile's operands with 32-bit offsets
-    if (D > kMaxBwdWidth || F > kMaxBwdWidth) return BASE_ERR_UNSUPPORTED;
-    if (dt == BASE_BF16 &&
-        (D % 8 != 0 || F % 8 != 0 || misaligned(h) || misaligned(w) || misaligned(W1) ||
-         misaligned(W2) || misaligned(dy) || misaligned(dh) || misaligned(dW1) || misaligned(dW2)))
-        return BASE_ERR_UNSUPPORTED;
-    const Layout L = layout(BASE_OP_LAYER_BWD, T, E, D, F, dt);
-    if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    char* W = (char*)ws;
-    AucStatsDev* sd = stats ? (AucStatsDev*)stats : (AucStatsDev*)(W + L.stats);
-    int32_t* pm = (int32_t*)(W + L.perm);
-    int32_t* offs = (int32_t*)(W + L.offsets);
-    int32_t* gblk = (int32_t*)(W + L.gblk);
-    void* Xg = W + L.xg;
-    void* dYg = W + L.dyg;
-    void* Z = W + L.zbuf;
-    void* gU = W + L.gubuf;
-    void* dZ = W + L.dzbuf;
-    float* part = (float*)(W + L.part);
-    float* dl = (float*)(W + L.dl);
-    const int64_t np = bwd_nparts(F, dt == BASE_BF16);
+    return layer_backward(h, w, W1, W2, T, E, D, F, dt, act, assign, scores, dy, dh, dw, dW1, dW2,
+                          nullptr, nullptr, stats, opts, ws, ws_bytes, stream);
+}
 
-    mark(0, st);
-    // expert groups of the given assignment (any sizes; ids outside [0, E)
-    // are reported through stats->status)
-    hipError_t e = launch_stats_reset(sd, st);
-    if (e == hipSuccess)
-        e = launch_perm(assign, T, E, pm, offs, nullptr, 0, &sd->status, W + L.permws, st);
-    if (e == hipSuccess) e = launch_gather2(h, dy, pm, Xg, dYg, T, D, dt, st);
-    if (e == hipSuccess)
-        e = launch_bwd_z(Xg, W1, pm, scores, Z, gU, T, E, D, F, dt, act, offs, gblk, st);
-    mark(1, st);
-    if (e == hipSuccess)
-        e = launch_bwd_v(dYg, W2, pm, scores, Z, dZ, part, T, E, D, F, dt, act, offs, gblk, st);
-    if (e == hipSuccess)
-        e = launch_gate_grad(part, np, Xg, dYg, pm, offs, scores, mix, dl, T, E, D, dt, st);
-    mark(2, st);
-    if (e == hipSuccess) e = launch_bwd_w(dYg, gU, D, F, E, offs, dW2, dt, st);
-    mark(3, st);
-    if (e == hipSuccess) e = launch_bwd_w(dZ, Xg, F, D, E, offs, dW1, dt, st);
-    mark(4, st);
-    if (e == hipSuccess)
-        e = launch_bwd_x(dZ, W1, pm, scores, dYg, w, dl, mix, dh, T, E, D, F, dt, offs, gblk, st);
-    if (e == hipSuccess) e = launch_centroid_grad(dl, Xg, offs, dw, E, D, dt, st);
-    mark(5, st);
-    return hip_rc(e);
+int base_layer_backward_ex(const void* h, const void* w, const void* W1, const void* W2,
+                           int64_t T, int64_t E, int64_t D, int64_t F, int dt, int act,
+                           const int32_t* assign, const float* scores, const void* dy, void* dh,
+                           void* dw, void* dW1, void* dW2, float* dgamma, float* dbeta,
+                           base_auction_stats* stats, const base_layer_opts* opts, void* ws,
+                           size_t ws_bytes, base_stream_t stream) {
+    return layer_backward(h, w, W1, W2, T, E, D, F, dt, act, assign, scores, dy, dh, dw, dW1, dW2,
+                          dgamma, dbeta, stats, opts, ws, ws_bytes, stream);
+}
+
+size_t base_workspace_bytes_ex(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dtype,
+                               int sublayers) {
+    if (sublayers < 0 || sublayers > kMaxSublayers) return 0;
+    if (op != BASE_OP_LAYER_BWD || sublayers == 0) return base_workspace_bytes(op, T, E, D, F, dtype);
+    if (T <= 0 || E <= 0 || F <= 0 || D <= 0) return 0;
+    return layout(op, T, E, D, F, dtype, sublayers).total;
 }
 
 }  // extern "C"

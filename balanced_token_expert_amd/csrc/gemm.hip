@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256) void gemm_f32_bwd_kernel(GemmParams p) {
         float gate = 0.0f;
         if (Kind != KIND_BW && rowok) {
             t = p.perm[row];
-            gate = sigmoid_f32(p.s_in[t * p.E + g]);
+            gate = p.epi_gate ? 1.0f : sigmoid_f32(p.s_in[t * p.E + g]);
         }
         float psum = 0.0f;
 #pragma unroll
@@ -498,6 +498,8 @@ __global__ __launch_bounds__(256) void gemm_f32_bwd_kernel(GemmParams p) {
                                        : (z > 0.0f ? 1.0f : 0.0f);
                 psum = fmaf(v, u, psum);
                 ((float*)p.H)[row * p.N + n] = gate * v * du;
+            } else if (Kind == KIND_BX && p.xo) {
+                ((float*)p.xo)[row * p.N + n] = v;
             } else if (Kind == KIND_BX) {
                 const float cx = p.mix ? 1.0f - gate : 1.0f;
                 ((float*)p.out)[t * p.N + n] =
@@ -675,8 +677,10 @@ int64_t bwd_nparts(int64_t F, int dt) { return dt == 0 ? (F + 63) / 64 : (F + 25
 
 hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, const float* s,
                         void* Z, void* gU, int64_t T, int64_t E, int64_t D, int64_t F, int dt,
-                        int act, const int32_t* goff, int32_t* gblk, hipStream_t st) {
+                        int act, const int32_t* goff, int32_t* gblk, int gate_one,
+                        hipStream_t st) {
     GemmParams p = {};
+    p.epi_gate = gate_one;
     p.A = Xg; p.B = W1; p.M = T / E; p.N = F; p.K = D; p.groups = E;
     p.perm = perm; p.b_gstride = F * D; p.s_in = s; p.E = E; p.H = Z; p.gu = gU; p.act = act;
     p.goff = goff; p.gblk = gblk;
@@ -687,8 +691,9 @@ hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, con
 hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, const float* s,
                         const void* Z, void* dZ, float* part, int64_t T, int64_t E, int64_t D,
                         int64_t F, int dt, int act, const int32_t* goff, int32_t* gblk,
-                        hipStream_t st) {
+                        int gate_one, hipStream_t st) {
     GemmParams p = {};
+    p.epi_gate = gate_one;
     p.A = dYg; p.B = W2; p.M = T / E; p.N = F; p.K = D; p.groups = E;
     p.perm = perm; p.b_gstride = D * F; p.ldb = F; p.s_in = s; p.E = E; p.zin = Z; p.H = dZ;
     p.part = part; p.nparts = bwd_nparts(F, dt); p.act = act;
@@ -700,8 +705,9 @@ hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, co
 hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, const float* s,
                         const void* dYg, const void* w, const float* dl, int mix, void* dh,
                         int64_t T, int64_t E, int64_t D, int64_t F, int dt, const int32_t* goff,
-                        int32_t* gblk, hipStream_t st) {
+                        int32_t* gblk, void* grouped_out, hipStream_t st) {
     GemmParams p = {};
+    p.xo = grouped_out;
     p.A = dZ; p.B = W1; p.M = T / E; p.N = D; p.K = F; p.groups = E;
     p.perm = perm; p.b_gstride = F * D; p.ldb = D; p.s_in = s; p.E = E; p.dyg = dYg; p.wc = w;
     p.dl = dl; p.mix = mix; p.out = dh;

@@ -470,6 +470,9 @@ BASE_DEV void dma_epilogue_bwd(const GemmParams& p, f32x16_t (&acc)[TM][TN], con
                         dz[c] = g * y[c] * du;
                     }
                     *(bf16x4_t*)((uint16_t*)p.H + row * p.N + n) = __builtin_convertvector(dz, bf16x4_t);
+                } else if (Kind == KIND_BX && p.xo) {
+                    // plain grouped rows (the input gradient of a layer-norm block)
+                    *(bf16x4_t*)((uint16_t*)p.xo + row * p.N + n) = __builtin_convertvector(y, bf16x4_t);
                 } else if (Kind == KIND_BX) {
                     const f32x4_t d = __builtin_convertvector(
                         *(const bf16x4_t*)((const uint16_t*)p.dyg + row * p.N + n), f32x4_t);
@@ -956,8 +959,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pers_kernel(GemmParams 
             const int64_t m = s.t.tm * BM + wm * WTM + i * 32 + (lane & 31);
             if (ROWTOK && s.ok && m < s.t.rows) {
                 tr[i] = p.perm[s.t.row0 + m];
-                ga[i] = (GEN && p.epi_gate) ? 1.0f
-                                            : sigmoid_f32(p.s_in[(int64_t)tr[i] * p.E + s.t.g]);
+                // epi_gate: a gate of 1 (the layer variants' inner blocks, and
+                // the backward of layer-norm blocks, whose upstream is g dy)
+                ga[i] = p.epi_gate ? 1.0f : sigmoid_f32(p.s_in[(int64_t)tr[i] * p.E + s.t.g]);
             }
         }
     };

@@ -153,6 +153,166 @@ __global__ __launch_bounds__(256) void centroid_grad_kernel(const float* dl, con
     }
 }
 
+// ---- experts of sec. 4.1 layer-norm blocks (x_{n+1} = x_n + W2 act(W1 LN(x_n)))
+
+template <int DT>
+BASE_DEV void st_elem(void* p, int64_t i, float v) {
+    if (DT) ((uint16_t*)p)[i] = f32_to_bf16(v);
+    else ((float*)p)[i] = v;
+}
+
+// one wave per grouped row: the blocks' upstream dX = g dy (fp32 copy in dXa,
+// operand copy in dXo) and the gate-logit gradient dl = g (1 - g) dg with
+// dg = dy . x_N (residual) or dy . (x_N - x_0) (convex)
+template <int DT>
+__global__ __launch_bounds__(256) void block_gate_kernel(const void* X0, const void* XN,
+                                                         const void* dYg, const int32_t* perm,
+                                                         const int32_t* goff, const float* s,
+                                                         int mix, float* dXa, void* dXo,
+                                                         float* dl, int64_t T, int64_t E,
+                                                         int64_t D) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < T; r += nw) {
+        const int64_t e = group_of(goff, E, r);
+        const float g = sigmoid_f32(s[(int64_t)perm[r] * E + e]);
+        float dg = 0.0f;
+        for (int64_t d = lane; d < D; d += 64) {
+            const int64_t i = r * D + d;
+            const float dy = ld_elem<DT>(dYg, i);
+            const float x = ld_elem<DT>(XN, i) - (mix ? ld_elem<DT>(X0, i) : 0.0f);
+            dg = fmaf(dy, x, dg);
+            dXa[i] = g * dy;
+            st_elem<DT>(dXo, i, g * dy);
+        }
+        dg = wave_sum(dg);
+        if (lane == 0) dl[r] = g * (1.0f - g) * dg;
+    }
+}
+
+// one wave per grouped row r of expert e: the layer-norm backward of
+// y = (x - mean) rstd gamma_e + beta_e (population variance, fp32
+// statistics): with xh = (x - mean) rstd and q = dY gamma_e,
+// dx = rstd (q - mean(q) - xh mean(q xh)); dXa[r] += dx, dXo[r] = dXa[r];
+// the row's mean and rstd go to stats (for the gamma / beta gradients)
+template <int DT>
+__global__ __launch_bounds__(256) void ln_backward_kernel(const void* X, const void* dY,
+                                                          const float* gamma, const int32_t* goff,
+                                                          float eps, float* dXa, void* dXo,
+                                                          float* stats, int64_t T, int64_t E,
+                                                          int64_t D) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const float inv_d = 1.0f / (float)D;
+    for (int64_t r = wave; r < T; r += nw) {
+        const int64_t e = group_of(goff, E, r);
+        const float* ga = gamma ? gamma + e * D : nullptr;
+        float sum = 0.0f;
+        for (int64_t d = lane; d < D; d += 64) sum += ld_elem<DT>(X, r * D + d);
+        const float mean = wave_sum(sum) * inv_d;
+        float ss = 0.0f;
+        for (int64_t d = lane; d < D; d += 64) {
+            const float c = ld_elem<DT>(X, r * D + d) - mean;
+            ss = fmaf(c, c, ss);
+        }
+        const float rstd = 1.0f / sqrtf(wave_sum(ss) * inv_d + eps);
+        float m1 = 0.0f, m2 = 0.0f;
+        for (int64_t d = lane; d < D; d += 64) {
+            const float xh = (ld_elem<DT>(X, r * D + d) - mean) * rstd;
+            const float q = ld_elem<DT>(dY, r * D + d) * (ga ? ga[d] : 1.0f);
+            m1 += q;
+            m2 = fmaf(q, xh, m2);
+        }
+        m1 = wave_sum(m1) * inv_d;
+        m2 = wave_sum(m2) * inv_d;
+        for (int64_t d = lane; d < D; d += 64) {
+            const int64_t i = r * D + d;
+            const float xh = (ld_elem<DT>(X, i) - mean) * rstd;
+            const float q = ld_elem<DT>(dY, i) * (ga ? ga[d] : 1.0f);
+            const float v = dXa[i] + rstd * (q - m1 - xh * m2);
+            dXa[i] = v;
+            st_elem<DT>(dXo, i, v);
+        }
+        if (lane == 0) {
+            stats[2 * r] = mean;
+            stats[2 * r + 1] = rstd;
+        }
+    }
+}
+
+// block (x, e): columns 256 x .. + 255 of dgamma[e] = sum over the expert's
+// rows of dY (x - mean) rstd and dbeta[e] = sum of dY (fp32). Wave w takes
+// rows goff[e] + w, + 4, ...; the waves' sums meet in LDS in a fixed order.
+template <int DT>
+__global__ __launch_bounds__(256) void ln_param_grad_kernel(const void* X, const void* dY,
+                                                            const float* stats,
+                                                            const int32_t* goff, float* dgamma,
+                                                            float* dbeta, int64_t D) {
+    __shared__ float red[2][4][256];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t e = blockIdx.y;
+    const int64_t d0 = (int64_t)blockIdx.x * 256 + 4 * lane;
+    const int64_t r0 = goff[e], r1 = goff[e + 1];
+    float ag[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ab[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t r = r0 + wv; r < r1; r += 4) {
+        const float mean = stats[2 * r], rstd = stats[2 * r + 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t d = d0 + i;
+            if (d < D) {
+                const float dy = ld_elem<DT>(dY, r * D + d);
+                ag[i] = fmaf(dy, (ld_elem<DT>(X, r * D + d) - mean) * rstd, ag[i]);
+                ab[i] += dy;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        red[0][wv][4 * lane + i] = ag[i];
+        red[1][wv][4 * lane + i] = ab[i];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t d = d0 + i;
+            if (d >= D) continue;
+            const int j = 4 * lane + i;
+            if (dgamma)
+                dgamma[e * D + d] = (red[0][0][j] + red[0][1][j]) + (red[0][2][j] + red[0][3][j]);
+            if (dbeta)
+                dbeta[e * D + d] = (red[1][0][j] + red[1][1][j]) + (red[1][2][j] + red[1][3][j]);
+        }
+    }
+}
+
+// one wave per grouped row: dh[perm[r]] = dXa[r] + c dYg[r] + dl[r] w_e with
+// c = 1 (residual) or 1 - g (convex)
+template <int DT>
+__global__ __launch_bounds__(256) void finish_dh_kernel(const float* dXa, const void* dYg,
+                                                        const float* dl, const void* w,
+                                                        const int32_t* perm, const int32_t* goff,
+                                                        const float* s, int mix, void* dh,
+                                                        int64_t T, int64_t E, int64_t D) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < T; r += nw) {
+        const int64_t e = group_of(goff, E, r);
+        const int64_t t = perm[r];
+        const float g = sigmoid_f32(s[t * E + e]);
+        const float c = mix ? 1.0f - g : 1.0f;
+        const float l = dl[r];
+        for (int64_t d = lane; d < D; d += 64) {
+            const float v = dXa[r * D + d] + c * ld_elem<DT>(dYg, r * D + d) +
+                            l * ld_elem<DT>(w, e * D + d);
+            st_elem<DT>(dh, t * D + d, v);
+        }
+    }
+}
+
 unsigned row_blocks(int64_t T) {
     int64_t b = (T + 3) / 4;  // 4 waves of 64 per block, one row each
     return (unsigned)(b > 65536 ? 65536 : b);
@@ -182,6 +342,60 @@ hipError_t launch_gate_grad(const float* part, int64_t nparts, const void* Xg, c
     else
         hipLaunchKernelGGL(gate_grad_kernel<0>, dim3(row_blocks(T)), dim3(256), 0, st, part,
                            nparts, Xg, dYg, perm, goff, s, mix, dl, T, E, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_gate(const void* X0, const void* XN, const void* dYg, const int32_t* perm,
+                             const int32_t* goff, const float* s, int mix, float* dXa, void* dXo,
+                             float* dl, int64_t T, int64_t E, int64_t D, int dt, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (dt)
+        hipLaunchKernelGGL(block_gate_kernel<1>, dim3(row_blocks(T)), dim3(256), 0, st, X0, XN,
+                           dYg, perm, goff, s, mix, dXa, dXo, dl, T, E, D);
+    else
+        hipLaunchKernelGGL(block_gate_kernel<0>, dim3(row_blocks(T)), dim3(256), 0, st, X0, XN,
+                           dYg, perm, goff, s, mix, dXa, dXo, dl, T, E, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_backward(const void* X, const void* dY, const float* gamma,
+                              const int32_t* goff, double eps, float* dXa, void* dXo,
+                              float* stats, int64_t T, int64_t E, int64_t D, int dt,
+                              hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (dt)
+        hipLaunchKernelGGL(ln_backward_kernel<1>, dim3(row_blocks(T)), dim3(256), 0, st, X, dY,
+                           gamma, goff, (float)eps, dXa, dXo, stats, T, E, D);
+    else
+        hipLaunchKernelGGL(ln_backward_kernel<0>, dim3(row_blocks(T)), dim3(256), 0, st, X, dY,
+                           gamma, goff, (float)eps, dXa, dXo, stats, T, E, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_param_grad(const void* X, const void* dY, const float* stats,
+                                const int32_t* goff, float* dgamma, float* dbeta, int64_t E,
+                                int64_t D, int dt, hipStream_t st) {
+    if (!dgamma && !dbeta) return hipSuccess;
+    const dim3 grid((unsigned)((D + 255) / 256), (unsigned)E);
+    if (dt)
+        hipLaunchKernelGGL(ln_param_grad_kernel<1>, grid, dim3(256), 0, st, X, dY, stats, goff,
+                           dgamma, dbeta, D);
+    else
+        hipLaunchKernelGGL(ln_param_grad_kernel<0>, grid, dim3(256), 0, st, X, dY, stats, goff,
+                           dgamma, dbeta, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish_dh(const float* dXa, const void* dYg, const float* dl, const void* w,
+                            const int32_t* perm, const int32_t* goff, const float* s, int mix,
+                            void* dh, int64_t T, int64_t E, int64_t D, int dt, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (dt)
+        hipLaunchKernelGGL(finish_dh_kernel<1>, dim3(row_blocks(T)), dim3(256), 0, st, dXa, dYg,
+                           dl, w, perm, goff, s, mix, dh, T, E, D);
+    else
+        hipLaunchKernelGGL(finish_dh_kernel<0>, dim3(row_blocks(T)), dim3(256), 0, st, dXa, dYg,
+                           dl, w, perm, goff, s, mix, dh, T, E, D);
     return hipGetLastError();
 }
 

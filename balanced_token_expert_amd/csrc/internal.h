@@ -64,22 +64,26 @@ hipError_t launch_ffn2_ex(const void* H, const int32_t* perm, const void* W2,
 // ---- backward products (gemm.hip). Rows are grouped (row r of group e is
 // token perm[r]); group e owns rows goff[e] .. goff[e+1]-1, T = goff[E];
 // gblk: E+1 ints of scratch. Gate g_r = sigmoid(s[perm[r], e]).
+// gate_one != 0 takes g = 1 (the blocks of a layer-norm expert, whose
+// upstream gradient already holds the gate).
 // Z = Xg W1_e^T and gU = g act(Z), both T x F.
 hipError_t launch_bwd_z(const void* Xg, const void* W1, const int32_t* perm, const float* s,
                         void* Z, void* gU, int64_t T, int64_t E, int64_t D, int64_t F, int dt,
-                        int act, const int32_t* goff, int32_t* gblk, hipStream_t st);
+                        int act, const int32_t* goff, int32_t* gblk, int gate_one,
+                        hipStream_t st);
 // V = dYg W2_e (T x F); dZ = g V act'(Z); part[r * bwd_nparts(F, dt) + j]
 // = partial sums over column blocks of V . act(Z)
 int64_t bwd_nparts(int64_t F, int dt);
 hipError_t launch_bwd_v(const void* dYg, const void* W2, const int32_t* perm, const float* s,
                         const void* Z, void* dZ, float* part, int64_t T, int64_t E, int64_t D,
                         int64_t F, int dt, int act, const int32_t* goff, int32_t* gblk,
-                        hipStream_t st);
-// dh[perm[r]] = (dZ W1_e)[r] + c dYg[r] + dl[r] w_e, c = 1 (mix 0) or 1 - g
+                        int gate_one, hipStream_t st);
+// dh[perm[r]] = (dZ W1_e)[r] + c dYg[r] + dl[r] w_e, c = 1 (mix 0) or 1 - g;
+// with grouped_out != nullptr instead grouped_out[r] = (dZ W1_e)[r]
 hipError_t launch_bwd_x(const void* dZ, const void* W1, const int32_t* perm, const float* s,
                         const void* dYg, const void* w, const float* dl, int mix, void* dh,
                         int64_t T, int64_t E, int64_t D, int64_t F, int dt, const int32_t* goff,
-                        int32_t* gblk, hipStream_t st);
+                        int32_t* gblk, void* grouped_out, hipStream_t st);
 // dW_e = P_e^T Q_e: P rows of length M, Q rows of length N, summed over the
 // rows of group e; dW is E x M x N. M % 8 == N % 8 == 0 for bf16.
 hipError_t launch_bwd_w(const void* P, const void* Q, int64_t M, int64_t N, int64_t E,
@@ -98,6 +102,28 @@ hipError_t launch_gate_grad(const float* part, int64_t nparts, const void* Xg, c
 // dw[e] = sum over the rows r of group e of dl[r] Xg[r]
 hipError_t launch_centroid_grad(const float* dl, const void* Xg, const int32_t* goff, void* dw,
                                 int64_t E, int64_t D, int dt, hipStream_t st);
+
+// experts of layer-norm blocks (grouped rows; expert of row r = its group):
+// dXa = g dYg (fp32) and dXo (dtype dt) = the same, dl = g (1 - g) dg with
+// dg = dYg . XN (mix 0) or dYg . (XN - X0) (mix 1)
+hipError_t launch_block_gate(const void* X0, const void* XN, const void* dYg, const int32_t* perm,
+                             const int32_t* goff, const float* s, int mix, float* dXa, void* dXo,
+                             float* dl, int64_t T, int64_t E, int64_t D, int dt, hipStream_t st);
+// layer-norm backward of the rows X (gamma: E x D fp32 or null): dXa += dx,
+// dXo = dXa (dtype dt), stats[2r] = mean, stats[2r+1] = rstd
+hipError_t launch_ln_backward(const void* X, const void* dY, const float* gamma,
+                              const int32_t* goff, double eps, float* dXa, void* dXo,
+                              float* stats, int64_t T, int64_t E, int64_t D, int dt,
+                              hipStream_t st);
+// dgamma[e] = sum dY (X - mean) rstd, dbeta[e] = sum dY over group e's rows
+// (E x D fp32 each; either may be null)
+hipError_t launch_ln_param_grad(const void* X, const void* dY, const float* stats,
+                                const int32_t* goff, float* dgamma, float* dbeta, int64_t E,
+                                int64_t D, int dt, hipStream_t st);
+// dh[perm[r]] = dXa[r] + c dYg[r] + dl[r] w_e, c = 1 (mix 0) or 1 - g
+hipError_t launch_finish_dh(const float* dXa, const void* dYg, const float* dl, const void* w,
+                            const int32_t* perm, const int32_t* goff, const float* s, int mix,
+                            void* dh, int64_t T, int64_t E, int64_t D, int dt, hipStream_t st);
 
 // ---- layernorm.hip
 // Y[r, :] = LN(X[r, :]) * gamma[e] + beta[e] over D, e = assign[perm[r]] the

@@ -270,7 +270,8 @@ int base_layer_forward_ex(const void *h, const void *w, const void *W1,
  *   expert ids it used (DEVICE; any group sizes, e.g. greedy routing).
  *   scores: DEVICE T x E fp32, the affinities the forward gated with (its
  *   `scores` output). dy: DEVICE T x D (dtype dt), original token order.
- *   opts: HOST, NULL or with sublayers == 0 (mix selects eq. 1 or convex).
+ *   opts: HOST, NULL or with sublayers == 0 (mix selects eq. 1 or convex;
+ *   layer-norm blocks: base_layer_backward_ex).
  *   Outputs (DEVICE, dtype dt, overwritten): dh T x D (original order),
  *   dw E x D, dW1 E x F x D, dW2 E x D x F. An expert with no token gets
  *   zero gradients.
@@ -295,6 +296,46 @@ int base_layer_backward(const void *h, const void *w, const void *W1,
                         void *dw, void *dW1, void *dW2,
                         base_auction_stats *stats, const base_layer_opts *opts,
                         void *ws, size_t ws_bytes, base_stream_t stream);
+
+/*
+ * base_layer_backward_ex -- base_layer_backward for the layer variants of
+ * base_layer_forward_ex as well: with opts->sublayers = N >= 1 each expert is
+ * N blocks of sec. 4.1 (layer norm, projection up, activation, projection
+ * back, residual; W1 N x E x F x D, W2 N x E x D x F, gamma / beta from
+ * opts), mixed by opts->mix. The chain rule of those blocks (the
+ * assignment fixed, the centroids learning through the gate only, as in
+ * base_layer_backward): the blocks' upstream is dx_N = g dy, the gate gets
+ * dg = dy . x_N (eq. 1) or dy . (x_N - x_0) (convex), and block n, last
+ * first, adds the layer-norm backward of W1_n^T dz_n to the residual path,
+ * dz_n = (W2_n^T dx_{n+1}) * act'(z_n).
+ *   Outputs as base_layer_backward (dW1, dW2 block-major) plus dgamma,
+ *   dbeta: DEVICE N x E x D fp32, the gradients of the layer norms' scales
+ *   and shifts (taken at ones / zeros when opts gives none), either may be
+ *   NULL. Unused when N = 0.
+ *   Precision: the blocks' forward is run again (every block input stored,
+ *   bf16 for bf16 workloads); the residual path's gradient accumulates in
+ *   fp32; layer-norm statistics fp32.
+ *   Errors: as base_layer_backward, plus INVALID_ARG for sublayers outside
+ *   [0, 64] or ln_eps < 0.
+ *   ws: scratch of base_workspace_bytes_ex(BASE_OP_LAYER_BWD, T, E, D, F,
+ *   dt, N). Phase events with N >= 1: [0] start, [1] after the grouping and
+ *   the blocks' forward, [2] after the gate, [3] = [4] after the blocks'
+ *   backward, [5] at the end.
+ */
+int base_layer_backward_ex(const void *h, const void *w, const void *W1,
+                           const void *W2, int64_t T, int64_t E, int64_t D,
+                           int64_t F, int dt, int act, const int32_t *assign,
+                           const float *scores, const void *dy, void *dh,
+                           void *dw, void *dW1, void *dW2, float *dgamma,
+                           float *dbeta, base_auction_stats *stats,
+                           const base_layer_opts *opts, void *ws,
+                           size_t ws_bytes, base_stream_t stream);
+
+/* base_workspace_bytes for calls whose scratch depends on the number of
+ * layer-norm blocks: BASE_OP_LAYER_BWD with sublayers N (0 ..
+ * 64); every other op ignores N. Returns 0 for invalid arguments. */
+size_t base_workspace_bytes_ex(int op, int64_t T, int64_t E, int64_t D,
+                               int64_t F, int dtype, int sublayers);
 
 /*
  * base_set_phase_events -- optional tracing. When `events` is non-NULL, every

@@ -152,3 +152,96 @@ def test_backward_full_size_sampled_experts():
         assert rel_err(dev_to_f64(r["dw"][e]), dw[e]) <= 2e-2, e
         assert rel_err(dev_to_f64(r["dW1"][e]), dW1[e]) <= 2e-2, e
         assert rel_err(dev_to_f64(r["dW2"][e]), dW2[e]) <= 2e-2, e
+
+
+# ---------------------------------------------------------------- layer-norm blocks
+
+BLOCK_CASES = [
+    # T, E, D, F, dtype, act, kind, mix, blocks, layer-norm params, assignment
+    dict(T=600, E=6, D=72, F=96, dtype="f32", act="gelu", kind="mixture", mix=1, sub=2, ln=True,
+         asg="balanced"),
+    dict(T=1536, E=4, D=320, F=520, dtype="bf16", act="gelu", kind="iid", mix=1, sub=1, ln=True,
+         asg="balanced"),
+    dict(T=2048, E=8, D=256, F=512, dtype="bf16", act="relu", kind="mixture", mix=0, sub=2,
+         ln=True, asg="ragged"),
+    dict(T=1000, E=5, D=264, F=200, dtype="bf16", act="gelu", kind="iid", mix=1, sub=3, ln=False,
+         asg="empty"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BLOCK_CASES)))
+def test_block_backward_parity(ci):
+    c = BLOCK_CASES[ci]
+    N = c["sub"]
+    wl = W.custom(c["T"], c["E"], c["D"], c["F"], dtype=c["dtype"], act=c["act"],
+                  kind=c["kind"], wid=985 + ci)
+    E = wl.E
+    w = W.gen_centroids(wl)
+    h = W.gen_tokens(wl, centroids=w)
+    dy = W.gen_dy(wl)
+    W1 = np.stack([np.stack([W.gen_block_w1(wl, n, e) for e in range(E)]) for n in range(N)])
+    W2 = np.stack([np.stack([W.gen_block_w2(wl, n, e) for e in range(E)]) for n in range(N)])
+    gam = bet = None
+    if c["ln"]:
+        lnp = [W.gen_ln(wl, n) for n in range(N)]
+        gam = np.stack([g for g, _ in lnp])
+        bet = np.stack([b for _, b in lnp])
+    a = _assignment(wl.T, E, c["asg"], 40 + ci)
+    dev = {k: to_dev(v, wl.dtype) for k, v in dict(h=h, w=w, W1=W1, W2=W2, dy=dy).items()}
+    s = api.base_affinity(dev["h"], dev["w"])
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    r = api.base_layer_backward_ex(
+        dev["h"], dev["w"], dev["W1"], dev["W2"], act, torch.from_numpy(a).cuda(), s, dev["dy"],
+        mix=c["mix"], sublayers=N,
+        ln_gamma=None if gam is None else torch.from_numpy(gam).cuda(),
+        ln_beta=None if bet is None else torch.from_numpy(bet).cuda())
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    s64 = s.cpu().numpy().astype(np.float64)
+    dh, dw, dW1, dW2, dga, dbe = oracle.layer_backward_ex(
+        f64(h, wl.dtype), f64(w, wl.dtype), lambda n, e: f64(W1[n][e], wl.dtype),
+        lambda n, e: f64(W2[n][e], wl.dtype), a, wl.act, f64(dy, wl.dtype),
+        mix="convex" if c["mix"] else "residual", sublayers=N, gamma=gam, beta=bet, ln_eps=1e-5,
+        s=s64, store=wl.dtype)
+    stack = lambda d: np.stack([np.stack([d[(n, e)] for e in range(E)]) for n in range(N)])
+    ref = {"dh": dh, "dw": dw, "dW1": stack(dW1), "dW2": stack(dW2), "dgamma": stack(dga),
+           "dbeta": stack(dbe)}
+    got = {k: dev_to_f64(r[k]) for k in ref}
+    tol = 1e-5 if wl.dtype == "f32" else 2e-2
+    errs = {k: rel_err(got[k], ref[k]) for k in ref}
+    print(ci, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    if c["asg"] == "empty":
+        assert not got["dW1"][:, -1].any() and not got["dW2"][:, -1].any()
+        assert not got["dgamma"][:, -1].any() and not got["dbeta"][:, -1].any()
+
+
+def test_block_backward_rejects_bad_options():
+    wl = W.custom(512, 4, 64, 128, dtype="bf16", act="relu", kind="iid", wid=990)
+    host = W.gen_all(wl)
+    dev = {k: to_dev(v, wl.dtype) for k, v in host.items()}
+    s = api.base_affinity(dev["h"], dev["w"])
+    a = torch.from_numpy(_assignment(wl.T, wl.E, "balanced", 3)).cuda()
+    dyd = dev["h"].clone()
+    with pytest.raises(api.BaseError):
+        api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"][None], dev["W2"][None], 0, a, s,
+                                   dyd, sublayers=65)
+    with pytest.raises(api.BaseError):
+        api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"][None], dev["W2"][None], 0, a, s,
+                                   dyd, sublayers=1, ln_eps=-1.0)
+    # the plain entry point does not take blocks
+    with pytest.raises(api.BaseError):
+        opts_call = api.base_layer_backward
+        lib = api.load()
+        o = api.LayerOpts(0, 1, 1e-5, None, None)
+        ws = api.workspace(api.BASE_OP_LAYER_BWD, wl.T, wl.E, wl.D, wl.F, api.BASE_BF16)
+        outs = [torch.empty_like(x) for x in (dev["h"], dev["w"], dev["W1"], dev["W2"])]
+        rc = lib.base_layer_backward(*(api._ptr(x) for x in (dev["h"], dev["w"], dev["W1"],
+                                                              dev["W2"])),
+                                     wl.T, wl.E, wl.D, wl.F, api.BASE_BF16, 0, api._ptr(a),
+                                     api._ptr(s), api._ptr(dyd), *(api._ptr(x) for x in outs),
+                                     None, api.ctypes.byref(o), api._ptr(ws), ws.numel(),
+                                     api._stream(None))
+        api._check(rc, "base_layer_backward")
+        del opts_call
