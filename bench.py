@@ -47,14 +47,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99994
+FETCH_SCALE = 1.99995
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "6215bae84037b15243817fc404ff29739007b83152358865214246d628a80510",
-             2504547.9, 1181926.9),
-    "ffn2": ("large_t64k_e128_d2048", "6215bae84037b15243817fc404ff29739007b83152358865214246d628a80510",
-             2848111.6, 362500.9),
+    "ffn1": ("large_t64k_e128_d2048", "b5b4dc60c52b4abf3566facc22e0df2666b8ce95e29cf77fed6b55d24d90957f",
+             2504683.8, 1179441.2),
+    "ffn2": ("large_t64k_e128_d2048", "b5b4dc60c52b4abf3566facc22e0df2666b8ce95e29cf77fed6b55d24d90957f",
+             2892980.2, 353476.9),
 }
 
 
@@ -299,6 +299,62 @@ def layer_backward(wl, hd, wd, W1d, W2d, act, lay, reps=5):
             "mix": "residual", "status": st.status}
 
 
+def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, reps=3):
+    """base_layer_backward_ex with experts of one and two sec. 4.1 blocks
+    (layer norm, up, activation, down, residual; the convex mix), on the
+    assignment and scores of the last balanced forward step; the blocks reuse
+    the layer's expert matrices and seeded layer-norm parameters. Median ms of
+    the whole call and of its phases (library phase events): grouping and the
+    blocks' forward recompute (2 products per block), the gate, the blocks
+    taken back (5 products per block: Z, dZ, dW2, dW1, dX, and the layer-norm
+    backward), and dh + dw; each product is 2 T D F flops."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    with ThreadPoolExecutor(16) as ex:
+        dy = np.concatenate(list(ex.map(lambda r0: W.gen_dy(wl, rows=slice(r0, min(T, r0 + 4096))),
+                                        range(0, T, 4096))))
+    dyd = to_dev(dy, wl.dtype)
+    lnp = [W.gen_ln(wl, b) for b in range(2)]
+    gam = torch.from_numpy(np.stack([g for g, _ in lnp])).cuda()
+    bet = torch.from_numpy(np.stack([b for _, b in lnp])).cuda()
+    flop = 2.0 * T * D * F
+    res = {}
+    for N in (1, 2):
+        W1n = W1d[None].expand(N, *W1d.shape).contiguous()
+        W2n = W2d[None].expand(N, *W2d.shape).contiguous()
+        out = dict(dh=torch.empty_like(hd), dw=torch.empty_like(wd), dW1=torch.empty_like(W1n),
+                   dW2=torch.empty_like(W2n), stats=api.new_stats())
+
+        def call():
+            api.base_layer_backward_ex(hd, wd, W1n, W2n, act, lay["assign"], lay["scores"], dyd,
+                                       mix=api.BASE_MIX_CONVEX, sublayers=N, ln_gamma=gam[:N],
+                                       ln_beta=bet[:N], **out)
+        call()
+        torch.cuda.synchronize()
+        ev = HipEvents(6 * reps)
+        for i in range(reps):
+            api.base_set_phase_events(ev.block(6 * i), 6)
+            call()
+        torch.cuda.synchronize()
+        api.base_set_phase_events(None, 0)
+        med = lambda j0, j1: float(np.median([ev.ms(6 * i + j0, 6 * i + j1) for i in range(reps)]))
+        tot = med(0, 5)
+        ph = {"group_fwd": med(0, 1), "gate": med(1, 2), "blocks_back": med(2, 3),
+              "dh_dw": med(4, 5)}
+        st = api.read_stats(out["stats"])
+        res[f"convex_blocks{N}_ln"] = {
+            "ms": round(tot, 4), "tokens_per_s": round(T / (tot * 1e-3), 1),
+            "products": 7 * N, "tflops": round(7 * N * flop / (tot * 1e-3) / 1e12, 1),
+            "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+            "blocks_back_tflops": round(5 * N * flop / (ph["blocks_back"] * 1e-3) / 1e12, 1),
+            "status": st.status}
+        del out, W1n, W2n
+        torch.cuda.empty_cache()
+    return res
+
+
 def auction_solve(reps=10):
     """Auction solve ms on the mixture workload (device-resident fp32 scores)."""
     import torch
@@ -488,6 +544,7 @@ def main():
     res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
     if not args.no_backward:
         res["layer_backward"] = layer_backward(wl, hd, wd, W1d, W2d, act, lay)
+        res["layer_backward_blocks"] = layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay)
     if not args.no_variants:
         res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c)
     if not args.no_auction:
