@@ -49,8 +49,11 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt, int ns
         take(L.permws, perm_ws_bytes(T, E));
         take(L.xg, (size_t)T * D * b);    // token rows, grouped
         take(L.dyg, (size_t)T * D * b);   // upstream gradient rows, grouped
-        take(L.zbuf, (size_t)T * F * b);  // pre-activations Z
-        take(L.gubuf, (size_t)T * F * b); // gate * act(Z)
+        // with blocks, Z and act(Z) (and below the normalised rows) of every
+        // block, kept from the forward recompute for the way back
+        const size_t nk = nsub >= 1 ? (size_t)nsub : 1;
+        take(L.zbuf, nk * T * F * b);     // pre-activations Z
+        take(L.gubuf, nk * T * F * b);    // gate * act(Z), or act(Z) of a block
         take(L.dzbuf, (size_t)T * F * b); // dZ
         take(L.part, (size_t)T * bwd_nparts(F, dt == BASE_BF16) * 4);
         take(L.dl, (size_t)T * 4);        // gate-logit gradients
@@ -60,7 +63,7 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt, int ns
             take(L.dxo, (size_t)T * D * b);   // the same as an operand
             take(L.dyn, (size_t)T * D * b);   // gradient of a block's normalised rows
             take(L.lnst, (size_t)T * 8);      // per-row mean and rstd
-            take(L.ybuf, (size_t)T * D * b);  // normalised rows
+            take(L.ybuf, nk * T * D * b);     // normalised rows of each block
         }
         L.total = off;
         return L;
@@ -306,7 +309,9 @@ static int layer_backward(const void* h, const void* w, const void* W1, const vo
     void* dXo = W + L.dxo;
     void* dYn = W + L.dyn;
     float* lnst = (float*)(W + L.lnst);
-    void* Y = W + L.ybuf;
+    auto Yn = [&](int n) -> void* { return W + L.ybuf + (size_t)n * T * D * b; };
+    auto Zn = [&](int n) -> void* { return (char*)Z + (size_t)n * T * F * b; };
+    auto Un = [&](int n) -> void* { return (char*)gU + (size_t)n * T * F * b; };
     const int64_t k = T / E;  // unused with ragged groups, which all launches here use
     auto ga = [&](int n) -> const float* {
         return opts->ln_gamma ? opts->ln_gamma + (size_t)n * E * D : nullptr;
@@ -318,13 +323,15 @@ static int layer_backward(const void* h, const void* w, const void* W1, const vo
     auto w2 = [&](int n) { return (const char*)W2 + (size_t)n * E * D * F * b; };
     if (e == hipSuccess) e = launch_gather2(h, dy, pm, X(0), dYg, T, D, dt, st);
     for (int n = 0; n < nsub && e == hipSuccess; ++n) {
-        e = launch_layernorm(X(n), 0, pm, assign, ga(n), be(n), opts->ln_eps, Y, T, E, D, dt, st);
-        if (e == hipSuccess)
-            e = launch_ffn1(Y, nullptr, w1(n), gU, E, k, D, F, dt, act, offs, gblk, T, st);
+        e = launch_layernorm(X(n), 0, pm, assign, ga(n), be(n), opts->ln_eps, Yn(n), T, E, D, dt,
+                             st);
+        if (e == hipSuccess)  // Z_n and act(Z_n) (gate 1)
+            e = launch_bwd_z(Yn(n), w1(n), pm, scores, Zn(n), Un(n), T, E, D, F, dt, act, offs,
+                             gblk, 1, st);
         const Ffn2Epi epi = {1, 2, 2, X(n), X(n + 1)};  // x_{n+1} = x_n + C, grouped
         if (e == hipSuccess)
-            e = launch_ffn2_ex(gU, pm, w2(n), scores, h, nullptr, E, k, D, F, dt, offs, gblk, T,
-                               epi, st);
+            e = launch_ffn2_ex(Un(n), pm, w2(n), scores, h, nullptr, E, k, D, F, dt, offs, gblk,
+                               T, epi, st);
     }
     mark(1, st);
     if (e == hipSuccess)
@@ -332,17 +339,15 @@ static int layer_backward(const void* h, const void* w, const void* W1, const vo
                               st);
     mark(2, st);
     for (int n = nsub - 1; n >= 0 && e == hipSuccess; --n) {
-        e = launch_layernorm(X(n), 0, pm, assign, ga(n), be(n), opts->ln_eps, Y, T, E, D, dt, st);
-        if (e == hipSuccess)  // Z and act(Z) (gate 1: dX already holds g)
-            e = launch_bwd_z(Y, w1(n), pm, scores, Z, gU, T, E, D, F, dt, act, offs, gblk, 1, st);
+        // gate 1: the upstream dX already holds g
+        e = launch_bwd_v(dXo, w2(n), pm, scores, Zn(n), dZ, part, T, E, D, F, dt, act, offs, gblk,
+                         1, st);
         if (e == hipSuccess)
-            e = launch_bwd_v(dXo, w2(n), pm, scores, Z, dZ, part, T, E, D, F, dt, act, offs, gblk,
-                             1, st);
+            e = launch_bwd_w(dXo, Un(n), D, F, E, offs, (char*)dW2 + (size_t)n * E * D * F * b,
+                             dt, st);
         if (e == hipSuccess)
-            e = launch_bwd_w(dXo, gU, D, F, E, offs, (char*)dW2 + (size_t)n * E * D * F * b, dt,
+            e = launch_bwd_w(dZ, Yn(n), F, D, E, offs, (char*)dW1 + (size_t)n * E * F * D * b, dt,
                              st);
-        if (e == hipSuccess)
-            e = launch_bwd_w(dZ, Y, F, D, E, offs, (char*)dW1 + (size_t)n * E * F * D * b, dt, st);
         if (e == hipSuccess)
             e = launch_bwd_x(dZ, w1(n), pm, scores, dYg, w, dl, mix, dh, T, E, D, F, dt, offs,
                              gblk, dYn, st);

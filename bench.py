@@ -305,9 +305,10 @@ def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, reps=3):
     assignment and scores of the last balanced forward step; the blocks reuse
     the layer's expert matrices and seeded layer-norm parameters. Median ms of
     the whole call and of its phases (library phase events): grouping and the
-    blocks' forward recompute (2 products per block), the gate, the blocks
-    taken back (5 products per block: Z, dZ, dW2, dW1, dX, and the layer-norm
-    backward), and dh + dw; each product is 2 T D F flops."""
+    blocks' forward recompute (2 products per block, keeping Z and act(Z)),
+    the gate, the blocks taken back (4 products per block: dZ, dW2, dW1, dX,
+    and the layer-norm backward), and dh + dw; each product is 2 T D F
+    flops."""
     import torch
     from balanced_token_expert_amd import api
     from balanced_token_expert_amd import workloads as W
@@ -346,9 +347,9 @@ def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, reps=3):
         st = api.read_stats(out["stats"])
         res[f"convex_blocks{N}_ln"] = {
             "ms": round(tot, 4), "tokens_per_s": round(T / (tot * 1e-3), 1),
-            "products": 7 * N, "tflops": round(7 * N * flop / (tot * 1e-3) / 1e12, 1),
+            "products": 6 * N, "tflops": round(6 * N * flop / (tot * 1e-3) / 1e12, 1),
             "phase_ms": {k: round(v, 4) for k, v in ph.items()},
-            "blocks_back_tflops": round(5 * N * flop / (ph["blocks_back"] * 1e-3) / 1e12, 1),
+            "blocks_back_tflops": round(4 * N * flop / (ph["blocks_back"] * 1e-3) / 1e12, 1),
             "status": st.status}
         del out, W1n, W2n
         torch.cuda.empty_cache()

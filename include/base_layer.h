@@ -312,9 +312,11 @@ int base_layer_backward(const void *h, const void *w, const void *W1,
  *   dbeta: DEVICE N x E x D fp32, the gradients of the layer norms' scales
  *   and shifts (taken at ones / zeros when opts gives none), either may be
  *   NULL. Unused when N = 0.
- *   Precision: the blocks' forward is run again (every block input stored,
- *   bf16 for bf16 workloads); the residual path's gradient accumulates in
- *   fp32; layer-norm statistics fp32.
+ *   Precision: the blocks' forward is run again and its state kept for the
+ *   way back (each block's input, layer-norm output, Z and act(Z), bf16 for
+ *   bf16 workloads); the residual path's gradient accumulates in fp32;
+ *   layer-norm statistics fp32. The scratch grows by about
+ *   N (2 T F + 2 T D) elements.
  *   Errors: as base_layer_backward, plus INVALID_ARG for sublayers outside
  *   [0, 64] or ln_eps < 0.
  *   ws: scratch of base_workspace_bytes_ex(BASE_OP_LAYER_BWD, T, E, D, F,

@@ -166,6 +166,15 @@ BLOCK_CASES = [
          ln=True, asg="ragged"),
     dict(T=1000, E=5, D=264, F=200, dtype="bf16", act="gelu", kind="iid", mix=1, sub=3, ln=False,
          asg="empty"),
+    # rows of 1032 and 2056 elements: the layer-norm backward holds 4 and 8
+    # pieces of 8 per lane
+    dict(T=900, E=3, D=1032, F=136, dtype="bf16", act="gelu", kind="iid", mix=0, sub=1, ln=True,
+         asg="ragged"),
+    dict(T=1024, E=4, D=2056, F=256, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=True,
+         asg="balanced"),
+    # D not a multiple of 8: the row kernels' one-element form
+    dict(T=700, E=5, D=100, F=120, dtype="f32", act="gelu", kind="mixture", mix=1, sub=2, ln=True,
+         asg="ragged"),
 ]
 
 
