@@ -254,3 +254,45 @@ def test_block_backward_rejects_bad_options():
                                      api._stream(None))
         api._check(rc, "base_layer_backward")
         del opts_call
+
+
+@pytest.mark.parametrize("mix", [0, 1])
+def test_backward_ex_without_blocks_matches_plain(mix):
+    """sublayers = 0 through base_layer_backward_ex is base_layer_backward,
+    bit for bit."""
+    wl = W.custom(1536, 4, 320, 520, dtype="bf16", act="gelu", kind="iid", wid=995 + mix)
+    host = W.gen_all(wl)
+    host["dy"] = W.gen_dy(wl)
+    a = _assignment(wl.T, wl.E, "ragged", 7)
+    r, _ = _run(wl, host, a, mix)
+    dev = {k: to_dev(v, wl.dtype) for k, v in host.items()}
+    s = api.base_affinity(dev["h"], dev["w"])
+    rx = api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_GELU,
+                                    torch.from_numpy(a).cuda(), s, dev["dy"], mix=mix,
+                                    sublayers=0)
+    torch.cuda.synchronize()
+    assert api.read_stats(rx["stats"]).status == 0
+    for k in ("dh", "dw", "dW1", "dW2"):
+        assert torch.equal(r[k], rx[k]), k
+
+
+def test_block_backward_zero_upstream_gradient_is_zero():
+    wl = W.custom(1024, 4, 256, 512, dtype="bf16", act="gelu", kind="iid", wid=997)
+    N, E = 2, wl.E
+    w = W.gen_centroids(wl)
+    h = W.gen_tokens(wl, centroids=w)
+    W1 = np.stack([np.stack([W.gen_block_w1(wl, n, e) for e in range(E)]) for n in range(N)])
+    W2 = np.stack([np.stack([W.gen_block_w2(wl, n, e) for e in range(E)]) for n in range(N)])
+    lnp = [W.gen_ln(wl, n) for n in range(N)]
+    dev = {k: to_dev(v, wl.dtype) for k, v in dict(h=h, w=w, W1=W1, W2=W2).items()}
+    s = api.base_affinity(dev["h"], dev["w"])
+    a = torch.from_numpy(_assignment(wl.T, E, "balanced", 8)).cuda()
+    r = api.base_layer_backward_ex(
+        dev["h"], dev["w"], dev["W1"], dev["W2"], api.BASE_ACT_GELU, a, s,
+        torch.zeros_like(dev["h"]), mix=1, sublayers=N,
+        ln_gamma=torch.from_numpy(np.stack([g for g, _ in lnp])).cuda(),
+        ln_beta=torch.from_numpy(np.stack([b for _, b in lnp])).cuda())
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    for k in ("dh", "dw", "dW1", "dW2", "dgamma", "dbeta"):
+        assert not r[k].float().abs().max().item(), k
