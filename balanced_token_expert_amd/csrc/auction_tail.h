@@ -38,6 +38,9 @@ static size_t tail_lds_bytes(int64_t E, int L, int threads) {
 }
 
 constexpr int kRbBatch = 8;  // slots per lane loaded at once by a rebuild
+// bids a wave makes before it adds them to the workgroup's count and checks
+// the bid cap (one shared atomic per batch instead of one per bid)
+constexpr int kBidBatch = 8;
 
 // Loads of data this workgroup wrote (after the writer's memory wait):
 // workgroup scope, i.e. plain loads that may hit the CU's L1.
@@ -251,11 +254,21 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
     double* xb = rbx_b + wave * 64;
     int32_t* xt = rbx_t + wave * 64;
     int32_t* xs = rbx_s + wave * 64;
-    auto count_bid = [&]() {
-        if (lane == 0) {
-            const unsigned long long nbd = atomicAdd(&nbids, 1ull) + 1;
+    // this wave's bids not yet in nbids, and whether the cap had been reached
+    // at its last check (other waves' stops are seen at this wave's next one)
+    int lbids = 0;
+    bool halted = first_lane_i32(stop) != 0;
+    auto flush_bids = [&]() {
+        if (lane == 0 && lbids > 0) {
+            const unsigned long long nbd =
+                atomicAdd(&nbids, (unsigned long long)lbids) + (unsigned long long)lbids;
             if (nbd >= cap) stop = 1;
         }
+        lbids = 0;
+        halted = first_lane_i32(stop) != 0;
+    };
+    auto count_bid = [&]() {
+        if (++lbids >= kBidBatch) flush_bids();
     };
 
     int pending = -1;        // expert with this wave's last slot store not yet counted
@@ -270,7 +283,7 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
         int t = ident ? j : first_lane_i32(list[j]);
         int fr = -1;  // expert t was just evicted from
         while (t >= 0) {
-            if (first_lane_i32(stop)) break;
+            if (halted) break;
             // the row: from the cache when the tag names t before and after
             float v[NCH];
             bool hit = false;
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                     // bid cap also ends a phase that cannot progress)
                     lds_unlock(&lock[e], lane);
                     count_bid();
-                    if (first_lane_i32(stop)) { t = -1; break; }
+                    if (halted) { t = -1; break; }
                     continue;
                 }
                 int slot, victim = -1;
@@ -361,7 +374,9 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
                 if (lane == 0) {
                     stk[slot] = t;
                     sbd[slot] = beta;
-                    st_issued[e] += 1;
+                    // no-return LDS add: visible before the unlock's wait ends
+                    __hip_atomic_fetch_add(&st_issued[e], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 pending = e;
                 // the new holder enters the list if the list covers it
@@ -419,6 +434,7 @@ __global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float
             }
         }
     }
+    flush_bids();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (pending >= 0) lds_count(&st_done[pending], lane);
     if (lane == 0) atomicMax(&max_steps, steps);

@@ -84,8 +84,10 @@ typedef enum {
  * phase). The result is within T * eps_end of the optimum of eq. 2, and is
  * the optimum itself when eps_end < gap / T, gap being the distance from the
  * optimum to the second-best balanced assignment. max_bids <= 0 means no cap;
- * otherwise the auction stops once that many bids have been made and reports
- * BASE_ERR_NOT_CONVERGED (a safety valve, not part of the method). */
+ * otherwise the auction stops at its first check after that many bids (after
+ * every parallel round, and every 8 bids of each wave of the single-workgroup
+ * phase ends) and reports BASE_ERR_NOT_CONVERGED (a safety valve, not part of
+ * the method). */
 typedef struct {
     double eps_start;
     double eps_end;
