@@ -47,7 +47,8 @@ Layout layout(int op, int64_t T, int64_t E, int64_t D, int64_t F, int dt, int ns
         take(L.offsets, (size_t)(E + 1) * 4);
         take(L.gblk, (size_t)(E + 1) * 4);
         take(L.permws, perm_ws_bytes(T, E));
-        take(L.xg, (size_t)T * D * b);    // token rows, grouped
+        // token rows, grouped (with blocks, the first block input holds them)
+        if (nsub == 0) take(L.xg, (size_t)T * D * b);
         take(L.dyg, (size_t)T * D * b);   // upstream gradient rows, grouped
         // with blocks, Z and act(Z) (and below the normalised rows) of every
         // block, kept from the forward recompute for the way back
