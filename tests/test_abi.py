@@ -136,3 +136,51 @@ def test_layer_ex_host_errors(lib):
     assert call(eps=-1.0) == api.BASE_ERR_INVALID_ARG
     assert call(ws=lay) == api.BASE_ERR_INVALID_ARG        # needs the LAYER_EX workspace
     assert call(T=10) == api.BASE_ERR_INDIVISIBLE
+
+
+def test_backward_host_errors(lib):
+    T, E, D, F = 12, 3, 8, 16
+    bf = api.BASE_BF16
+    ws_plain = api.base_workspace_bytes(api.BASE_OP_LAYER_BWD, T, E, D, F, bf)
+
+    def call(T=T, D=D, F=F, dt=1, act=1, mix=0, sub=None, eps=1e-5, ws=1 << 30, ex=False,
+             ptr=FAKE):
+        o = None if sub is None else api.LayerOpts(mix, sub, eps, None, None)
+        op = None if o is None else ctypes.byref(o)
+        args = [ptr, FAKE, FAKE, FAKE, T, E, D, F, dt, act, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                FAKE]
+        if ex:
+            return lib.base_layer_backward_ex(*args, None, None, None, op, FAKE, ws, None)
+        return lib.base_layer_backward(*args, None, op, FAKE, ws, None)
+
+    for ex in (False, True):
+        assert call(ptr=None, ex=ex) == api.BASE_ERR_INVALID_ARG
+        assert call(T=0, ex=ex) == api.BASE_ERR_INVALID_ARG
+        assert call(dt=9, ex=ex) == api.BASE_ERR_INVALID_ARG
+        assert call(act=5, ex=ex) == api.BASE_ERR_INVALID_ARG
+        assert call(mix=2, sub=0, ex=ex) == api.BASE_ERR_INVALID_ARG
+        assert call(D=12, ex=ex) == api.BASE_ERR_UNSUPPORTED          # bf16 needs D % 8 == 0
+        assert call(F=(1 << 20) + 8, ex=ex) == api.BASE_ERR_UNSUPPORTED  # 32-bit tile offsets
+        assert call(ws=100, ex=ex) == api.BASE_ERR_INVALID_ARG
+    # the plain entry point takes plain experts only
+    assert call(sub=1) == api.BASE_ERR_UNSUPPORTED
+    assert call(sub=65, ex=True) == api.BASE_ERR_INVALID_ARG
+    assert call(sub=-1, ex=True) == api.BASE_ERR_INVALID_ARG
+    assert call(sub=1, eps=-1.0, ex=True) == api.BASE_ERR_INVALID_ARG
+    # blocks need the larger workspace
+    assert call(sub=1, ws=ws_plain, ex=True) == api.BASE_ERR_INVALID_ARG
+
+
+def test_backward_workspace_grows_with_blocks(lib):
+    T, E, D, F = 65536, 128, 2048, 8192
+    bf = api.BASE_BF16
+    ex = lambda op, n: api.base_workspace_bytes_ex(op, T, E, D, F, bf, n)
+    plain = api.base_workspace_bytes(api.BASE_OP_LAYER_BWD, T, E, D, F, bf)
+    assert ex(api.BASE_OP_LAYER_BWD, 0) == plain
+    one, two = ex(api.BASE_OP_LAYER_BWD, 1), ex(api.BASE_OP_LAYER_BWD, 2)
+    # each block keeps its input, layer-norm output, Z and act(Z)
+    assert two - one >= 2 * T * F * 2 + 2 * T * D * 2
+    assert one > plain
+    assert ex(api.BASE_OP_LAYER_BWD, 65) == 0 and ex(api.BASE_OP_LAYER_BWD, -1) == 0
+    # other ops ignore the block count
+    assert ex(api.BASE_OP_LAYER, 3) == api.base_workspace_bytes(api.BASE_OP_LAYER, T, E, D, F, bf)
