@@ -167,7 +167,7 @@ def cpu_baseline(wl, h, w, W1, W2, sample_experts=96):
     per_tok = (t_aff + t_auc + t_gr) / wl.T + t_ffn / max(n_tok, 1)
     cores = len(os.sched_getaffinity(0))
     return {"value": round(1.0 / per_tok, 1), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": (f"{wl.name}: fp64 affinity, CPU auction (1 thread) and greedy over all "
                        f"{wl.T} tokens ({t_aff:.2f}s, {t_auc:.2f}s, {t_gr:.2f}s); fp64 expert "
                        f"FFN + eq. 1 for the {n_tok} tokens of experts 0..{sample_experts - 1} "
@@ -399,7 +399,31 @@ def auction_solve(reps=10):
             "min_ms": round(float(np.min(times)), 4), "status": st.status,
             "bids_per_phase": st.bids, "rounds_per_phase": st.rounds,
             "balanced": balanced, "dual_gap": gap, "dual_gap_bound": T * wl.eps_end,
-            "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1}
+            "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1,
+            "last_solve": solve_rates(times[-1], st, T, E)}
+
+
+def solve_rates(ms, st, T, E):
+    """Bid rate, time per dependent round and effective bandwidth of one
+    solve: a bid reads a score row (4E bytes) and writes an fp64 bid; the
+    result is T int32 ids and the permutation."""
+    nb, nr = int(sum(st.bids)), int(sum(st.rounds))
+    sec = ms * 1e-3
+    alg = nb * (4 * E + 8) + 8 * T
+    return {"ms": round(ms, 4), "bids": nb, "bids_per_s": round(nb / sec, 1),
+            "dependent_rounds": nr, "us_per_dependent_round": round(1e6 * sec / max(nr, 1), 3),
+            "algorithmic_bytes": alg, "effective_GBps": round(alg / sec / 1e9, 2)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_probe(nbytes=1 << 30, reps=4):
