@@ -124,6 +124,43 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _expect(t, shape, dtype, name):
+    """The library sees plain pointers and trusts the sizes it is given: check
+    each tensor's shape and dtype here, before anything is launched."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _layer_shapes(h, w, W1, W2, nsub, assign=None, scores=None, io=(), ln=(), lngrad=()):
+    """Shapes of a layer call: h T x D, w E x D, W1 [N x] E x F x D, W2
+    [N x] E x D x F (N = nsub when nsub >= 1), assign T int32, scores T x E
+    fp32; io: tensors shaped and typed like h / w / W1 / W2 (name, tensor,
+    like); ln / lngrad: N x E x D fp32 tensors. Returns (T, E, D, F)."""
+    if h.dim() != 2 or w.dim() != 2:
+        raise ValueError("h and w must be 2-D")
+    T, D = h.shape
+    E = w.shape[0]
+    lead = (nsub,) if nsub >= 1 else ()
+    if W1.dim() != len(lead) + 3:
+        raise ValueError(f"W1 must be {'N x ' if lead else ''}E x F x D")
+    F = W1.shape[-2]
+    _expect(w, (E, D), h.dtype, "w")
+    _expect(W1, lead + (E, F, D), h.dtype, "W1")
+    _expect(W2, lead + (E, D, F), h.dtype, "W2")
+    _expect(assign, (T,), torch.int32, "assign")
+    _expect(scores, (T, E), torch.float32, "scores")
+    like = {"h": h, "w": w, "W1": W1, "W2": W2}
+    for name, t, ref in io:
+        _expect(t, like[ref].shape, h.dtype, name)
+    for name, t in tuple(ln) + tuple(lngrad):
+        _expect(t, (nsub, E, D), torch.float32, name)
+    return T, E, D, F
+
+
 def base_workspace_bytes(op: int, T: int, E: int, D: int = 0, F: int = 0,
                          dtype: int = BASE_BF16) -> int:
     return int(load().base_workspace_bytes(op, T, E, D, F, dtype))
@@ -210,9 +247,8 @@ def base_layer_forward(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = None, 
                        scores=None, perm=None, out=None, stats=None, ws=None, stream=None,
                        want_scores=True):
     _dev(h, w, W1, W2, assign, scores, perm, out)
-    T, D = h.shape
-    E = w.shape[0]
-    F = W1.shape[1]
+    T, E, D, F = _layer_shapes(h, w, W1, W2, 0, assign, scores, io=(("out", out, "h"),))
+    _expect(perm, (T,), torch.int32, "perm")
     dev = h.device
     dt = _dt(h)
     c = cfg() if c is None else c
@@ -241,12 +277,10 @@ def base_layer_forward_ex(h, w, W1, W2, act: int, mode: int, c: AuctionCfg = Non
     or N x E x F x D / N x E x D x F; ln_gamma / ln_beta N x E x D fp32 or
     None."""
     _dev(h, w, W1, W2, assign, scores, perm, out, ln_gamma, ln_beta)
-    for t in (ln_gamma, ln_beta):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError("layer-norm parameters are fp32")
-    T, D = h.shape
-    E = w.shape[0]
-    F = W1.shape[-2]
+    T, E, D, F = _layer_shapes(h, w, W1, W2, sublayers, assign, scores,
+                               io=(("out", out, "h"),),
+                               ln=(("ln_gamma", ln_gamma), ("ln_beta", ln_beta)))
+    _expect(perm, (T,), torch.int32, "perm")
     dev = h.device
     dt = _dt(h)
     c = cfg() if c is None else c
@@ -277,9 +311,9 @@ def base_layer_backward(h, w, W1, W2, act: int, assign, scores, dy, mix: int = 0
     assignment fixed; returns dict(dh, dw, dW1, dW2, stats), each gradient
     in the dtype of h."""
     _dev(h, w, W1, W2, assign, scores, dy, dh, dw, dW1, dW2)
-    T, D = h.shape
-    E = w.shape[0]
-    F = W1.shape[1]
+    T, E, D, F = _layer_shapes(h, w, W1, W2, 0, assign, scores,
+                               io=(("dy", dy, "h"), ("dh", dh, "h"), ("dw", dw, "w"),
+                                   ("dW1", dW1, "W1"), ("dW2", dW2, "W2")))
     dev = h.device
     dt = _dt(h)
     dh = torch.empty_like(h) if dh is None else dh
@@ -310,9 +344,11 @@ def base_layer_backward_ex(h, w, W1, W2, act: int, assign, scores, dy, mix: int 
     base_layer_forward_ex; returns dict(dh, dw, dW1, dW2, dgamma, dbeta,
     stats) (dgamma / dbeta N x E x D fp32 when sublayers >= 1)."""
     _dev(h, w, W1, W2, assign, scores, dy, dh, dw, dW1, dW2, ln_gamma, ln_beta, dgamma, dbeta)
-    T, D = h.shape
-    E = w.shape[0]
-    F = W1.shape[-2]
+    T, E, D, F = _layer_shapes(h, w, W1, W2, sublayers, assign, scores,
+                               io=(("dy", dy, "h"), ("dh", dh, "h"), ("dw", dw, "w"),
+                                   ("dW1", dW1, "W1"), ("dW2", dW2, "W2")),
+                               ln=(("ln_gamma", ln_gamma), ("ln_beta", ln_beta)),
+                               lngrad=(("dgamma", dgamma), ("dbeta", dbeta)))
     dev = h.device
     dt = _dt(h)
     dh = torch.empty_like(h) if dh is None else dh

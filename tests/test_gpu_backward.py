@@ -233,9 +233,21 @@ def test_block_backward_rejects_bad_options():
     s = api.base_affinity(dev["h"], dev["w"])
     a = torch.from_numpy(_assignment(wl.T, wl.E, "balanced", 3)).cuda()
     dyd = dev["h"].clone()
-    with pytest.raises(api.BaseError):
+    W1x = dev["W1"][None].expand(65, *dev["W1"].shape).contiguous()
+    W2x = dev["W2"][None].expand(65, *dev["W2"].shape).contiguous()
+    with pytest.raises(api.BaseError):  # more blocks than the library takes
+        api.base_layer_backward_ex(dev["h"], dev["w"], W1x, W2x, 0, a, s, dyd, sublayers=65,
+                                   want_ln_grads=False)
+    del W1x, W2x
+    # shapes that do not match the block count never reach the library
+    with pytest.raises(ValueError):
         api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"][None], dev["W2"][None], 0, a, s,
-                                   dyd, sublayers=65)
+                                   dyd, sublayers=2)
+    with pytest.raises(TypeError):
+        api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"][None], dev["W2"][None], 0, a, s,
+                                   dyd, sublayers=1,
+                                   ln_gamma=torch.ones((1, wl.E, wl.D), dtype=torch.bfloat16,
+                                                       device="cuda"))
     with pytest.raises(api.BaseError):
         api.base_layer_backward_ex(dev["h"], dev["w"], dev["W1"][None], dev["W2"][None], 0, a, s,
                                    dyd, sublayers=1, ln_eps=-1.0)
