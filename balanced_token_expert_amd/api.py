@@ -135,6 +135,18 @@ def _expect(t, shape, dtype, name):
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
 
 
+def _score_shapes(scores, assign=None, perm=None, offsets=None):
+    """scores T x E fp32; assign, perm T int32; offsets E + 1 int32."""
+    if scores.dim() != 2:
+        raise ValueError("scores must be T x E")
+    T, E = scores.shape
+    _expect(scores, (T, E), torch.float32, "scores")
+    _expect(assign, (T,), torch.int32, "assign")
+    _expect(perm, (T,), torch.int32, "perm")
+    _expect(offsets, (E + 1,), torch.int32, "offsets")
+    return T, E
+
+
 def _layer_shapes(h, w, W1, W2, nsub, assign=None, scores=None, io=(), ln=(), lngrad=()):
     """Shapes of a layer call: h T x D, w E x D, W1 [N x] E x F x D, W2
     [N x] E x D x F (N = nsub when nsub >= 1), assign T int32, scores T x E
@@ -198,8 +210,12 @@ def cfg(eps_start=1.0, eps_end=1e-4, eps_factor=10.0, max_bids=0) -> AuctionCfg:
 
 def base_affinity(h: torch.Tensor, w: torch.Tensor, scores=None, stream=None):
     _dev(h, w, scores)
+    if h.dim() != 2 or w.dim() != 2:
+        raise ValueError("h and w must be 2-D")
     T, D = h.shape
     E = w.shape[0]
+    _expect(w, (E, D), h.dtype, "w")
+    _expect(scores, (T, E), torch.float32, "scores")
     if scores is None:
         scores = torch.empty((T, E), dtype=torch.float32, device=h.device)
     rc = load().base_affinity(_ptr(h), _ptr(w), _ptr(scores), T, E, D, _dt(h), _stream(stream))
@@ -209,8 +225,9 @@ def base_affinity(h: torch.Tensor, w: torch.Tensor, scores=None, stream=None):
 
 def base_assign_auction(scores: torch.Tensor, c: AuctionCfg, assign=None, perm=None,
                         offsets=None, prices=None, stats=None, ws=None, stream=None):
-    _dev(scores)
-    T, E = scores.shape
+    _dev(scores, assign, perm, offsets, prices)
+    T, E = _score_shapes(scores, assign=assign, perm=perm, offsets=offsets)
+    _expect(prices, (E,), torch.float64, "prices")
     dev = scores.device
     assign = torch.empty(T, dtype=torch.int32, device=dev) if assign is None else assign
     perm = torch.empty(T, dtype=torch.int32, device=dev) if perm is None else perm
@@ -228,8 +245,9 @@ def base_assign_auction(scores: torch.Tensor, c: AuctionCfg, assign=None, perm=N
 
 def base_route_greedy(scores: torch.Tensor, assign=None, counts=None, perm=None,
                       offsets=None, ws=None, stream=None, with_perm=True):
-    _dev(scores)
-    T, E = scores.shape
+    _dev(scores, assign, counts, perm, offsets)
+    T, E = _score_shapes(scores, assign=assign, perm=perm, offsets=offsets)
+    _expect(counts, (E,), torch.int32, "counts")
     dev = scores.device
     assign = torch.empty(T, dtype=torch.int32, device=dev) if assign is None else assign
     counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts

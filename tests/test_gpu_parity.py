@@ -361,3 +361,28 @@ def test_host_errors():
     W1 = torch.zeros((3, 16, 8), dtype=torch.bfloat16, device="cuda")
     W2 = torch.zeros((3, 8, 16), dtype=torch.bfloat16, device="cuda")
 
+
+
+def test_binding_rejects_mismatched_tensors():
+    """Shapes and dtypes are checked in the binding, before the library (which
+    sees plain pointers) could read past a buffer."""
+    s = torch.zeros((12, 3), device="cuda")
+    with pytest.raises(TypeError):
+        api.base_assign_auction(s.to(torch.bfloat16), api.cfg())
+    with pytest.raises(ValueError):
+        api.base_assign_auction(s, api.cfg(), perm=torch.empty(11, dtype=torch.int32,
+                                                               device="cuda"))
+    with pytest.raises(TypeError):
+        api.base_route_greedy(s, assign=torch.empty(12, dtype=torch.int64, device="cuda"))
+    h = torch.zeros((12, 8), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3, 8), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((3, 16, 8), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((3, 8, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError):
+        api.base_affinity(h, w.float())
+    with pytest.raises(ValueError):
+        api.base_layer_forward(h, w, W1, W2[:, :, :8].contiguous(), api.BASE_ACT_RELU,
+                               api.BASE_ROUTE_BALANCED)
+    with pytest.raises(ValueError):
+        api.base_layer_forward_ex(h, w, W1, W2, api.BASE_ACT_RELU, api.BASE_ROUTE_BALANCED,
+                                  sublayers=1)
