@@ -1,0 +1,115 @@
+"""The layer variants and the block backward at the large workload's full size
+(T = 65536, E = 128, D = 2048, F = 8192, bf16, GELU), in the configuration the
+benchmark times: balanced routing, the convex mix, experts of sec. 4.1
+layer-norm blocks that reuse the layer's expert matrices, seeded layer-norm
+parameters. Three experts (first, one between, last) are checked against the
+oracle computed for those experts only: every output row of their tokens, and
+every gradient of their matrices, layer norms, centroids and token rows.
+Tolerance 2e-2 max-abs relative (bf16)."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from balanced_token_expert_amd import api
+from balanced_token_expert_amd import workloads as W
+from tests.gpu_util import dev_to_f64, f64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+EXPERTS = [0, 77, 127]
+
+
+@pytest.fixture(scope="module")
+def large():
+    wl = W.workload(5)
+    T, E = wl.T, wl.E
+    with ThreadPoolExecutor(16) as ex:
+        w = W.gen_centroids(wl)
+        h = np.concatenate(list(ex.map(
+            lambda r0: W.gen_tokens(wl, rows=slice(r0, min(T, r0 + 4096)), centroids=w),
+            range(0, T, 4096))))
+        dy = np.concatenate(list(ex.map(
+            lambda r0: W.gen_dy(wl, rows=slice(r0, min(T, r0 + 4096))), range(0, T, 4096))))
+        W1 = list(ex.map(lambda e: W.gen_w1(wl, e), range(E)))
+        W2 = list(ex.map(lambda e: W.gen_w2(wl, e), range(E)))
+    dev = {"h": to_dev(h, wl.dtype), "w": to_dev(w, wl.dtype), "dy": to_dev(dy, wl.dtype)}
+    dev["W1"] = torch.empty((E, wl.F, wl.D), dtype=torch.bfloat16, device="cuda")
+    dev["W2"] = torch.empty((E, wl.D, wl.F), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        dev["W1"][e].copy_(to_dev(W1[e], wl.dtype))
+        dev["W2"][e].copy_(to_dev(W2[e], wl.dtype))
+    lnp = [W.gen_ln(wl, n) for n in range(2)]
+    gam = np.stack([g for g, _ in lnp])
+    bet = np.stack([b for _, b in lnp])
+    yield dict(wl=wl, h=h, w=w, dy=dy, W1=W1, W2=W2, dev=dev, gam=gam, bet=bet)
+    del dev
+    torch.cuda.empty_cache()
+
+
+def _blocks(d, N):
+    W1 = d["dev"]["W1"][None].expand(N, *d["dev"]["W1"].shape).contiguous()
+    W2 = d["dev"]["W2"][None].expand(N, *d["dev"]["W2"].shape).contiguous()
+    return W1, W2
+
+
+def test_full_layer_two_blocks_convex(large):
+    d, wl = large, large["wl"]
+    T = wl.T
+    W1n, W2n = _blocks(d, 2)
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=500 * T)
+    r = api.base_layer_forward_ex(d["dev"]["h"], d["dev"]["w"], W1n, W2n, api.BASE_ACT_GELU,
+                                  api.BASE_ROUTE_BALANCED, c, mix=api.BASE_MIX_CONVEX,
+                                  sublayers=2, ln_gamma=torch.from_numpy(d["gam"]).cuda(),
+                                  ln_beta=torch.from_numpy(d["bet"]).cuda())
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    del W1n, W2n
+    a = r["assign"].cpu().numpy()
+    assert (np.bincount(a, minlength=wl.E) == T // wl.E).all()
+    rows = np.nonzero(np.isin(a, EXPERTS))[0]
+    s = np.empty((T, wl.E))
+    s[rows] = r["scores"][torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    ref = oracle.layer_forward_ex(
+        f64(d["h"], wl.dtype), f64(d["w"], wl.dtype), lambda n, e: f64(d["W1"][e], wl.dtype),
+        lambda n, e: f64(d["W2"][e], wl.dtype), a, wl.act, mix="convex", sublayers=2,
+        gamma=d["gam"], beta=d["bet"], ln_eps=1e-5, experts=EXPERTS, s=s)
+    got = dev_to_f64(r["out"][torch.from_numpy(rows).cuda()])
+    assert rel_err(got, ref[rows]) <= 2e-2
+
+
+def test_full_block_backward_convex(large):
+    d, wl = large, large["wl"]
+    T, E = wl.T, wl.E
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=500 * T)
+    fwd = api.base_layer_forward(d["dev"]["h"], d["dev"]["w"], d["dev"]["W1"], d["dev"]["W2"],
+                                 api.BASE_ACT_GELU, api.BASE_ROUTE_BALANCED, c)
+    torch.cuda.synchronize()
+    assert api.read_stats(fwd["stats"]).status == 0
+    W1n, W2n = _blocks(d, 1)
+    r = api.base_layer_backward_ex(d["dev"]["h"], d["dev"]["w"], W1n, W2n, api.BASE_ACT_GELU,
+                                   fwd["assign"], fwd["scores"], d["dev"]["dy"],
+                                   mix=api.BASE_MIX_CONVEX, sublayers=1,
+                                   ln_gamma=torch.from_numpy(d["gam"][:1]).cuda(),
+                                   ln_beta=torch.from_numpy(d["bet"][:1]).cuda())
+    torch.cuda.synchronize()
+    assert api.read_stats(r["stats"]).status == 0
+    del W1n, W2n
+    a = fwd["assign"].cpu().numpy()
+    rows = np.nonzero(np.isin(a, EXPERTS))[0]
+    s = np.empty((T, E))
+    s[rows] = fwd["scores"][torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    dh, dw, dW1, dW2, dga, dbe = oracle.layer_backward_ex(
+        f64(d["h"], wl.dtype), f64(d["w"], wl.dtype), lambda n, e: f64(d["W1"][e], wl.dtype),
+        lambda n, e: f64(d["W2"][e], wl.dtype), a, wl.act, f64(d["dy"], wl.dtype),
+        mix="convex", sublayers=1, gamma=d["gam"][:1], beta=d["bet"][:1], ln_eps=1e-5, s=s,
+        experts=EXPERTS, store="bf16")
+    assert rel_err(dev_to_f64(r["dh"][torch.from_numpy(rows).cuda()]), dh[rows]) <= 2e-2
+    for e in EXPERTS:
+        assert rel_err(dev_to_f64(r["dw"][e]), dw[e]) <= 2e-2, e
+        assert rel_err(dev_to_f64(r["dW1"][0, e]), dW1[(0, e)]) <= 2e-2, e
+        assert rel_err(dev_to_f64(r["dW2"][0, e]), dW2[(0, e)]) <= 2e-2, e
+        assert rel_err(r["dgamma"][0, e].double().cpu().numpy(), dga[(0, e)]) <= 2e-2, e
+        assert rel_err(r["dbeta"][0, e].double().cpu().numpy(), dbe[(0, e)]) <= 2e-2, e
