@@ -376,7 +376,7 @@ const char* base_strerror(int code) {
         case BASE_OK: return "ok";
         case BASE_ERR_INVALID_ARG: return "invalid argument";
         case BASE_ERR_INDIVISIBLE: return "T is not a multiple of E";
-        case BASE_ERR_UNSUPPORTED: return "unsupported by this build";
+        case BASE_ERR_UNSUPPORTED: return "unsupported: outside the library's size or layout limits";
         case BASE_ERR_HIP: return "HIP launch failed";
         case BASE_ERR_NOT_CONVERGED: return "auction stopped at its bid cap";
         case BASE_ERR_NONFINITE: return "no finite affinity";

@@ -458,7 +458,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (every expert resident on one "
+        print("bench.py: this implementation runs on one GPU only (every expert resident on one "
               "MI355X, no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

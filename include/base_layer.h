@@ -55,7 +55,7 @@ typedef enum {
                                     workspace too small */
     BASE_ERR_INDIVISIBLE = -2,   /* T % E != 0 (eq. 2 needs T/E per expert;
                                     the paper leaves this case open) */
-    BASE_ERR_UNSUPPORTED = -3,   /* a valid request this build does not serve */
+    BASE_ERR_UNSUPPORTED = -3,   /* a valid request outside the library's limits */
     BASE_ERR_HIP = -4,           /* a HIP launch or query failed */
     BASE_ERR_NOT_CONVERGED = -5, /* device: the auction hit cfg.max_bids */
     BASE_ERR_NONFINITE = -6,     /* device: no finite affinity at all */
