@@ -316,6 +316,8 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // val(j, q) gives out[j][q] (computed just before its half is staged, so
 // only half a row set of packed values is live at a time).
+constexpr int kCpolNT = 2;  // buffer-instruction cache policy: non-temporal
+
 template <int TN, class Val>
 BASE_DEV void store_rows_staged(char* lds, int lane, int i, Val&& val, buf_rsrc_t dst, int64_t ld,
                                 int64_t ncols) {
@@ -341,7 +343,11 @@ BASE_DEV void store_rows_staged(char* lds, int lane, int i, Val&& val, buf_rsrc_
             const uint4 v = *(const uint4*)(lds + r * 128 + ((c ^ (r & 7)) << 4));
             const int64_t col = 64 * jh + 8 * c;
             const uint32_t off = col < ncols ? (uint32_t)(((32 * i + r) * ld + col) * 2) : kOob;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), dst, (int)off, 0, 0);
+            // non-temporal: these outputs (GBs, read by a later launch) would
+            // otherwise evict the operand panels neighbouring tiles re-read
+            // from L2 (cache-policy bit NT)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), dst, (int)off, 0,
+                                                   kCpolNT);
         }
     }
 }

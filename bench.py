@@ -47,14 +47,14 @@ PHASES = ("affinity", "route", "ffn1", "ffn2")
 TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
                    "balanced_token_expert_amd/csrc/gemm_dma.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99995
+FETCH_SCALE = 1.99994
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "b5b4dc60c52b4abf3566facc22e0df2666b8ce95e29cf77fed6b55d24d90957f",
-             2504683.8, 1179441.2),
-    "ffn2": ("large_t64k_e128_d2048", "b5b4dc60c52b4abf3566facc22e0df2666b8ce95e29cf77fed6b55d24d90957f",
-             2892980.2, 353476.9),
+    "ffn1": ("large_t64k_e128_d2048", "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d",
+             2504542.3, 1181884.7),
+    "ffn2": ("large_t64k_e128_d2048", "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d",
+             2918153.5, 353082.8),
 }
 
 
