@@ -32,6 +32,9 @@ CASES = [
          asg="balanced"),
     dict(T=1000, E=5, D=264, F=200, dtype="bf16", act="gelu", kind="iid", mix=0, asg="empty"),
     dict(T=3000, E=3, D=136, F=784, dtype="bf16", act="relu", kind="skew", mix=0, asg="ragged"),
+    # one expert holding every token; one token per expert
+    dict(T=700, E=1, D=128, F=200, dtype="bf16", act="gelu", kind="iid", mix=1, asg="balanced"),
+    dict(T=256, E=256, D=64, F=96, dtype="f32", act="relu", kind="iid", mix=0, asg="balanced"),
 ]
 
 
@@ -175,6 +178,11 @@ BLOCK_CASES = [
     # D not a multiple of 8: the row kernels' one-element form
     dict(T=700, E=5, D=100, F=120, dtype="f32", act="gelu", kind="mixture", mix=1, sub=2, ln=True,
          asg="ragged"),
+    # one expert; one token per expert
+    dict(T=640, E=1, D=192, F=256, dtype="bf16", act="gelu", kind="iid", mix=0, sub=2, ln=True,
+         asg="balanced"),
+    dict(T=128, E=128, D=64, F=64, dtype="f32", act="gelu", kind="iid", mix=1, sub=1, ln=True,
+         asg="balanced"),
 ]
 
 
