@@ -32,6 +32,9 @@ CASES = [
     dict(T=512, E=4, D=2056, F=64, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=False),
     dict(T=256, E=2, D=4104, F=32, dtype="bf16", act="gelu", kind="iid", mix=0, sub=2, ln=True),
     dict(T=256, E=2, D=8200, F=32, dtype="bf16", act="relu", kind="iid", mix=1, sub=1, ln=True),
+    # one expert holding every token; one token per expert
+    dict(T=300, E=1, D=128, F=96, dtype="bf16", act="gelu", kind="iid", mix=1, sub=2, ln=True),
+    dict(T=64, E=64, D=64, F=64, dtype="f32", act="relu", kind="iid", mix=0, sub=1, ln=True),
 ]
 MODES = [api.BASE_ROUTE_BALANCED, api.BASE_ROUTE_GIVEN, api.BASE_ROUTE_GREEDY]
 
