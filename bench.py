@@ -201,7 +201,7 @@ def greedy_layer(hd, wd, W1d, W2d, act, T, E, reps=5):
             "largest_group": int(counts.max()), "empty_experts": int((counts == 0).sum())}
 
 
-def layer_variants(wl, hd, wd, W1d, W2d, act, c, reps=5):
+def layer_variants(wl, hd, wd, W1d, W2d, act, c, host=None, reps=5):
     """base_layer_forward_ex on the same inputs and balanced routing: the
     released code's convex mix with plain experts, and experts of one and two
     sec. 4.1 blocks (layer norm, up, activation, down, residual). Block 0
@@ -246,17 +246,29 @@ def layer_variants(wl, hd, wd, W1d, W2d, act, c, reps=5):
         tot = [ev.ms(6 * i, 6 * i + 4) for i in range(reps)]
         exp = [ev.ms(6 * i + 2, 6 * i + 4) for i in range(reps)]
         st = api.read_stats(bufs["stats"])
+        xt = 2.0 * 2 * T * D * F * max(kw["sublayers"], 1) / (np.median(exp) * 1e-3) / 1e12
         res[name] = {"ms": round(float(np.median(tot)), 4),
                      "tokens_per_s": round(T / (np.median(tot) * 1e-3), 1),
                      "expert_ms": round(float(np.median(exp)), 4),
-                     "expert_tflops": round(2.0 * 2 * T * D * F * max(kw["sublayers"], 1)
-                                            / (np.median(exp) * 1e-3) / 1e12, 1),
+                     "expert_tflops": round(xt, 1),
+                     "expert_frac_bf16_peak": round(xt / PEAK_BF16_TFLOPS, 4),
                      "status": st.status}
+        if host is not None and name == "convex_blocks2_ln":
+            import oracle
+            a = bufs["assign"].cpu().numpy()
+            s = bufs["scores"].cpu().numpy().astype(np.float64)
+            n_tok = int(np.isin(a, ORACLE_EXPERTS).sum())
+            g2, b2 = gam.cpu().numpy(), bet.cpu().numpy()
+            res[name]["cpu_oracle"] = oracle_leg(lambda: oracle.layer_forward_ex(
+                host["h64"], host["w64"], lambda n, e: W.as_f64(host["W1"][e], wl.dtype),
+                lambda n, e: W.as_f64(host["W2"][e], wl.dtype), a, wl.act, mix="convex",
+                sublayers=2, gamma=g2, beta=b2, ln_eps=1e-5, experts=list(ORACLE_EXPERTS),
+                s=s), n_tok, "fp64 layer with two layer-norm blocks (convex)")
     del W1x2, W2x2
     return res
 
 
-def layer_backward(wl, hd, wd, W1d, W2d, act, lay, reps=5):
+def layer_backward(wl, hd, wd, W1d, W2d, act, lay, host=None, reps=5):
     """base_layer_backward on the same inputs, with the assignment and the
     scores of the last balanced forward step and a seeded upstream gradient
     (eq. 1's residual mix). Median ms of the whole call and of its phases
@@ -292,14 +304,26 @@ def layer_backward(wl, hd, wd, W1d, W2d, act, lay, reps=5):
     flop = 2.0 * T * D * F
     st = api.read_stats(out["stats"])
     del out
+    cpu = None
+    if host is not None:
+        import oracle
+        a = lay["assign"].cpu().numpy()
+        s = lay["scores"].cpu().numpy().astype(np.float64)
+        n_tok = int(np.isin(a, ORACLE_EXPERTS).sum())
+        cpu = oracle_leg(lambda: oracle.layer_backward(
+            host["h64"], host["w64"], lambda e: W.as_f64(host["W1"][e], wl.dtype),
+            lambda e: W.as_f64(host["W2"][e], wl.dtype), a, wl.act, W.as_f64(dy, wl.dtype),
+            s=s, experts=list(ORACLE_EXPERTS)), n_tok, "fp64 gradients of the layer (residual)")
     return {"ms": round(tot, 4), "tokens_per_s": round(T / (tot * 1e-3), 1),
             "tflops": round(5 * flop / (tot * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(5 * flop / (tot * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "cpu_oracle": cpu,
             "phase_ms": {k: round(v, 4) for k, v in ph.items()},
             "phase_tflops": {k: round(flop / (v * 1e-3) / 1e12, 1) for k, v in ph.items()},
             "mix": "residual", "status": st.status}
 
 
-def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, reps=3):
+def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, host=None, reps=3):
     """base_layer_backward_ex with experts of one and two sec. 4.1 blocks
     (layer norm, up, activation, down, residual; the convex mix), on the
     assignment and scores of the last balanced forward step; the blocks reuse
@@ -348,11 +372,24 @@ def layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, reps=3):
         res[f"convex_blocks{N}_ln"] = {
             "ms": round(tot, 4), "tokens_per_s": round(T / (tot * 1e-3), 1),
             "products": 6 * N, "tflops": round(6 * N * flop / (tot * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(6 * N * flop / (tot * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "phase_ms": {k: round(v, 4) for k, v in ph.items()},
             "blocks_back_tflops": round(4 * N * flop / (ph["blocks_back"] * 1e-3) / 1e12, 1),
             "status": st.status}
         del out, W1n, W2n
         torch.cuda.empty_cache()
+    if host is not None:
+        import oracle
+        a = lay["assign"].cpu().numpy()
+        s = lay["scores"].cpu().numpy().astype(np.float64)
+        n_tok = int(np.isin(a, ORACLE_EXPERTS).sum())
+        g1, b1 = gam[:1].cpu().numpy(), bet[:1].cpu().numpy()
+        res["convex_blocks1_ln"]["cpu_oracle"] = oracle_leg(lambda: oracle.layer_backward_ex(
+            host["h64"], host["w64"], lambda n, e: W.as_f64(host["W1"][e], wl.dtype),
+            lambda n, e: W.as_f64(host["W2"][e], wl.dtype), a, wl.act, W.as_f64(dy, wl.dtype),
+            mix="convex", sublayers=1, gamma=g1, beta=b1, ln_eps=1e-5, s=s,
+            experts=list(ORACLE_EXPERTS), store="bf16"), n_tok,
+            "fp64 gradients of one layer-norm block (convex)")
     return res
 
 
@@ -401,6 +438,21 @@ def auction_solve(reps=10):
             "balanced": balanced, "dual_gap": gap, "dual_gap_bound": T * wl.eps_end,
             "cpu_oracle_ms": round(1e3 * t_cpu, 2), "cpu_oracle_cores": 1,
             "last_solve": solve_rates(times[-1], st, T, E)}
+
+
+ORACLE_EXPERTS = tuple(range(8))
+
+
+def oracle_leg(fn, tokens, what):
+    """The oracle as it stands, timed on the host for a bounded sample (the
+    tokens of eight experts), as tokens/s: the CPU reference beside a GPU leg."""
+    t0 = time.perf_counter()
+    fn()
+    sec = time.perf_counter() - t0
+    return {"value": round(tokens / sec, 1), "unit": "tokens/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{what}, the {tokens} tokens of experts {list(ORACLE_EXPERTS)}",
+            "seconds": round(sec, 2)}
 
 
 def solve_rates(ms, st, T, E):
@@ -567,11 +619,14 @@ def main():
                            "uniform_share": round(1.0 / E, 5)},
            "roofline": roof, "wall_s_timed": round(wall, 3)}
     res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
+    host = None
+    if not args.no_cpu_baseline:  # the oracle beside each GPU leg, on eight experts' tokens
+        host = {"h64": W.as_f64(h, wl.dtype), "w64": W.as_f64(w, wl.dtype), "W1": W1, "W2": W2}
     if not args.no_backward:
-        res["layer_backward"] = layer_backward(wl, hd, wd, W1d, W2d, act, lay)
-        res["layer_backward_blocks"] = layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay)
+        res["layer_backward"] = layer_backward(wl, hd, wd, W1d, W2d, act, lay, host)
+        res["layer_backward_blocks"] = layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, host)
     if not args.no_variants:
-        res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c)
+        res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c, host)
     if not args.no_auction:
         res["auction_solve_ms"] = auction_solve()
     if not args.no_cpu_baseline:
