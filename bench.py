@@ -500,7 +500,7 @@ def copy_probe(nbytes=1 << 30, reps=4):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=5, help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
