@@ -128,7 +128,7 @@ hipError_t launch_greedy(const float* s, int64_t T, int64_t E, const ScoreScan* 
 
 // ---------------------------------------------------------------- perm
 
-constexpr int kPermChunk = 4096;  // tokens per block
+constexpr int kPermChunk = 512;  // tokens per block (128 blocks at 65536 tokens)
 constexpr int kPermThreads = 256;
 
 size_t perm_ws_bytes(int64_t T, int64_t E) {
@@ -158,53 +158,58 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(const int32_t* 
     for (int64_t e = threadIdx.x; e < E; e += blockDim.x) cnt[blockIdx.x * E + e] = hist[e];
 }
 
-// one block: base[b*E+e] = offsets[e] + sum_{b'<b} cnt[b'*E+e]; offsets, counts
+// one block: base[b*E+e] = offsets[e] + sum_{b'<b} cnt[b'*E+e], i.e. the
+// exclusive prefix sum of the counts taken in (expert, block) order; then
+// offsets[e] = base[e] (block 0), counts[e] = offsets[e+1] - offsets[e]. Each
+// thread sums a contiguous run of that order, the runs' sums are scanned
+// across the block (wave prefix sums, then the 16 wave totals), and each
+// thread writes its run's bases.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* cnt, int64_t nb, int64_t E,
                                                          int64_t T, int32_t* base, int32_t* offsets,
                                                          int32_t* counts, int64_t want_k,
-                                                         int32_t* status, int32_t* tot) {
-    __shared__ int32_t part[1024];
-    // per-expert totals (and the running per-block prefix kept in base)
-    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t run = 0;
-        for (int64_t b = 0; b < nb; ++b) {
-            base[b * E + e] = run;
-            run += cnt[b * E + e];
+                                                         int32_t* status) {
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = nb * E;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t i0 = min(n, (int64_t)tid * per), i1 = min(n, i0 + per);
+    auto at = [&](int64_t i) -> int64_t { return (i % nb) * E + i / nb; };  // i = e nb + b
+    int32_t own = 0;
+    for (int64_t i = i0; i < i1; ++i) own += cnt[at(i)];
+    int32_t v = own;  // inclusive prefix over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int32_t x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int32_t u = __shfl_up(x, o, 64);
+            if (lane >= o) x += u;
         }
-        tot[e] = run;
-        if (counts) counts[e] = run;
-        if (want_k > 0 && run != want_k && status) *status = kStatusUnbalanced;
+        if (lane < 16) wsum[lane] = x;
     }
     __syncthreads();
-    // exclusive scan of tot over e: each thread sums a contiguous slice
-    const int64_t per = (E + blockDim.x - 1) / blockDim.x;
-    const int64_t e0 = threadIdx.x * per, e1 = min(E, e0 + per);
-    int32_t sum = 0;
-    for (int64_t e = e0; e < e1; ++e) sum += tot[e];
-    part[threadIdx.x] = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t run = 0;
-        for (unsigned i = 0; i < blockDim.x; ++i) {
-            int32_t v = part[i];
-            part[i] = run;
-            run += v;
-        }
+    int32_t run = v - own + (wave > 0 ? wsum[wave - 1] : 0);
+    for (int64_t i = i0; i < i1; ++i) {
+        const int64_t j = at(i);
+        const int32_t c = cnt[j];
+        base[j] = run;
+        run += c;
     }
     __syncthreads();
-    int32_t run = part[threadIdx.x];
-    for (int64_t e = e0; e < e1; ++e) {
-        int32_t v = tot[e];
-        tot[e] = run;  // now the exclusive offset
-        if (offsets) offsets[e] = run;
-        run += v;
+    for (int64_t e = tid; e < E; e += blockDim.x) {
+        const int32_t off = base[e];
+        const int32_t next = e + 1 < E ? base[e + 1] : (int32_t)T;
+        if (offsets) offsets[e] = off;
+        if (counts) counts[e] = next - off;
+        if (want_k > 0 && next - off != want_k && status) *status = kStatusUnbalanced;
     }
-    if (threadIdx.x == 0 && offsets) offsets[E] = (int32_t)T;
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
-        const int32_t off = tot[e];
-        for (int64_t b = 0; b < nb; ++b) base[b * E + e] += off;
-    }
+    if (tid == 0 && offsets) offsets[E] = (int32_t)T;
 }
 
 // block b: stable placement of its chunk. Tokens are taken 256 at a time in
@@ -259,11 +264,10 @@ hipError_t launch_perm(const int32_t* assign, int64_t T, int64_t E, int32_t* per
     const int64_t nb = (T + kPermChunk - 1) / kPermChunk;
     int32_t* cnt = (int32_t*)ws;
     int32_t* base = cnt + nb * E;
-    int32_t* tot = base + nb * E;
     hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nb), dim3(kPermThreads), E * sizeof(int32_t),
                        st, assign, T, E, cnt, status);
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, nb, E, T, base, offsets,
-                       counts, want_k, status, tot);
+                       counts, want_k, status);
     hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)nb), dim3(kPermThreads),
                        5 * E * sizeof(int32_t), st, assign, T, E, base, perm);
     return hipGetLastError();
