@@ -130,6 +130,7 @@ hipError_t launch_greedy(const float* s, int64_t T, int64_t E, const ScoreScan* 
 
 constexpr int kPermChunk = 512;  // tokens per block (128 blocks at 65536 tokens)
 constexpr int kPermThreads = 256;
+constexpr int kScanLds = 32768;  // per-block counts the scan stages in LDS (128 KB)
 
 size_t perm_ws_bytes(int64_t T, int64_t E) {
     int64_t nb = (T + kPermChunk - 1) / kPermChunk;
@@ -169,13 +170,29 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* cnt, int
                                                          int32_t* counts, int64_t want_k,
                                                          int32_t* status) {
     __shared__ int32_t wsum[16];
+    __shared__ int32_t sc[kScanLds];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = nb * E;
+    // the counts come into LDS with coalesced loads when they fit, so the two
+    // strided passes below read LDS instead of waiting on L2 per element
+    const bool staged = n <= kScanLds;
+    if (staged) {
+        for (int64_t j = tid; j < n; j += blockDim.x) sc[j] = cnt[j];
+        __syncthreads();
+    }
+    auto get = [&](int64_t j) -> int32_t { return staged ? sc[j] : cnt[j]; };
     const int64_t per = (n + 1023) / 1024;
     const int64_t i0 = min(n, (int64_t)tid * per), i1 = min(n, i0 + per);
-    auto at = [&](int64_t i) -> int64_t { return (i % nb) * E + i / nb; };  // i = e nb + b
+    // i = e nb + b; the run starts at (e0, b0) and steps b, then e
+    const int64_t e0 = i0 / nb, b0 = i0 % nb;
     int32_t own = 0;
-    for (int64_t i = i0; i < i1; ++i) own += cnt[at(i)];
+    {
+        int64_t e = e0, b = b0;
+        for (int64_t i = i0; i < i1; ++i) {
+            own += get(b * E + e);
+            if (++b == nb) { b = 0; ++e; }
+        }
+    }
     int32_t v = own;  // inclusive prefix over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -195,11 +212,15 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* cnt, int
     }
     __syncthreads();
     int32_t run = v - own + (wave > 0 ? wsum[wave - 1] : 0);
-    for (int64_t i = i0; i < i1; ++i) {
-        const int64_t j = at(i);
-        const int32_t c = cnt[j];
-        base[j] = run;
-        run += c;
+    {
+        int64_t e = e0, b = b0;
+        for (int64_t i = i0; i < i1; ++i) {
+            const int64_t j = b * E + e;
+            const int32_t c = get(j);
+            base[j] = run;
+            run += c;
+            if (++b == nb) { b = 0; ++e; }
+        }
     }
     __syncthreads();
     for (int64_t e = tid; e < E; e += blockDim.x) {
