@@ -89,40 +89,66 @@ hipError_t launch_scan_scores(const float* s, int64_t n, ScoreScan* scan, hipStr
 
 // ---------------------------------------------------------------- greedy
 
+// 16 lanes per token (4 tokens per wave): lane j of a token's group reads
+// experts j, j + 16, ... (with VEC, 4 consecutive experts from 4 j, 4 j + 64,
+// ...), keeps the largest value and its lowest index, and the group merges
+// its 16 candidates with xor shuffles (larger value, then lower index, wins).
+template <bool VEC>
 __global__ __launch_bounds__(256) void greedy_kernel(const float* s, int64_t T, int64_t E,
                                                      const ScoreScan* scan, int32_t* assign) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int lane = threadIdx.x & 63, sub = lane & 15;
+    const int64_t grp = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const int64_t ngrp = ((int64_t)gridDim.x * blockDim.x) >> 4;
     const bool fix = scan->nonfinite != 0;
     const float repl = scan->min_key == 0xffffffffu ? 0.0f : f32_unkey(scan->min_key);
-    for (int64_t t = wave; t < T; t += nwaves) {
-        const float* row = s + t * E;
+    // every group of the wave runs the same number of iterations, so the
+    // shuffles below always see all 64 lanes active
+    const int64_t iters = (T + ngrp - 1) / ngrp;
+    for (int64_t it = 0; it < iters; ++it) {
+        const int64_t t = grp + it * ngrp;
         float best = 0.0f;
         int bi = 0x7fffffff;
-        for (int64_t e = lane; e < E; e += 64) {
-            float v = row[e];
+        auto take = [&](float v, int e) {
             if (fix && !is_finite_f32(v)) v = repl;
-            if (bi == 0x7fffffff || v > best) { best = v; bi = (int)e; }
+            if (bi == 0x7fffffff || v > best) { best = v; bi = e; }
+        };
+        if (t < T) {
+            const float* row = s + t * E;
+            if (VEC) {
+                for (int64_t e = 4 * sub; e < E; e += 64) {
+                    const float4 v = *(const float4*)(row + e);
+                    take(v.x, (int)e);
+                    take(v.y, (int)e + 1);
+                    take(v.z, (int)e + 2);
+                    take(v.w, (int)e + 3);
+                }
+            } else {
+                for (int64_t e = sub; e < E; e += 16) take(row[e], (int)e);
+            }
         }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(best, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
+        for (int o = 8; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
             if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > best || (ov == best && oi < bi))) {
                 best = ov;
                 bi = oi;
             }
         }
-        if (lane == 0) assign[t] = bi;
+        if (sub == 0 && t < T) assign[t] = bi;
     }
 }
 
 hipError_t launch_greedy(const float* s, int64_t T, int64_t E, const ScoreScan* scan,
                          int32_t* assign, int32_t* /*counts*/, hipStream_t st) {
-    int64_t blocks = (T + 3) / 4;
+    int64_t blocks = (T + 15) / 16;  // 16 tokens per 256-thread block at once
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, T, E, scan, assign);
+    if (E % 64 == 0 && ((uintptr_t)s & 15) == 0)
+        hipLaunchKernelGGL(greedy_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, s, T, E,
+                           scan, assign);
+    else
+        hipLaunchKernelGGL(greedy_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, s, T, E,
+                           scan, assign);
     return hipGetLastError();
 }
 
