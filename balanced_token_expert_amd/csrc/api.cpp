@@ -440,6 +440,9 @@ int base_route_greedy(const float* scores, int64_t T, int64_t E, int32_t* assign
     if (!scores || !assign || T <= 0 || E <= 0) return BASE_ERR_INVALID_ARG;
     if ((perm == nullptr) != (offsets == nullptr)) return BASE_ERR_INVALID_ARG;
     if (T > kMaxT || E > kMaxT) return BASE_ERR_UNSUPPORTED;
+    // counts and the grouping come from the grouping kernels, whose LDS
+    // tables hold E entries: refuse before anything is enqueued
+    if ((counts || perm) && E > kPermMaxE) return BASE_ERR_UNSUPPORTED;
     const Layout L = layout(BASE_OP_GREEDY, T, E, 0, 0, 0);
     if (!ws || ws_bytes < L.total) return BASE_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;

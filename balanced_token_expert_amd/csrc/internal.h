@@ -143,6 +143,9 @@ hipError_t launch_scan_scores(const float* s, int64_t n, ScoreScan* scan,
 hipError_t launch_greedy(const float* s, int64_t T, int64_t E,
                          const ScoreScan* scan, int32_t* assign,
                          int32_t* counts, hipStream_t st);
+// largest expert count the grouping kernels take (their per-block LDS holds
+// five E-entry tables)
+constexpr int64_t kPermMaxE = 4096;
 size_t perm_ws_bytes(int64_t T, int64_t E);
 // Stable grouping of tokens by expert. If want_k > 0 also checks that every
 // expert holds exactly want_k tokens and all ids are in range, else sets

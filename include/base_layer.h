@@ -175,6 +175,10 @@ int base_assign_auction(const float *scores, int64_t T, int64_t E,
  *   offsets go together).
  *   ws: scratch of base_workspace_bytes(BASE_OP_GREEDY, ...).
  * T % E need not be 0.
+ * Errors: INVALID_ARG (null scores/assign, sizes <= 0, perm without
+ *   offsets, workspace too small); UNSUPPORTED for T or E above 2^24, and
+ *   for E above 4096 when counts or perm is asked for (the grouping keeps
+ *   per-expert tables in on-chip memory); nothing is enqueued then.
  */
 int base_route_greedy(const float *scores, int64_t T, int64_t E,
                       int32_t *assign, int32_t *counts, int32_t *perm,

@@ -44,3 +44,4 @@ def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
 
 def dev_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
+

@@ -113,6 +113,14 @@ def test_greedy_and_affinity_host_errors(lib):
                                  None) == api.BASE_ERR_INVALID_ARG   # perm without offsets
     assert lib.base_route_greedy(FAKE, 12, 3, FAKE, None, None, None, FAKE, 8,
                                  None) == api.BASE_ERR_INVALID_ARG   # workspace too small
+    # more experts than the grouping kernels hold: refused on the host when
+    # counts or the grouping are asked for (nothing is launched)
+    big = api.base_workspace_bytes(api.BASE_OP_GREEDY, 8192, 8192, 0, 0, 0)
+    assert big > 0
+    assert lib.base_route_greedy(FAKE, 8192, 8192, FAKE, FAKE, None, None, FAKE, big,
+                                 None) == api.BASE_ERR_UNSUPPORTED   # counts
+    assert lib.base_route_greedy(FAKE, 8192, 8192, FAKE, None, FAKE, FAKE, FAKE, big,
+                                 None) == api.BASE_ERR_UNSUPPORTED   # perm + offsets
     assert lib.base_affinity(FAKE, FAKE, None, 12, 3, 8, 1, None) == api.BASE_ERR_INVALID_ARG
     assert lib.base_affinity(FAKE, FAKE, FAKE, 12, 3, 12, 1, None) == api.BASE_ERR_UNSUPPORTED
     assert lib.base_affinity(FAKE, FAKE, FAKE, 12, 3, 8, 4, None) == api.BASE_ERR_INVALID_ARG

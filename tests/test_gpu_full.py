@@ -86,8 +86,8 @@ def _check_assignment(wl, s32, a, perm=None, offsets=None):
 
 def test_full_tiny_fp32_everything():
     """T=512, E=8, D=64, F=256 fp32 ReLU: affinities, the auction against the
-    Hungarian optimum (bit-exact when eps is below the gap over T), greedy
-    routing and every output row."""
+    Hungarian optimum (within T * eps_end), greedy routing and every output
+    row."""
     wl = W.workload(1)
     host = _gen(wl)
     dev = {k: to_dev(v, wl.dtype) for k, v in host.items()}
@@ -101,10 +101,10 @@ def test_full_tiny_fp32_everything():
     a = r["assign"].cpu().numpy()
     _check_assignment(wl, s32, a, r["perm"].cpu().numpy(), None)
     s = s32.astype(np.float64)
-    exact = oracle.hungarian(s)
-    gap = oracle.min_cycle_gap(s, exact)
-    if gap > wl.T * wl.eps_end:
-        assert (a == exact).all()
+    # within T * eps_end of the Hungarian optimum (exactness below the gap is
+    # tests/test_gpu_exact.py's, with eps_end set from the gap)
+    opt = oracle.objective(s, oracle.hungarian(s))
+    assert oracle.objective(s, a) >= opt - wl.T * wl.eps_end - 1e-9 * abs(opt)
     ga, gc = oracle.greedy_route(s)
     assert (g["assign"].cpu().numpy() == ga).all() and (g["counts"].cpu().numpy() == gc).all()
     ref = oracle.layer_forward(f64(host["h"], wl.dtype), f64(host["w"], wl.dtype),

@@ -105,7 +105,7 @@ def test_full_block_backward_convex(large):
         f64(d["h"], wl.dtype), f64(d["w"], wl.dtype), lambda n, e: f64(d["W1"][e], wl.dtype),
         lambda n, e: f64(d["W2"][e], wl.dtype), a, wl.act, f64(d["dy"], wl.dtype),
         mix="convex", sublayers=1, gamma=d["gam"][:1], beta=d["bet"][:1], ln_eps=1e-5, s=s,
-        experts=EXPERTS, store="bf16")
+        experts=EXPERTS)
     assert rel_err(dev_to_f64(r["dh"][torch.from_numpy(rows).cuda()]), dh[rows]) <= 2e-2
     for e in EXPERTS:
         assert rel_err(dev_to_f64(r["dw"][e]), dw[e]) <= 2e-2, e

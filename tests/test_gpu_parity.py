@@ -356,10 +356,6 @@ def test_host_errors():
     with pytest.raises(api.BaseError) as ei:
         api.base_assign_auction(s, api.cfg(), ws=torch.empty(8, dtype=torch.uint8, device="cuda"))
     assert ei.value.code == api.BASE_ERR_INVALID_ARG
-    h = torch.zeros((12, 8), dtype=torch.bfloat16, device="cuda")
-    w = torch.zeros((3, 8), dtype=torch.bfloat16, device="cuda")
-    W1 = torch.zeros((3, 16, 8), dtype=torch.bfloat16, device="cuda")
-    W2 = torch.zeros((3, 8, 16), dtype=torch.bfloat16, device="cuda")
 
 
 

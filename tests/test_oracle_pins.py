@@ -300,6 +300,55 @@ def test_auction_certificates(kind):
         assert Dv >= opt - 1e-9  # weak duality
 
 
+def test_eps_cs_violation_hand_cases():
+    """Hand-derived values (dyadic numbers, so every difference is exact).
+    s = [[1, 1/4], [1/2, 1]], p = [1/2, 0]: the values s - p are
+    [[1/2, 1/4], [0, 1]].
+      a = [0, 1]: each token holds its best expert -> 0.
+      a = [1, 0]: token 0 gives up 1/2 - 1/4 = 1/4, token 1 gives up
+                  1 - 0 = 1 -> the largest shortfall, 1.
+      a = [1, 1]: token 0's 1/4 only -> 1/4 (balance is not required).
+    A 3 x 3 case with prices that make the second expert the best for the
+    first token: s = [[2, 1.75, 0], [0, 1, 0.5], [0.25, 0, 1]],
+    p = [0.5, 0, 0]: values [[1.5, 1.75, 0], [-0.5, 1, 0.5], [0.25, 0, 1]];
+    a = [0, 1, 2] -> token 0 gives up 1.75 - 1.5 = 0.25, the others 0 -> 0.25;
+    a = [0, 2, 1] -> token 1 gives up 1 - 0.5 = 0.5, token 2 gives up
+    1 - 0 = 1 -> 1."""
+    s = np.array([[1.0, 0.25], [0.5, 1.0]])
+    p = np.array([0.5, 0.0])
+    assert oracle.eps_cs_violation(s, np.array([0, 1]), p) == 0.0
+    assert oracle.eps_cs_violation(s, np.array([1, 0]), p) == 1.0
+    assert oracle.eps_cs_violation(s, np.array([1, 1]), p) == 0.25
+    s3 = np.array([[2.0, 1.75, 0.0], [0.0, 1.0, 0.5], [0.25, 0.0, 1.0]])
+    p3 = np.array([0.5, 0.0, 0.0])
+    assert oracle.eps_cs_violation(s3, np.array([0, 1, 2]), p3) == 0.25
+    assert oracle.eps_cs_violation(s3, np.array([0, 2, 1]), p3) == 1.0
+    # prices shift every value of a column: raising p_1 by 1/2 makes expert
+    # 0 token 0's best again (1.5 vs 1.25) -> 0
+    assert oracle.eps_cs_violation(s3, np.array([0, 1, 2]), p3 + [0, 0.5, 0]) == 0.0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_eps_cs_violation_against_duality_gap(seed):
+    """For a balanced assignment a and any prices p, the per-token
+    shortfalls max_e (s[t,e] - p_e) - (s[t,a_t] - p_{a_t}) sum to
+    D(p) - sum_t s[t,a_t] (sum_t p_{a_t} = k sum_e p_e). So the largest
+    shortfall lies between that gap / T and the gap itself -- a check
+    through dual_value and objective, which share no code with it."""
+    rng = np.random.default_rng(50 + seed)
+    T, E = 24, 4
+    s = rng.standard_normal((T, E))
+    p = rng.standard_normal(E)
+    a = rng.permutation(np.repeat(np.arange(E), T // E))
+    gap = oracle.dual_value(s, p, T // E) - oracle.objective(s, a)
+    v = oracle.eps_cs_violation(s, a, p)
+    assert gap >= 0
+    assert gap / T - 1e-12 <= v <= gap + 1e-12
+    # an optimal assignment with the auction's prices satisfies eps-CS
+    r = oracle.auction(s, 1.0, 1e-6)
+    assert 0.0 <= oracle.eps_cs_violation(s, r["assign"], r["prices"]) <= 1e-6 * (1 + 1e-9)
+
+
 def test_auction_bid_cap_reports_error():
     s = np.random.default_rng(7).standard_normal((64, 4))
     with pytest.raises(oracle.OracleError) as ei:
