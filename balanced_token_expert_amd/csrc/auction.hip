@@ -23,13 +23,11 @@
 //     prices at once (one wave per token, wave-level max/second-max); then one
 //     workgroup per expert keeps the k best of its holders and new bidders
 //     (bitonic sort in LDS) and returns the rest to the bidder list.
-//   tail (one persistent workgroup): once few tokens are left, each wave
-//     follows a displacement chain -- bid, take the expert's lock in LDS,
-//     evict its lowest holder, continue with the evicted token. Prices,
-//     counts and, per expert, a sorted list of its L lowest holders live in
-//     LDS, so a step needs one score-row load (often from an LDS cache) plus
-//     LDS work; the list is rebuilt from the expert's slots in global memory
-//     only when it runs dry.
+//   tail (one persistent workgroup): once few tokens are left, the rest of
+//     the phase is finished by shortest augmenting paths on the graph whose
+//     nodes are the experts (auction_tail.h): a token's displacement chain
+//     becomes one path search, and the prices rise in one step by the
+//     amounts the chain would have added bid by bid.
 // Prices and bids are fp64: exactness needs eps below gap/T, far below fp32
 // resolution at prices of order one.
 #include <float.h>
@@ -53,12 +51,6 @@ constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
 constexpr int32_t kNoTok = 0x7fffffff;
 
-// lowest-holder list length per expert (LDS budget of the tail; at most 64,
-// one entry per lane). A longer list means fewer rebuilds from the slots.
-static int low_len(int64_t E) {
-    return E <= 64 ? 64 : (E <= 128 ? 32 : (E <= 256 ? 16 : (E <= 512 ? 8 : 4)));
-}
-
 struct AucCtl {
     int32_t cur;          // bidder list in use (0/1)
     int32_t bulk_done;    // the tail owns the rest of this phase
@@ -77,50 +69,44 @@ struct AucWs {
     double* floor_;    // E   price floors p_e
     double* pi;        // E   prices for the next bulk round
     int32_t* cnt;      // E   holders per expert
-    int32_t* nlow;     // E   entries in the lowest-holder list
-    int32_t* comp;     // E   1 if the list holds every holder
-    double* lowb;      // E*L lowest holders, eviction order: bid
-    int32_t* lowt;     // E*L                                 token
-    int32_t* lows;     // E*L                                 slot
     int32_t* list0;    // T
     int32_t* list1;    // T
     int32_t* bexp;     // T   bid of token t: expert
     double* bval;      // T   bid of token t: amount
-    int32_t* stok;     // E*k slot tokens
+    int32_t* stok;     // E*k slot tokens (slots 0 .. cnt-1 of each expert are held)
     double* sbid;      // E*k slot bids
-    int L;
+    int32_t* slot_of;  // T   slot of each held token (tail)
+    double* C;         // E*E tail: cheapest move of a holder of a to b
+    int32_t* Ct;       // E*E tail: the holder that makes it
+    unsigned long long* stale;  // E*ceil(E/64) tail: C entries whose holder left
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 static AucWs carve(void* ws, int64_t T, int64_t E) {
     char* p = (char*)ws;
-    const int L = low_len(E);
     AucWs w;
-    w.L = L;
     w.ctl = (AucCtl*)p; p += align256(sizeof(AucCtl));
     w.floor_ = (double*)p; p += align256(E * 8);
     w.pi = (double*)p; p += align256(E * 8);
     w.cnt = (int32_t*)p; p += align256(E * 4);
-    w.nlow = (int32_t*)p; p += align256(E * 4);
-    w.comp = (int32_t*)p; p += align256(E * 4);
-    w.lowb = (double*)p; p += align256(E * L * 8);
-    w.lowt = (int32_t*)p; p += align256(E * L * 4);
-    w.lows = (int32_t*)p; p += align256(E * L * 4);
     w.list0 = (int32_t*)p; p += align256(T * 4);
     w.list1 = (int32_t*)p; p += align256(T * 4);
     w.bexp = (int32_t*)p; p += align256(T * 4);
     w.bval = (double*)p; p += align256(T * 8);
     w.stok = (int32_t*)p; p += align256(T * 4);
     w.sbid = (double*)p; p += align256(T * 8);
+    w.slot_of = (int32_t*)p; p += align256(T * 4);
+    w.C = (double*)p; p += align256(E * E * 8);
+    w.Ct = (int32_t*)p; p += align256(E * E * 4);
+    w.stale = (unsigned long long*)p; p += align256(E * ((E + 63) / 64) * 8);
     return w;
 }
 
 size_t auction_ws_bytes(int64_t T, int64_t E) {
-    const int L = low_len(E);
-    return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + 3 * align256(E * 4) +
-           align256(E * L * 8) + 2 * align256(E * L * 4) + 4 * align256(T * 4) +
-           2 * align256(T * 8) + 256;
+    return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
+           5 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
+           align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + 256;
 }
 
 // ---------------------------------------------------------------- helpers
@@ -260,8 +246,6 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < E) {
         w.cnt[i] = 0;
-        w.nlow[i] = 0;
-        w.comp[i] = 1;
         w.pi[i] = w.floor_[i];
     }
     if (i == 0) {
@@ -416,21 +400,11 @@ BASE_DEV void block_sort_best(double* cb, int32_t* ct, double* ob, int32_t* ot, 
     }
 }
 
-// An expert's lowest holders in eviction order (slots m-1, m-2, ... of its
-// best-first slots), its count, list state and price.
-BASE_DEV void publish_expert(AucWs& w, int e, int64_t k, int m, const double* hb,
-                             const int32_t* ht) {
-    const int L = w.L;
-    const int nl = min(m, L);
-    for (int i = threadIdx.x; i < nl; i += blockDim.x) {
-        w.lowb[(int64_t)e * L + i] = hb[m - 1 - i];
-        w.lowt[(int64_t)e * L + i] = ht[m - 1 - i];
-        w.lows[(int64_t)e * L + i] = m - 1 - i;
-    }
+// An expert's count and price after a round: the lowest bid it holds once
+// full, else its floor.
+BASE_DEV void publish_expert(AucWs& w, int e, int64_t k, int m, const double* hb) {
     if (threadIdx.x == 0) {
         w.cnt[e] = m;
-        w.nlow[e] = nl;
-        w.comp[e] = (m <= L) ? 1 : 0;
         w.pi[e] = (m == k) ? hb[k - 1] : w.floor_[e];
     }
 }
@@ -453,7 +427,6 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     int32_t* outl = cur ? w.list0 : w.list1;
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int L = w.L;
     int32_t* stok = w.stok + (int64_t)e * k;
     double* sbid = w.sbid + (int64_t)e * k;
 
@@ -574,7 +547,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     if (changed) {
         const int m = nhold;
         for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
-        publish_expert(w, e, k, m, hb, ht);
+        publish_expert(w, e, k, m, hb);
     }
     __syncthreads();
     if (tid == 0) {
@@ -609,9 +582,16 @@ __global__ void auc_finalize_kernel(AucWs w, int64_t E, int64_t k, int32_t* assi
 template <int NCH>
 static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
-                        AucStatsDev* st, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL(auc_tail_kernel<NCH>, dim3(1), dim3(tail_threads(NCH)), lds, stream, s, T, E,
-                       k, w, scan, eps, phase, max_bids, st);
+                        AucStatsDev* st, hipStream_t stream) {
+    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(256), 48 * E, stream, s,
+                       E, k, w, scan);
+    const size_t lds = ssp_lds_bytes(E);
+    if (ssp_c_in_lds(E))
+        hipLaunchKernelGGL((auc_ssp_kernel<NCH, true>), dim3(1), dim3(kSspThreads), lds, stream, s,
+                           T, E, k, w, scan, eps, phase, max_bids, st);
+    else
+        hipLaunchKernelGGL((auc_ssp_kernel<NCH, false>), dim3(1), dim3(kSspThreads), lds, stream,
+                           s, T, E, k, w, scan, eps, phase, max_bids, st);
 }
 
 template <int NCH>
@@ -625,7 +605,6 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     const int rounds = (k > kBulkKMax) ? 0 : (k <= kSmallK ? kBulkRoundsSmallK : kBulkRounds);
     int64_t bid_blocks = (T + 15) / 16;
     if (bid_blocks > 2048) bid_blocks = 2048;
-    const size_t tail_lds = tail_lds_bytes(E, w.L, tail_threads(NCH));
     double eps = eps_start;
     for (int phase = 0;; ++phase) {
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
@@ -638,7 +617,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
                                E, k, w);
         }
-        launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, tail_lds, stream);
+        launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, stream);
         if (eps <= eps_end) break;
         eps = eps / eps_factor;
         if (eps < eps_end) eps = eps_end;

@@ -1,457 +1,700 @@
-// Tail of each eps phase of the auction (included by auction.hip, inside
-// namespace base): one persistent workgroup finishes the displacement chains
-// left after the bulk rounds.
+// End of each eps phase of the auction (included by auction.hip, inside
+// namespace base): the tokens the bulk rounds left unassigned are placed by
+// shortest augmenting paths on the graph whose nodes are the experts.
 //
-// The end of a phase is a long sequence of dependent steps (a token evicts
-// an expert's lowest holder, which bids next, ...). Each wave takes a queued
-// bidder and follows its chain: bid against the current prices (b1 / v1 / v2
-// by wave-wide DPP reductions), take the expert's lock in LDS, compare with
-// its lowest holder, evict it, continue with the evicted token; when the
-// chain ends (a free slot was filled) the wave takes the next queued bidder.
-// A bid made against prices that rose meanwhile is just compared with the
-// expert's current lowest holder: if it no longer beats it, the token bids
-// again. Prices, price floors, holder counts and, per expert, a sorted list
-// of its L lowest holders (bid, token, slot) with a flag telling whether it
-// holds every holder live in LDS, so a step needs no memory round trip
-// except the score row. Slot stores go to global memory; a full expert whose
-// list runs dry rebuilds it from its k slots, after every store issued to
-// that expert has landed (per expert counters: issued under the lock; a wave
-// counts its store as landed at its next step, after its memory wait and
-// before it takes any lock, so waiting for them cannot deadlock). The slots
-// are written and read by this workgroup only, so plain loads (through the
-// CU's own L1 and its XCD's L2) see them.
-// For E <= 128 each expert's lowest holder -- the next token it will evict --
-// has its score row cached in LDS: the wave that makes a token the lowest
-// holder loads its row and publishes it at its next step (under the lock,
-// if that token is still the lowest holder; the tag is cleared first and set
-// last, and a reader checks it before and after reading), so an evicted
-// token usually bids from LDS.
+// Why: near the end of a phase an unassigned token starts a displacement
+// chain -- it evicts a holder, who evicts another, ... -- that ends only at
+// an expert with a free slot. Each step raises one price by the evicted
+// token's margin, often about eps, so a chain that must lift a group of
+// experts by some amount takes about (group size) * amount / eps dependent
+// steps: hundreds to thousands at these sizes. A chain is an augmenting path
+// of the transportation problem behind eq. 2 ("BASE Layers" sec. 3.2.1); the
+// cheapest one, and a price change that keeps every holder
+// eps-complementary-slack after it, come from a shortest-path computation
+// over the E experts (the successive-shortest-path step of min-cost flow,
+// with the auction's prices as node potentials).
+//
+// Graph. For holders t of expert a, moving t to b costs, in reduced terms,
+//   r_t(a,b) = (s[t][a] - p_a) - (s[t][b] - p_b) >= -eps   (eps-CS),
+// so arc a->b gets length w(a,b) = C[a][b] - p_a + p_b + eps >= 0 with
+// C[a][b] = min over holders t of a of s[t][a] - s[t][b] (and Ct[a][b] that
+// holder). D(a) is the length of a shortest path from a to an expert with a
+// free slot (0 at those), computed for all experts at once by Bellman-Ford
+// rounds over a frontier (the experts whose distance just changed); nx(a) is
+// the next expert on it. An unassigned token u
+// enters expert e at cost entry(u,e) = max_e' (s[u][e'] - p_e') -
+// (s[u][e] - p_e) >= 0; its best augmentation enters at the e1 minimising
+// L_u = entry(u,e1) + D(e1) and follows nx to a free slot.
+//
+// Prices. With L the largest L_u among the paths a batch applies, every
+// price drops by max(0, L - D(e)). Each holder's reduced costs stay >= -eps
+// (D(a) <= w(a,b) + D(b) for every arc), each applied path's arcs become
+// tight -- a moved token is eps-CS at its new expert -- and each entering
+// token is exactly CS at e1 (L_u <= entry(u,e) + D(e) for every e). So all
+// paths of a batch are valid under one price change, provided they move
+// distinct tokens and their free slots suffice: paths through a full expert
+// a use its one "out" holder Ct[a][nx(a)], so the applied paths are those,
+// in order of L_u, whose full experts no earlier applied path used and whose
+// free expert still has a slot. The others wait for the next batch.
+//
+// Slots. Counts only grow in the tail (a path's inner experts lose one
+// holder and gain one), so an expert's free slots are always cnt .. k-1 and
+// a moved token takes the slot of the token it displaces.
+//
+// C is maintained lazily. After each batch, one wave per expert the applied
+// paths touched (no two waves share an expert, so no locks) lets every token
+// that joined lower the columns it beats; a column whose cheapest holder
+// left is only marked stale. A stale C[a][b] can only be too small (the
+// minimum over fewer holders), so the distances computed with it still obey
+// D(a) <= w(a,b) + D(b) for the true lengths, which is all the price change
+// needs; what an applied path needs is exact arcs. So the Bellman-Ford
+// rounds never let a row take a stale arc: it is recomputed over its
+// expert's holders first, and the row looks again. When the rounds end, every
+// arc of the tree a -> nx(a) is exact, and then so is D. C and the stale bits
+// live in LDS for E <= 128 (128 KB of fp64), in global memory otherwise.
+// Every loop of the kernel is bounded: a batch places at least one token (its
+// first path in order of L_u is always applied), and a batch count beyond
+// that bound stops the phase with an error status instead of looping.
 
-__host__ __device__ static inline bool tail_row_cache(int64_t E) { return E <= 128; }
-__host__ __device__ constexpr int tail_threads(int nch) { return nch <= 8 ? 1024 : 512; }
+constexpr int kSspWaves = 16;
+constexpr int kSspThreads = 64 * kSspWaves;
+constexpr int kSspCand = 64;  // unassigned tokens a batch considers (one per lane of wave 0)
 
-static size_t tail_lds_bytes(int64_t E, int L, int threads) {
-    size_t b = 8 * (2 * (size_t)E + (size_t)E * L) + 4 * (2 * (size_t)E * L + 6 * (size_t)E);
-    b += (size_t)threads * 16;  // rebuild scratch: 64 entries per wave
-    if (tail_row_cache(E)) b += 4 * (size_t)E + 4 * (size_t)E * (size_t)E;
+__host__ __device__ static inline bool ssp_c_in_lds(int64_t E) { return E <= 128; }
+// row stride of C in LDS: 8 doubles of padding move consecutive rows to
+// different LDS banks
+__host__ __device__ static inline int64_t ssp_c_stride(int64_t E) { return ssp_c_in_lds(E) ? E + 8 : E; }
+
+static size_t ssp_lds_bytes(int64_t E) {
+    const size_t nw = (size_t)((E + 63) / 64);
+    size_t b = 0;
+    if (ssp_c_in_lds(E)) b += 8 * (size_t)E * ((size_t)ssp_c_stride(E) + nw);  // C, stale bits
+    b += 8 * 5 * (size_t)E;               // prices, distances, frontier values (three lists)
+    b += 4 * 11 * (size_t)E;              // counts, next, frontier experts (three lists), full
+                                          // experts, out token, list head, touched, stale arcs (two)
+    b += 4 * 3 * (size_t)(E + kSspCand);  // item joiner / leaver / next
     return b;
 }
 
-constexpr int kRbBatch = 8;  // slots per lane loaded at once by a rebuild
-// bids a wave makes before it adds them to the workgroup's count and checks
-// the bid cap (one shared atomic per batch instead of one per bid)
-constexpr int kBidBatch = 8;
-
-// Loads of data this workgroup wrote (after the writer's memory wait):
-// workgroup scope, i.e. plain loads that may hit the CU's L1.
-BASE_DEV double load_wg_f64(const double* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Loads of data other waves of this workgroup wrote during the kernel (after
+// their memory wait and a barrier): device scope, so the
+// load is served by L2, never by a stale line of the CU's L1.
+BASE_DEV int ld_fresh_i32(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-BASE_DEV int load_wg_i32(const int32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+BASE_DEV double ld_fresh_f64(const double* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-BASE_DEV void lds_lock(int32_t* p, int lane) {
-    if (lane == 0) {
-        int expect = 0;
-        while (!__hip_atomic_compare_exchange_strong(p, &expect, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) {
-            expect = 0;
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    asm volatile("" ::: "memory");
-}
-BASE_DEV bool lds_trylock(int32_t* p, int lane) {
-    int ok = 0;
-    if (lane == 0) {
-        int expect = 0;
-        ok = __hip_atomic_compare_exchange_strong(p, &expect, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    asm volatile("" ::: "memory");
-    return first_lane_i32(ok) != 0;
-}
-// release after this wave's LDS writes have completed (its global stores are
-// tracked by the store counters instead)
-BASE_DEV void lds_unlock(int32_t* p, int lane) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-BASE_DEV void lds_count(int32_t* p, int lane) {
-    if (lane == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+BASE_DEV unsigned long long ld_fresh_u64(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sort (bid, token, slot) triples across the wave into eviction order
-// (bitonic network over the 64 lanes; entries (DBL_MAX, kNoTok) pad).
-BASE_DEV void wave_sort_evict(double& b, int& t, int& s, int lane) {
-#pragma unroll
-    for (int k2 = 2; k2 <= 64; k2 <<= 1) {
-#pragma unroll
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            const double ob = shfl_xor_f64(b, j);
-            const int ot = __shfl_xor(t, j, 64), os = __shfl_xor(s, j, 64);
-            const bool take_first = ((lane & j) == 0) == ((lane & k2) == 0);
-            const bool swap = take_first ? evict_first(ob, ot, b, t) : evict_first(b, t, ob, ot);
-            if (swap) { b = ob; t = ot; s = os; }
-        }
-    }
+// A frontier expert's D + p + eps, rounded up by 2^-50 times the magnitudes
+// summed. An arc's length then adds C (rounded up the same way) and -p_a
+// (likewise); the margins exceed the rounding error of every sum, so each
+// computed path length is at least its exact value, rounding makes no cycle
+// negative and the rounds end. The eps-CS the tail keeps is eps plus that
+// margin (about 1e-15 relative), far below any eps in use.
+BASE_DEV double frontier_value(double d, double pe, double eps) {
+    return (d + pe + eps) + 0x1p-50 * (fabs(d) + fabs(pe) + eps);
 }
 
-// Rebuild an expert's lowest-holder list from its k slots (k >= 1, a full
-// expert): the result is exactly its n lowest holders in eviction order, in
-// lanes 0..n-1, n = min(L, k) as a rule. Each lane takes the first of the
-// slots it reads (at most S = ceil(k / 64)); the r-th of those 64 lane minima
-// bounds the r lowest holders from above, so only the slots at or before it
-// -- typically a few more than r -- are gathered (scratch: 64 entries per
-// wave in LDS) and sorted. At most r * S slots can qualify, so if more than
-// 64 do, the gather is redone with r = 64 / S and the list is that long.
-BASE_DEV void wave_rebuild(const double* sbid, const int32_t* stok, int64_t k, int lane, int L,
-                           double* xb, int32_t* xt, int32_t* xs, double& lb, int& lt, int& ls,
-                           int& n) {
-    const bool single = k <= kRbBatch * 64;  // every slot of this lane stays in registers
-    double bb[kRbBatch];
-    int tt[kRbBatch];
-    auto load = [&](int64_t i0) {
+// Wave-wide (value, index) minimum, lowest index among equal values; the
+// result is uniform.
+BASE_DEV void argmin_merge(double& v, int& i, double ov, int oi) {
+    if (ov < v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+BASE_DEV void wave_argmin_f64(double& v, int& i) {
+    argmin_merge(v, i, dpp_f64<kDppXor1>(v), dpp_i32<kDppXor1>(i));
+    argmin_merge(v, i, dpp_f64<kDppXor2>(v), dpp_i32<kDppXor2>(i));
+    argmin_merge(v, i, dpp_f64<kDppHalfMirror>(v), dpp_i32<kDppHalfMirror>(i));
+    argmin_merge(v, i, dpp_f64<kDppMirror>(v), dpp_i32<kDppMirror>(i));
+    double bv = readlane_f64(v, 0);
+    int bi = readlane_i32(i, 0);
+    argmin_merge(bv, bi, readlane_f64(v, 16), readlane_i32(i, 16));
+    argmin_merge(bv, bi, readlane_f64(v, 32), readlane_i32(i, 32));
+    argmin_merge(bv, bi, readlane_f64(v, 48), readlane_i32(i, 48));
+    v = bv;
+    i = bi;
+}
+
+BASE_DEV float sani(float x, Sani sn) { return (sn.fix && !is_finite_f32(x)) ? sn.repl : x; }
+
+// C and Ct of every expert from its holders after the bulk rounds (one block
+// per expert; waves split the holders, lanes the columns), and the slot of
+// every holder.
+template <int NCH>
+__global__ __launch_bounds__(256) void auc_ssp_setup_kernel(const float* s, int64_t E, int64_t k,
+                                                            AucWs w, const ScoreScan* scan) {
+    extern __shared__ __attribute__((aligned(16))) char sm[];
+    double* pv = (double*)sm;                   // 4 waves x E
+    int32_t* pt = (int32_t*)(pv + 4 * E);       // 4 waves x E
+    const AucCtl* ctl = w.ctl;
+    if (ctl->abort || ctl->nbid[ctl->cur] == 0) return;
+    const int a = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const Sani sn = read_sani(scan);
+    const int n = w.cnt[a];
+    double bv[NCH];
+    int bt[NCH];
 #pragma unroll
-        for (int u = 0; u < kRbBatch; ++u) {
-            const int64_t i = i0 + u * 64 + lane;
-            bb[u] = DBL_MAX;
-            tt[u] = kNoTok;
-            if (i < k) { bb[u] = load_wg_f64(sbid + i); tt[u] = load_wg_i32(stok + i); }
-        }
-    };
-    // pass 1: the first slot of each lane in eviction order, then sorted
-    double mb = DBL_MAX;
-    int mt = kNoTok, ms = -1;
-    for (int64_t i0 = 0; i0 < k; i0 += kRbBatch * 64) {
-        load(i0);
+    for (int c = 0; c < NCH; ++c) { bv[c] = DBL_MAX; bt[c] = kNoTok; }
+    for (int i = wave; i < n; i += 4) {
+        const int h = w.stok[(int64_t)a * k + i];
+        if (lane == 0) w.slot_of[h] = i;
+        const float* row = s + (int64_t)h * E;
+        const double sa = (double)sani(row[a], sn);
 #pragma unroll
-        for (int u = 0; u < kRbBatch; ++u)
-            if (evict_first(bb[u], tt[u], mb, mt)) { mb = bb[u]; mt = tt[u]; ms = (int)(i0 + u * 64 + lane); }
-    }
-    wave_sort_evict(mb, mt, ms, lane);
-    // pass 2: gather every slot at or before the r-th lane minimum
-    auto gather = [&](int r) -> int {
-        const double tb = readlane_f64(mb, r - 1);
-        const int tk = readlane_i32(mt, r - 1);
-        int cnt = 0;
-        for (int64_t i0 = 0; i0 < k; i0 += kRbBatch * 64) {
-            if (!single) load(i0);
-#pragma unroll
-            for (int u = 0; u < kRbBatch; ++u) {
-                const bool in = tt[u] != kNoTok && !evict_first(tb, tk, bb[u], tt[u]);
-                const unsigned long long m = __ballot(in);
-                if (in) {
-                    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-                    const int at = cnt + __popcll(m & below);
-                    if (at < 64) { xb[at] = bb[u]; xt[at] = tt[u]; xs[at] = (int)(i0 + u * 64 + lane); }
-                }
-                cnt += __popcll(m);
+        for (int c = 0; c < NCH; ++c) {
+            const int e = lane + 64 * c;
+            if (e < E) {
+                const double v = sa - (double)sani(row[e], sn);
+                argmin_merge(bv[c], bt[c], v, h);
             }
         }
-        return cnt;
-    };
-    int r = (int)(k < (int64_t)L ? k : (int64_t)L);
-    int cnt = gather(r);
-    if (cnt > 64) {
-        const int S = (int)((k + 63) / 64);
-        r = 64 / S < r ? 64 / S : r;
-        if (r < 1) r = 1;
-        cnt = gather(r);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lb = DBL_MAX; lt = kNoTok; ls = -1;
-    if (lane < cnt) { lb = xb[lane]; lt = xt[lane]; ls = xs[lane]; }
-    wave_sort_evict(lb, lt, ls, lane);
-    n = r;
-    if (lane >= n) { lb = DBL_MAX; lt = kNoTok; ls = -1; }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        if (e < E) { pv[wave * E + e] = bv[c]; pt[wave * E + e] = bt[c]; }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        double v = pv[e];
+        int t = pt[e];
+        for (int q = 1; q < 4; ++q) argmin_merge(v, t, pv[q * E + e], pt[q * E + e]);
+        w.C[(int64_t)a * E + e] = v;
+        w.Ct[(int64_t)a * E + e] = t;
+    }
 }
 
-template <int NCH>
-__global__ __launch_bounds__(tail_threads(NCH)) void auc_tail_kernel(const float* s, int64_t T,
-                                                                     int64_t E, int64_t k, AucWs w,
-                                                                     const ScoreScan* scan,
-                                                                     double eps, int phase,
-                                                                     int64_t max_bids,
-                                                                     AucStatsDev* st) {
+template <int NCH, bool CL>
+__global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, int64_t T, int64_t E,
+                                                              int64_t k, AucWs w,
+                                                              const ScoreScan* scan, double eps,
+                                                              int phase, int64_t max_bids,
+                                                              AucStatsDev* st) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    constexpr int kThreads = tail_threads(NCH);
-    const int L = w.L;
-    double* pi = (double*)smem;                  // E
-    double* flo = pi + E;                        // E
-    double* lowb = flo + E;                      // E*L
-    double* rbx_b = lowb + E * L;                // 64 per wave: rebuild scratch
-    int32_t* lowt = (int32_t*)(rbx_b + kThreads);  // E*L
-    int32_t* lows = lowt + E * L;                // E*L
-    int32_t* cnt = lows + E * L;                 // E
-    int32_t* nlow = cnt + E;                     // E
-    int32_t* comp = nlow + E;                    // E
-    int32_t* lock = comp + E;                    // E
-    int32_t* st_issued = lock + E;               // E   slot stores issued
-    int32_t* st_done = st_issued + E;            // E   slot stores landed
-    int32_t* rbx_t = st_done + E;                // 64 per wave
-    int32_t* rbx_s = rbx_t + kThreads;           // 64 per wave
-    int32_t* rowtag = rbx_s + kThreads;          // E   token whose row is cached (cache on)
-    float* rowc = (float*)(rowtag + E);          // E*E cached rows             (cache on)
-    __shared__ int32_t next;
-    __shared__ int32_t stop;
-    __shared__ int32_t max_steps;
-    __shared__ unsigned long long nbids;
+    const int64_t cs = ssp_c_stride(E);
+    const int nw = (int)((E + 63) / 64);
+    char* sp = smem;
+    double* Cl = (double*)sp;                                    // E x cs (CL)
+    if (CL) sp += 8 * E * cs;
+    unsigned long long* stl = (unsigned long long*)sp;           // E x nw stale bits (CL)
+    if (CL) sp += 8 * E * nw;
+    double* p = (double*)sp;                                     // E   prices
+    double* D = p + E;                                           // E   distance to a free slot
+    double* fq = D + E;                                          // 3E  frontier: D + p + eps
+    int32_t* cnt = (int32_t*)(fq + 3 * E);                       // E   holders
+    int32_t* nx = cnt + E;                                       // E   next expert
+    int32_t* fl = nx + E;                                        // 3E  frontier experts
+    int32_t* rows = fl + 3 * E;                                  // E   full experts
+    int32_t* otok = rows + E;                                    // E   out holder Ct[a][nx(a)]
+    int32_t* head = otok + E;                                    // E   item list per expert
+    int32_t* ux = head + E;                                      // E   touched experts
+    int32_t* sarc = ux + E;                                      // 2E  stale best arcs (two lists)
+    int32_t* ij = sarc + 2 * E;                                      // E + kSspCand  item joiner
+    int32_t* il = ij + (E + kSspCand);                           //               item leaver
+    int32_t* inext = il + (E + kSspCand);                        //               item next
+    __shared__ int32_t cand[kSspCand], ce1[kSspCand], cf[kSspCand], clen[kSspCand],
+        order[kSspCand], alist[kSspCand], ring[kSspCand];
+    __shared__ double cL[kSspCand];
+    __shared__ int32_t nring, nc_s, nacc_s, nux, nitem, stop, nrows, nsarc[2], fn[3];
+    __shared__ double Lmax_s;
+    __shared__ int64_t ghead;
+    __shared__ long long placed, batches;
 
     AucCtl* ctl = w.ctl;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = first_lane_i32(tid >> 6);
-    const bool cache = tail_row_cache(E);
     const bool aborted = ctl->abort;
     const int cur = ctl->cur;
     const int64_t nb = aborted ? 0 : ctl->nbid[cur];
     const bool ident = ctl->identity;
     const int32_t* list = cur ? w.list1 : w.list0;
-    for (int64_t e = tid; e < E; e += kThreads) {
-        pi[e] = w.pi[e];
-        flo[e] = w.floor_[e];
+    const Sani sn = read_sani(scan);
+    double* Cg = w.C;
+    int32_t* Ct = w.Ct;
+    unsigned long long* stg = w.stale;
+    auto cget = [&](int a, int e) -> double {
+        if constexpr (CL) return Cl[a * cs + e];
+        else return ld_fresh_f64(Cg + (int64_t)a * E + e);
+    };
+    auto cset = [&](int a, int e, double v) {
+        if constexpr (CL) Cl[a * cs + e] = v;
+        else __hip_atomic_store(Cg + (int64_t)a * E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto sget = [&](int a, int c) -> unsigned long long {
+        if constexpr (CL) return stl[a * nw + c];
+        else return ld_fresh_u64(stg + (int64_t)a * nw + c);
+    };
+    auto sput = [&](int a, int c, unsigned long long v) {
+        if constexpr (CL) stl[a * nw + c] = v;
+        else __hip_atomic_store(stg + (int64_t)a * nw + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto stale = [&](int a, int b) -> bool { return (sget(a, b >> 6) >> (b & 63)) & 1ull; };
+
+    for (int64_t e = tid; e < E; e += kSspThreads) {
+        p[e] = w.pi[e];
         cnt[e] = w.cnt[e];
-        nlow[e] = w.nlow[e];
-        comp[e] = w.comp[e];
-        lock[e] = 0;
-        st_issued[e] = 0;
-        st_done[e] = 0;
-        if (cache) rowtag[e] = -1;
+        head[e] = -1;
     }
-    for (int64_t i = tid; i < E * L; i += kThreads) {
-        lowb[i] = w.lowb[i];
-        lowt[i] = w.lowt[i];
-        lows[i] = w.lows[i];
+    if (nb > 0) {
+        if (CL)
+            for (int64_t i = tid; i < E * E; i += kSspThreads) Cl[(i / E) * cs + i % E] = Cg[i];
+        for (int i = tid; i < (int)E * nw; i += kSspThreads) sput(i / nw, i % nw, 0ull);
     }
+    const unsigned long long used0 = ctl->bids_total + ctl->bids_phase;
+    const long long cap_left =
+        max_bids > 0 ? (long long)max_bids - (long long)min<unsigned long long>(used0, (unsigned long long)max_bids)
+                     : LLONG_MAX;
     if (tid == 0) {
-        next = 0;
-        max_steps = 0;
-        const unsigned long long before = ctl->bids_total + ctl->bids_phase;
-        stop = (max_bids > 0 && before >= (unsigned long long)max_bids && nb > 0) ? 1 : 0;
-        nbids = 0;
+        nring = 0;
+        ghead = 0;
+        placed = 0;
+        batches = 0;
+        stop = (nb > 0 && cap_left <= 0) ? 1 : 0;
     }
     __syncthreads();
-    const Sani sn = read_sani(scan);
-    const unsigned long long cap =
-        max_bids > 0 ? (unsigned long long)max_bids - min<unsigned long long>(
-                           (unsigned long long)max_bids, ctl->bids_total + ctl->bids_phase)
-                     : ~0ull;
-    // fill the row cache with every expert's lowest holder (its next victim)
-    if (cache) {
-        for (int64_t e = wave; e < E; e += kThreads / 64) {
-            if (first_lane_i32(nlow[e]) == 0) continue;
-            const int h = first_lane_i32(lowt[e * L]);
-            float r[NCH];
-            load_row<NCH>(s, h, E, lane, sn, r);
+
+    for (;;) {
+        // ---- this batch's tokens: those not placed last batch, then the list
+        if (tid == 0) {
+            int n = 0;
+            for (int r = 0; r < nring; ++r) cand[n++] = ring[r];
+            nring = 0;
+            while (n < kSspCand && ghead < nb) {
+                cand[n++] = ident ? (int32_t)ghead : list[ghead];
+                ++ghead;
+            }
+            nc_s = stop ? 0 : n;
+            nacc_s = 0;
+            nux = 0;
+            nitem = 0;
+        }
+        __syncthreads();
+        const int nc = first_lane_i32(nc_s);
+        if (nc == 0) break;
+
+        // ---- D and nx: shortest paths to a free slot, with every arc of the
+        // tree they form exact
+        for (int64_t e = tid; e < E; e += kSspThreads) {
+            D[e] = cnt[e] < k ? 0.0 : DBL_MAX;
+            nx[e] = -1;
+        }
+        if (tid == 0) {
+            fn[0] = 0;
+            fn[1] = 0;
+            fn[2] = 0;
+            nrows = 0;
+            nsarc[0] = 0;
+            nsarc[1] = 0;
+        }
+        __syncthreads();
+        for (int64_t e = tid; e < E; e += kSspThreads) {
+            if (cnt[e] < k) {
+                const int j = atomicAdd(&fn[0], 1);
+                fl[j] = (int)e;
+                fq[j] = frontier_value(0.0, p[e], eps);
+            } else {
+                rows[atomicAdd(&nrows, 1)] = (int)e;
+            }
+        }
+        __syncthreads();
+        const int nr = first_lane_i32(nrows);
+        // Bellman-Ford rounds. Round r relaxes the full experts' arcs into the
+        // experts listed in frontier list r % 3 (those whose distance changed
+        // in round r - 1; the free experts first) and lists the experts it
+        // improves in list (r + 1) % 3; list (r + 2) % 3, read in round r - 1,
+        // is emptied for round r + 1. The distance of a full expert is written
+        // only by the lanes that own its row, and read by others only through
+        // the lists. A row whose best arc is stale does not move: the arc goes
+        // on a repair list, all waves recompute the listed arcs over their
+        // expert's holders, and those rows look at the same frontier again
+        // (a repair only raises C, so the arcs a row passed over stay no
+        // better than its distance). Each repair clears a stale bit, so this
+        // ends; then every tree arc is exact and so is D.
+        //
+        // Evaluation of a list of rows against the frontier. Lanes per row: a
+        // power of two that covers the frontier, at most 16 and at most what
+        // lets all rows run at once.
+        auto relax = [&](const int32_t* rl, int n, bool coded, const int32_t* fle, const double* fqe,
+                         int nf, int ln, int tl) {
+            int sh = 0;
+            while (sh < 4 && (1 << sh) < nf && (n << (sh + 1)) <= kSspThreads) ++sh;
+            const int G = 1 << sh, gpw = 64 >> sh;
+            const int l = lane & (G - 1);
+            for (int r0 = wave * gpw; r0 < n; r0 += kSspWaves * gpw) {
+                const int r = r0 + (lane >> sh);
+                const bool ok = r < n;
+                const int a = ok ? (coded ? rl[r] / (int)E : rl[r]) : 0;
+                double bv = DBL_MAX;
+                int bn = 0x7fffffff;
+                if (ok) {
+                    const double pa = p[a];
+                    const double ra = fma(fabs(pa), 0x1p-50, -pa);
+#pragma unroll 2
+                    for (int j = l; j < nf; j += G) {
+                        const int b = fle[j];
+                        const double c = cget(a, b);
+                        const double v = (fma(fabs(c), 0x1p-50, c) + fqe[j]) + ra;
+                        const bool take = (v < bv) | ((v == bv) & (b < bn));
+                        bv = take ? v : bv;
+                        bn = take ? b : bn;
+                    }
+                }
+                // the row's minimum, then the lowest expert that reaches it
+                double m = bv;
+                if (sh >= 1) m = fmin(m, dpp_f64<kDppXor1>(m));
+                if (sh >= 2) m = fmin(m, dpp_f64<kDppXor2>(m));
+                if (sh >= 3) m = fmin(m, dpp_f64<kDppHalfMirror>(m));
+                if (sh >= 4) m = fmin(m, dpp_f64<kDppMirror>(m));
+                int ib = bv == m ? bn : 0x7fffffff;
+                if (sh >= 1) ib = min(ib, dpp_i32<kDppXor1>(ib));
+                if (sh >= 2) ib = min(ib, dpp_i32<kDppXor2>(ib));
+                if (sh >= 3) ib = min(ib, dpp_i32<kDppHalfMirror>(ib));
+                if (sh >= 4) ib = min(ib, dpp_i32<kDppMirror>(ib));
+                if (ok && l == 0 && m < D[a]) {
+                    if (stale(a, ib)) {
+                        sarc[tl * E + atomicAdd(&nsarc[tl], 1)] = a * (int)E + ib;
+                    } else {
+                        D[a] = m;
+                        nx[a] = ib;
+                        const int j = atomicAdd(&fn[ln], 1);
+                        fl[ln * E + j] = a;
+                        fq[ln * E + j] = frontier_value(m, p[a], eps);
+                    }
+                }
+            }
+        };
+        bool conv = false;
+        int par = 0;  // repair list the current evaluation fills
+        for (int it = 0; it <= E + 1; ++it) {
+            const int li = it % 3, ln = (it + 1) % 3;
+            const int nf = first_lane_i32(fn[li]);
+            if (nf == 0) { conv = true; break; }
+            if (tid == 0) fn[(it + 2) % 3] = 0;
+            const int32_t* fle = fl + li * E;
+            const double* fqe = fq + li * E;
+            relax(rows, nr, false, fle, fqe, nf, ln, par);
+            __syncthreads();
+            for (int rep = 0;; ++rep) {
+                const int ns = first_lane_i32(nsarc[par]);
+                if (ns == 0) break;
+                if (rep > E * nw * 64) { it = (int)E + 2; break; }
+                if (tid == 0) nsarc[par ^ 1] = 0;
+                const int32_t* sl = sarc + par * E;
+                for (int i = wave; i < ns; i += kSspWaves) {
+                    const int code = first_lane_i32(sl[i]);
+                    const int a = code / (int)E, b = code - a * (int)E;
+                    const int ha = first_lane_i32(cnt[a]);
+                    double bv = DBL_MAX;
+                    int bt = kNoTok;
+                    for (int j0 = 0; j0 < ha; j0 += 8 * 64) {
+                        int hh[8];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c)
-                if (lane + 64 * c < E) rowc[e * E + lane + 64 * c] = r[c];
-            if (lane == 0) rowtag[e] = h;
+                        for (int v = 0; v < 8; ++v) {
+                            const int j = j0 + v * 64 + lane;
+                            hh[v] = (j < ha) ? ld_fresh_i32(w.stok + (int64_t)a * k + j) : -1;
+                        }
+                        float sa[8], sb[8];
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) {
+                            const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
+                            sa[v] = hh[v] >= 0 ? sani(row[a], sn) : 0.0f;
+                            sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
+                        }
+#pragma unroll
+                        for (int v = 0; v < 8; ++v)
+                            if (hh[v] >= 0) argmin_merge(bv, bt, (double)sa[v] - (double)sb[v], hh[v]);
+                    }
+                    wave_argmin_f64(bv, bt);
+                    if (lane == 0) {
+                        cset(a, b, bv);
+                        __hip_atomic_store(Ct + (int64_t)a * E + b, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        sput(a, b >> 6, sget(a, b >> 6) & ~(1ull << (b & 63)));
+                    }
+                }
+                __syncthreads();
+                relax(sl, ns, true, fle, fqe, nf, ln, par ^ 1);
+                __syncthreads();
+                par ^= 1;
+            }
+        }
+        if (!conv) {
+            // rounding made a cycle negative: stop with an error status
+            if (tid == 0) stop = 1;
+            __syncthreads();
+            continue;
+        }
+        // each full expert's out holder (the token its shortest path moves)
+        for (int64_t a = tid; a < E; a += kSspThreads)
+            otok[a] = (cnt[a] >= k && nx[a] >= 0) ? ld_fresh_i32(Ct + a * E + nx[a]) : -1;
+
+        // ---- each token's best entry: L_u = min_e entry(u,e) + D(e)
+        for (int q = wave; q < nc; q += kSspWaves) {
+            const int u = first_lane_i32(cand[q]);
+            float v[NCH];
+            load_row<NCH>(s, u, E, lane, sn, v);
+            double val[NCH], best = -DBL_MAX;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int e = lane + 64 * c;
+                val[c] = e < E ? (double)v[c] - p[e] : -DBL_MAX;
+                best = fmax(best, val[c]);
+            }
+            const double pu = wave_max_f64(best);
+            double bv = DBL_MAX;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int e = lane + 64 * c;
+                if (e < E && D[e] < DBL_MAX) {
+                    const double cst = (pu - val[c]) + D[e];
+                    if (cst < bv) { bv = cst; be = e; }
+                }
+            }
+            wave_argmin_f64(bv, be);
+            if (lane == 0) {
+                cL[q] = bv;
+                ce1[q] = be == 0x7fffffff ? -1 : be;
+            }
+        }
+        __syncthreads();
+
+        // ---- apply, in order of L_u, the paths whose full experts no
+        // earlier applied path uses and whose free expert has a slot left
+        if (wave == 0) {
+            const bool mine = lane < nc;
+            const double lq = mine ? cL[lane] : DBL_MAX;
+            int rank = 0;
+            for (int r = 0; r < nc; ++r) {
+                const double lr = readlane_f64(lq, r);
+                rank += (lr < lq || (lr == lq && r < lane)) ? 1 : 0;
+            }
+            if (mine) order[rank] = lane;
+            // the experts of this lane's path, and its free expert
+            unsigned long long msk[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) msk[c] = 0;
+            int f = -1, steps = 0;
+            if (mine && ce1[lane] >= 0) {
+                int a = ce1[lane];
+                while (a >= 0 && cnt[a] >= k && steps < E) {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        if (c == (a >> 6)) msk[c] |= 1ull << (a & 63);
+                    a = nx[a];
+                    ++steps;
+                }
+                f = (a >= 0 && cnt[a] < k) ? a : -1;
+            }
+            if (mine) {
+                cf[lane] = f;
+                clen[lane] = steps;
+            }
+            int capc[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int e = lane + 64 * c;
+                capc[c] = e < E ? (int)(k - cnt[e]) : 0;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            unsigned long long used[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) used[c] = 0;
+            int nacc = 0;
+            double Lmax = 0.0;
+            for (int r = 0; r < nc; ++r) {
+                const int q = first_lane_i32(order[r]);
+                const int fq_ = readlane_i32(f, q);
+                if (fq_ < 0) continue;
+                int capq = 0;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    if (c == (fq_ >> 6)) capq = capc[c];
+                capq = readlane_i32(capq, fq_ & 63);
+                bool ok = capq > 0;
+                unsigned long long mq[NCH];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const unsigned lo = (unsigned)readlane_i32((int)(unsigned)msk[c], q);
+                    const unsigned hi = (unsigned)readlane_i32((int)(unsigned)(msk[c] >> 32), q);
+                    mq[c] = ((unsigned long long)hi << 32) | lo;
+                    ok = ok && (mq[c] & used[c]) == 0;
+                }
+                if (!ok) continue;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    used[c] |= mq[c];
+                    if (c == (fq_ >> 6) && lane == (fq_ & 63)) --capc[c];
+                }
+                if (lane == 0) alist[nacc] = q;
+                ++nacc;
+                Lmax = fmax(Lmax, readlane_f64(lq, q));
+            }
+            if (lane == 0) {
+                nacc_s = nacc;
+                Lmax_s = Lmax;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // tokens not placed search again next batch (in candidate order)
+            bool placedq = false;
+            for (int j = 0; j < nacc; ++j) placedq = placedq || alist[j] == lane;
+            const unsigned long long rej = __ballot(mine && !placedq);
+            if (mine && !placedq) {
+                const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+                ring[__popcll(rej & below)] = cand[lane];
+            }
+            if (lane == 0) nring = __popcll(rej);
+        }
+        __syncthreads();
+
+        // ---- prices drop by max(0, L - D(e))
+        {
+            const double Lmax = Lmax_s;
+            for (int64_t e = tid; e < E; e += kSspThreads)
+                if (D[e] < Lmax) p[e] = p[e] - (Lmax - D[e]);
+        }
+        // ---- move the tokens of the applied paths; one item per expert on a
+        // path. Lane i takes node i of the path (nodes 0 .. m; node m is the
+        // free expert), found by following nx from e1.
+        const int nacc = first_lane_i32(nacc_s);
+        for (int j = wave; j < nacc; j += kSspWaves) {
+            const int q = first_lane_i32(alist[j]);
+            const int u = first_lane_i32(cand[q]);
+            const int m = first_lane_i32(clen[q]);
+            const int e1 = first_lane_i32(ce1[q]);
+            for (int i0 = 0; i0 <= m; i0 += 64) {
+                const int i = i0 + lane;
+                int x = e1, prv = -1;
+                if (i <= m)
+                    for (int h = 0; h < i; ++h) {
+                        prv = x;
+                        x = nx[x];
+                    }
+                int jn = 0, lv = -1, slot = 0;
+                if (i <= m) {
+                    jn = i == 0 ? u : otok[prv];
+                    lv = i < m ? otok[x] : -1;
+                    if (i < m) slot = ld_fresh_i32(w.slot_of + lv);
+                }
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                if (i == m) slot = atomicAdd(&cnt[x], 1);
+                if (i <= m) {
+                    w.stok[(int64_t)x * k + slot] = jn;
+                    w.slot_of[jn] = slot;
+                    const int id = atomicAdd(&nitem, 1);
+                    ij[id] = jn;
+                    il[id] = lv;
+                    const int prev = __hip_atomic_exchange(&head[x], id, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                    inext[id] = prev;
+                    if (prev < 0) ux[atomicAdd(&nux, 1)] = x;
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+
+        // ---- C and Ct after the moves: one wave per touched expert. The
+        // tokens that joined lower the columns they beat (those become
+        // exact); every other column whose cheapest holder left is marked
+        // stale and keeps its old value, which can only underestimate it.
+        const int nx_ = first_lane_i32(nux);
+        for (int uu = wave; uu < nx_; uu += kSspWaves) {
+            const int x = first_lane_i32(ux[uu]);
+            // this expert's items: lane j holds item j's joiner and leaver
+            int myj = -1, myl = -1, nit = 0;
+            for (int id = first_lane_i32(head[x]); id >= 0 && nit < 64;
+                 id = first_lane_i32(inext[id]), ++nit) {
+                const int jn = first_lane_i32(ij[id]);
+                const int lv = first_lane_i32(il[id]);
+                if (lane == nit) { myj = jn; myl = lv; }
+            }
+            int ct[NCH];
+            double cv[NCH];
+            bool upd[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int e = lane + 64 * c;
+                ct[c] = e < E ? ld_fresh_i32(Ct + (int64_t)x * E + e) : -1;
+                cv[c] = e < E ? cget(x, e) : 0.0;
+                upd[c] = false;
+            }
+            // joiners (their rows four at a time)
+            for (int j0 = 0; j0 < nit; j0 += 4) {
+                float r[4][NCH];
+                int jt[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    jt[q] = (j0 + q < nit) ? readlane_i32(myj, (j0 + q) & 63) : -1;
+                    if (jt[q] >= 0) load_row<NCH>(s, jt[q], E, lane, sn, r[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (jt[q] < 0) continue;
+                    float rx = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        if (c == (x >> 6)) rx = r[q][c];
+                    const double sx = (double)readlane_f64((double)rx, x & 63);
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        const int e = lane + 64 * c;
+                        const double v = sx - (double)r[q][c];
+                        if (e < E && (v < cv[c] || (v == cv[c] && jt[q] < ct[c]))) {
+                            cv[c] = v;
+                            ct[c] = jt[q];
+                            upd[c] = true;
+                            cset(x, e, v);
+                            __hip_atomic_store(Ct + (int64_t)x * E + e, jt[q], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                }
+            }
+            bool bad[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) bad[c] = false;
+            for (int j = 0; j < nit; ++j) {
+                const int lv = readlane_i32(myl, j & 63);
+                if (lv < 0) continue;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) bad[c] = bad[c] || ct[c] == lv;
+            }
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const bool in = lane + 64 * c < E;
+                const unsigned long long nb_ = __ballot(bad[c] && in), nu = __ballot(upd[c] && in);
+                if (c < nw && lane == 0 && (nb_ | nu)) sput(x, c, (sget(x, c) & ~nu) | nb_);
+            }
+            if (lane == 0) head[x] = -1;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            placed += nacc;
+            ++batches;
+            // every batch places a token: more batches than tokens means the
+            // state is inconsistent; stop with an error instead of looping
+            if (placed >= cap_left || batches > nb + 1) stop = 1;
         }
         __syncthreads();
     }
-    double* xb = rbx_b + wave * 64;
-    int32_t* xt = rbx_t + wave * 64;
-    int32_t* xs = rbx_s + wave * 64;
-    // this wave's bids not yet in nbids, and whether the cap had been reached
-    // at its last check (other waves' stops are seen at this wave's next one)
-    int lbids = 0;
-    bool halted = first_lane_i32(stop) != 0;
-    auto flush_bids = [&]() {
-        if (lane == 0 && lbids > 0) {
-            const unsigned long long nbd =
-                atomicAdd(&nbids, (unsigned long long)lbids) + (unsigned long long)lbids;
-            if (nbd >= cap) stop = 1;
-        }
-        lbids = 0;
-        halted = first_lane_i32(stop) != 0;
-    };
-    auto count_bid = [&]() {
-        if (++lbids >= kBidBatch) flush_bids();
-    };
 
-    int pending = -1;        // expert with this wave's last slot store not yet counted
-    int cpe = -1, cpt = -1;  // row loaded for the cache: expert, token
-    float cpv[NCH];
-    int steps = 0;
-    for (;;) {
-        int j = 0;
-        if (lane == 0) j = atomicAdd(&next, 1);
-        j = first_lane_i32(j);
-        if (j >= nb || first_lane_i32(stop)) break;
-        int t = ident ? j : first_lane_i32(list[j]);
-        int fr = -1;  // expert t was just evicted from
-        while (t >= 0) {
-            if (halted) break;
-            // the row: from the cache when the tag names t before and after
-            float v[NCH];
-            bool hit = false;
-            if (cache && fr >= 0 && first_lane_i32(rowtag[fr]) == t) {
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) v[c] = (lane + 64 * c < E) ? rowc[fr * E + lane + 64 * c] : 0.0f;
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                hit = first_lane_i32(rowtag[fr]) == t;
-            }
-            if (!hit) load_row<NCH>(s, t, E, lane, sn, v);
-            if (cpe >= 0) {
-                // publish the row loaded last step if its token is still the lowest holder
-                if (lds_trylock(&lock[cpe], lane)) {
-                    if (first_lane_i32(nlow[cpe]) > 0 && first_lane_i32(lowt[(int64_t)cpe * L]) == cpt) {
-                        if (lane == 0) rowtag[cpe] = -1;
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-                        for (int c = 0; c < NCH; ++c) {
-                            float x = cpv[c];
-                            if (sn.fix && !is_finite_f32(x)) x = sn.repl;
-                            if (lane + 64 * c < E) rowc[cpe * E + lane + 64 * c] = x;
-                        }
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        if (lane == 0) rowtag[cpe] = cpt;
-                    }
-                    lds_unlock(&lock[cpe], lane);
-                }
-                cpe = -1;
-            }
-            for (;;) {
-                int e;
-                double v1, v2, pb;
-                best_two<NCH>(v, pi, E, lane, e, v1, v2, pb);
-                const double beta = bid_amount(pb, v1, v2, eps);
-                // the slot store of the previous step has landed once this
-                // returns; it is counted before this wave waits for any lock
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                if (pending >= 0) {
-                    lds_count(&st_done[pending], lane);
-                    pending = -1;
-                }
-                lds_lock(&lock[e], lane);
-                // ---- under the lock of e
-                const int64_t eb = (int64_t)e * L;
-                int32_t* stk = w.stok + (int64_t)e * k;
-                double* sbd = w.sbid + (int64_t)e * k;
-                int c = first_lane_i32(cnt[e]), nl = first_lane_i32(nlow[e]);
-                int cp = first_lane_i32(comp[e]);
-                double lb = DBL_MAX;
-                int lt = kNoTok, ls = -1;
-                if (lane < nl) { lb = lowb[eb + lane]; lt = lowt[eb + lane]; ls = lows[eb + lane]; }
-                const int head0 = readlane_i32(lt, 0);
-                auto rebuild = [&]() {
-                    if (lane == 0) {
-                        const int want = __hip_atomic_load(&st_issued[e], __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                        while (__hip_atomic_load(&st_done[e], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP) != want)
-                            __builtin_amdgcn_s_sleep(1);
-                    }
-                    asm volatile("" ::: "memory");
-                    wave_rebuild(sbd, stk, k, lane, L, xb, xt, xs, lb, lt, ls, nl);
-                    cp = (nl >= k) ? 1 : 0;
-                };
-                if (c >= k && nl == 0) rebuild();
-                if (c >= k && !evict_first(readlane_f64(lb, 0), readlane_i32(lt, 0), beta, t)) {
-                    // the price rose since the bid: bid again (counted, so the
-                    // bid cap also ends a phase that cannot progress)
-                    lds_unlock(&lock[e], lane);
-                    count_bid();
-                    if (halted) { t = -1; break; }
-                    continue;
-                }
-                int slot, victim = -1;
-                if (c < k) {
-                    slot = c++;
-                } else {
-                    // pop the lowest holder (lane 0 of the list)
-                    victim = readlane_i32(lt, 0);
-                    slot = readlane_i32(ls, 0);
-                    const double nb_ = dpp_f64<kDppWaveShl1>(lb);
-                    const int nt = dpp_i32<kDppWaveShl1>(lt);
-                    const int ns = dpp_i32<kDppWaveShl1>(ls);
-                    if (lane + 1 < nl) { lb = nb_; lt = nt; ls = ns; }
-                    else { lb = DBL_MAX; lt = kNoTok; ls = -1; }
-                    --nl;
-                }
-                if (lane == 0) {
-                    stk[slot] = t;
-                    sbd[slot] = beta;
-                    // no-return LDS add: visible before the unlock's wait ends
-                    __hip_atomic_fetch_add(&st_issued[e], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-                pending = e;
-                // the new holder enters the list if the list covers it
-                const bool before = lane < nl && evict_first(lb, lt, beta, t);
-                const int pos = __popcll(__ballot(before));
-                if ((nl < L && cp) || pos < nl) {
-                    const double pb_ = dpp_f64<kDppWaveShr1>(lb);
-                    const int pt_ = dpp_i32<kDppWaveShr1>(lt);
-                    const int ps = dpp_i32<kDppWaveShr1>(ls);
-                    if (lane == pos) { lb = beta; lt = t; ls = slot; }
-                    else if (lane > pos) { lb = pb_; lt = pt_; ls = ps; }
-                    if (nl == L) cp = 0;  // the old last entry dropped out
-                    else ++nl;
-                } else {
-                    cp = 0;
-                }
-                if (c >= k && nl == 0) {
-                    // a full expert publishes its lowest bid: count this wave's
-                    // own store as landed first, then rebuild
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    lds_count(&st_done[e], lane);
-                    pending = -1;
-                    rebuild();
-                }
-                if (lane < nl) { lowb[eb + lane] = lb; lowt[eb + lane] = lt; lows[eb + lane] = ls; }
-                const double head_bid = readlane_f64(lb, 0);
-                const int head1 = readlane_i32(lt, 0);
-                if (lane == 0) {
-                    cnt[e] = c;
-                    nlow[e] = nl;
-                    comp[e] = cp;
-                    pi[e] = (c >= k) ? head_bid : flo[e];
-                }
-                if (cache && nl > 0 && head1 != head0) {
-                    // a new lowest holder: load its row for the cache
-                    cpe = e;
-                    cpt = head1;
-                    if (head1 == t) {
-#pragma unroll
-                        for (int cc = 0; cc < NCH; ++cc) cpv[cc] = v[cc];
-                    } else {
-                        // raw load (sanitized when published): nothing waits for it here
-                        const float* row = s + (int64_t)head1 * E;
-#pragma unroll
-                        for (int cc = 0; cc < NCH; ++cc)
-                            cpv[cc] = (lane + 64 * cc < E) ? row[lane + 64 * cc] : 0.0f;
-                    }
-                }
-                lds_unlock(&lock[e], lane);
-                count_bid();
-                ++steps;
-                t = victim;
-                fr = e;
-                break;
-            }
-        }
-    }
-    flush_bids();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (pending >= 0) lds_count(&st_done[pending], lane);
-    if (lane == 0) atomicMax(&max_steps, steps);
-    __syncthreads();
     if (tid == 0) {
-        const unsigned long long pb = ctl->bids_phase + nbids;
+        const unsigned long long pb = ctl->bids_phase + (unsigned long long)placed;
         ctl->bids_total += pb;
         if (phase < 16) {
             st->bids[phase] = (long long)pb;
-            st->rounds[phase] = ctl->rounds_phase + max_steps;
+            st->rounds[phase] = ctl->rounds_phase + batches;
         }
         st->phases = phase + 1;
         if (stop && !aborted) st->status = kErrNotConverged;
     }
-    // every expert is full: its price floor becomes its lowest held bid
-    for (int64_t e = tid; e < E; e += kThreads) {
-        w.floor_[e] = (cnt[e] == k) ? pi[e] : flo[e];
+    // the next phase starts from these prices
+    for (int64_t e = tid; e < E; e += kSspThreads) {
+        w.floor_[e] = p[e];
         w.cnt[e] = cnt[e];
     }
 }
