@@ -46,6 +46,10 @@ constexpr int kBulkRoundsSmallK = 32;
 constexpr int64_t kSmallK = 128;
 constexpr int kTailMax = 64;         // bidders left when the tail takes over
 constexpr int kResolveCap = 2048;    // bidders sorted at once per expert
+constexpr int64_t kBinMax = 2048;    // rounds with at most this many bidders file bids by expert
+constexpr int kOvfCap = 6144;        // an expert's bidders beyond kResolveCap kept in its bin
+static_assert(kBinMax <= kResolveCap, "a round's bin for one expert must fit the resolve buffer");
+static_assert(kBinMax <= kOvfCap, "the bins hold either a round's bids or the overflow");
 constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
@@ -55,10 +59,8 @@ struct AucCtl {
     int32_t cur;          // bidder list in use (0/1)
     int32_t bulk_done;    // the tail owns the rest of this phase
     int32_t identity;     // the bidder list is 0..T-1 (round 0)
-    int32_t done_blocks;  // resolve blocks finished (last one flips cur)
     int32_t nbid[2];
     int32_t abort;        // a device error is set: skip all work
-    int32_t pad;
     unsigned long long bids_total;
     unsigned long long bids_phase;
     long long rounds_phase;
@@ -79,6 +81,9 @@ struct AucWs {
     double* C;         // E*E tail: cheapest move of a holder of a to b
     int32_t* Ct;       // E*E tail: the holder that makes it
     unsigned long long* stale;  // E*ceil(E/64) tail: C entries whose holder left
+    int32_t* bcnt;     // E   bids filed for each expert this round
+    int32_t* bin_t;    // E*kOvfCap  the bidders (few-bidder rounds), else the overflow
+    double* bin_v;     // E*kBinMax  their bids (few-bidder rounds)
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -100,13 +105,17 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.C = (double*)p; p += align256(E * E * 8);
     w.Ct = (int32_t*)p; p += align256(E * E * 4);
     w.stale = (unsigned long long*)p; p += align256(E * ((E + 63) / 64) * 8);
+    w.bcnt = (int32_t*)p; p += align256(E * 4);
+    w.bin_t = (int32_t*)p; p += align256(E * kOvfCap * 4);
+    w.bin_v = (double*)p; p += align256(E * kBinMax * 8);
     return w;
 }
 
 size_t auction_ws_bytes(int64_t T, int64_t E) {
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
            5 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
-           align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + 256;
+           align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
+           align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) + 256;
 }
 
 // ---------------------------------------------------------------- helpers
@@ -246,6 +255,7 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < E) {
         w.cnt[i] = 0;
+        w.bcnt[i] = 0;
         w.pi[i] = w.floor_[i];
     }
     if (i == 0) {
@@ -253,7 +263,6 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
         c->cur = 0;
         c->bulk_done = 0;
         c->identity = 1;
-        c->done_blocks = 0;
         c->nbid[0] = (int32_t)T;
         c->nbid[1] = 0;
         c->abort = st->status != 0;
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
                                                            int round, double eps) {
     AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->bulk_done) return;
-    const int cur = ctl->cur;
+    const int cur = round & 1;  // round r bids from list r % 2
     const int64_t nb = ctl->nbid[cur];
     if (round > 0 && nb <= kTailMax) {
         if (blockIdx.x == 0 && threadIdx.x == 0) ctl->bulk_done = 1;
@@ -280,7 +289,8 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
         ctl->nbid[cur ^ 1] = 0;
         ctl->bids_phase += (unsigned long long)nb;  // every listed token bids once
     }
-    const bool ident = ctl->identity;
+    const bool ident = round == 0;
+    const bool binned = nb <= kBinMax;
     const int32_t* list = cur ? w.list1 : w.list0;
     const Sani sn = read_sani(scan);
     const int lane = threadIdx.x & 63;
@@ -307,8 +317,16 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
         double v1, v2, pb;
         best_two_pv<NCH>(v, pv, E, lane, b1, v1, v2, pb);
         if (lane == 0) {
+            // the bid, and in a round with few bidders a copy filed under its
+            // expert (the resolve kernel then reads only its own)
+            const double bid = bid_amount(pb, v1, v2, eps);
             w.bexp[t] = b1;
-            w.bval[t] = bid_amount(pb, v1, v2, eps);
+            w.bval[t] = bid;
+            if (binned) {
+                const int pos = atomicAdd(&w.bcnt[b1], 1);
+                w.bin_t[(int64_t)b1 * kOvfCap + pos] = (int32_t)t;
+                w.bin_v[(int64_t)b1 * kBinMax + pos] = bid;
+            }
         }
         ++mine;
         j = jn;
@@ -321,14 +339,16 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
 
 // One block per expert: keep the k best of (current holders + this round's
 // bidders for this expert), return the others to the next bidder list, and
-// publish the expert's price and its L lowest holders. The holders are kept
+// publish the expert's price. In a round with at most kBinMax bidders the bid
+// kernel files each bid under its expert, so an expert reads only its own
+// bidders; in larger rounds (where those atomics would contend) every expert
+// scans the round's list. The list a round reads and writes follows from the
+// round's parity, so no block waits for the others. The holders are kept
 // sorted best first (bid descending, then token ascending) in the expert's
 // slots across the bulk rounds of a phase, so a round sorts only its new
 // bidders and merges by rank: a holder's new position is its old one plus
 // the number of bidders better than it, a bidder's is its position among the
 // bidders plus the number of holders better than it (binary searches).
-// Bidders are gathered kResolveCap at a time; a full buffer is merged before
-// the scan goes on.
 BASE_DEV bool better(double ba, int ta, double bb, int tb) { return ba > bb || (ba == bb && ta < tb); }
 
 // Sort (bid, token) pairs across the wave, best first (bitonic network over
@@ -410,7 +430,7 @@ BASE_DEV void publish_expert(AucWs& w, int e, int64_t k, int m, const double* hb
 }
 
 __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
-                                                               AucWs w) {
+                                                               AucWs w, int round) {
     __shared__ double cb[kResolveCap];   // bidders
     __shared__ int32_t ct[kResolveCap];
     __shared__ double hb[kBulkKMax];     // holders, best first
@@ -420,9 +440,9 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     __shared__ int32_t ncand, nhold;
     AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->bulk_done) return;
-    const int cur = ctl->cur;
+    const int cur = round & 1;
     const int64_t nb = ctl->nbid[cur];
-    const bool ident = ctl->identity;
+    const bool ident = round == 0;
     const int32_t* list = cur ? w.list1 : w.list0;
     int32_t* outl = cur ? w.list0 : w.list1;
     const int e = blockIdx.x;
@@ -489,77 +509,116 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     };
 
     const int c0 = w.cnt[e];
-    for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
-    // gather this expert's bidders in one pass with 16 loads in flight per
-    // thread (the bids were written by other XCDs: every load is a far round
-    // trip); tokens first, their bids in a second, parallel sweep. More
-    // bidders than the buffer holds (rare) fall back to chunks merged in turn.
     if (tid == 0) { ncand = 0; nhold = c0; }
-    __syncthreads();
-    auto scan_bidders = [&](auto&& fn) {
-        constexpr int U = 16;
-        for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
-            int64_t tt[U];
-            int ee[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t j = j0 + (int64_t)u * blockDim.x + tid;
-                tt[u] = (j < nb) ? (ident ? j : (int64_t)list[j]) : -1;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) ee[u] = (tt[u] >= 0) ? w.bexp[tt[u]] : -1;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (ee[u] == e) fn(tt[u]);
-        }
-    };
-    scan_bidders([&](int64_t t) {
-        const int pos = atomicAdd(&ncand, 1);
-        if (pos < kResolveCap) ct[pos] = (int32_t)t;
-    });
-    __syncthreads();
-    const int nbe = ncand;
-    const bool changed = nbe > 0;
-    if (nbe > 0 && nbe <= kResolveCap) {
-        for (int i = tid; i < nbe; i += blockDim.x) cb[i] = w.bval[ct[i]];
-        __syncthreads();
-        merge(nbe);
-    } else if (nbe > 0) {
-        __syncthreads();
-        if (tid == 0) ncand = 0;
-        __syncthreads();
-        for (int64_t j0 = 0; j0 < nb; j0 += blockDim.x) {
-            const int64_t j = j0 + tid;
-            if (j < nb) {
-                const int64_t t = ident ? j : list[j];
-                if (w.bexp[t] == e) {
-                    const int pos = atomicAdd(&ncand, 1);
-                    cb[pos] = w.bval[t];
-                    ct[pos] = (int32_t)t;
-                }
+    int nbe;  // this round's bidders for e
+    if (nb <= kBinMax) {
+        // as the bid kernel filed them (at most kBinMax <= kResolveCap)
+        nbe = w.bcnt[e];
+        if (nbe > 0) {
+            for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
+            for (int i = tid; i < nbe; i += blockDim.x) {
+                ct[i] = w.bin_t[(int64_t)e * kOvfCap + i];
+                cb[i] = w.bin_v[(int64_t)e * kBinMax + i];
             }
             __syncthreads();
-            const int n = ncand;
-            if (n > kResolveCap - (int)blockDim.x) merge(n);
+            if (tid == 0) w.bcnt[e] = 0;
+            merge(nbe);
         }
-        if (ncand > 0) merge(ncand);
+    } else {
+        // gather e's bidders from the round's list in one pass, 16 loads in
+        // flight per thread (the bids were written by other XCDs: every load
+        // is a far round trip); tokens first, their bids in a second sweep
+        for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
+        __syncthreads();
+        {
+            constexpr int U = 16;
+            for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
+                int64_t tt[U];
+                int ee[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t j = j0 + (int64_t)u * blockDim.x + tid;
+                    tt[u] = (j < nb) ? (ident ? j : (int64_t)list[j]) : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) ee[u] = (tt[u] >= 0) ? w.bexp[tt[u]] : -1;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ee[u] == e) {
+                        const int pos = atomicAdd(&ncand, 1);
+                        if (pos < kResolveCap) ct[pos] = (int32_t)tt[u];
+                        else if (pos < kResolveCap + kOvfCap)
+                            w.bin_t[(int64_t)e * kOvfCap + pos - kResolveCap] = (int32_t)tt[u];
+                    }
+            }
+        }
+        __syncthreads();
+        nbe = ncand;
+        if (nbe > kResolveCap) {
+            __threadfence();  // the overflow stores, before other threads load them
+            __syncthreads();
+        }
+        if (nbe > 0 && nbe <= kResolveCap + kOvfCap) {
+            // the first kResolveCap from LDS, the rest from the bin, merged
+            // kResolveCap at a time
+            for (int c0 = 0; c0 < nbe; c0 += kResolveCap) {
+                const int cn = min(kResolveCap, nbe - c0);
+                if (c0 > 0)
+                    for (int i = tid; i < cn; i += blockDim.x)
+                        ct[i] = __hip_atomic_load(w.bin_t + (int64_t)e * kOvfCap + (c0 - kResolveCap) + i,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = tid; i < cn; i += blockDim.x) cb[i] = w.bval[ct[i]];
+                __syncthreads();
+                merge(cn);
+            }
+        } else if (nbe > 0) {
+            // more than the buffer holds (rare): gather again, four loads in
+            // flight, merging whenever the buffer may not hold another pass.
+            // Every thread reads the count between two barriers, so all take
+            // the same branch.
+            __syncthreads();
+            if (tid == 0) ncand = 0;
+            __syncthreads();
+            constexpr int U = 4;
+            for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
+                int64_t tt[U];
+                int ee[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t j = j0 + (int64_t)u * blockDim.x + tid;
+                    tt[u] = (j < nb) ? (ident ? j : (int64_t)list[j]) : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) ee[u] = (tt[u] >= 0) ? w.bexp[tt[u]] : -1;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ee[u] == e) {
+                        const int pos = atomicAdd(&ncand, 1);
+                        cb[pos] = w.bval[tt[u]];
+                        ct[pos] = (int32_t)tt[u];
+                    }
+                __syncthreads();
+                const int n = ncand;
+                __syncthreads();
+                if (n > kResolveCap - U * (int)blockDim.x) merge(n);
+            }
+            const int n = ncand;
+            __syncthreads();
+            if (n > 0) merge(n);
+        }
     }
+    const bool changed = nbe > 0;
     if (changed) {
         const int m = nhold;
         for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
         publish_expert(w, e, k, m, hb);
     }
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const int done = atomicAdd(&ctl->done_blocks, 1);
-        if (done == (int)gridDim.x - 1) {
-            ctl->done_blocks = 0;
-            ctl->identity = 0;
-            ctl->cur = cur ^ 1;
-            ctl->rounds_phase += 1;
-            __threadfence();
-        }
+    // where the tail finds the bidders if it takes over after this round
+    // (no block of this kernel reads these fields)
+    if (e == 0 && tid == 0) {
+        ctl->cur = cur ^ 1;
+        ctl->identity = 0;
+        ctl->rounds_phase = round + 1;
     }
 }
 
@@ -583,7 +642,7 @@ template <int NCH>
 static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
                         AucStatsDev* st, hipStream_t stream) {
-    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(256), 48 * E, stream, s,
+    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(256), 48 * E + 4 * kSetupChunk, stream, s,
                        E, k, w, scan);
     const size_t lds = ssp_lds_bytes(E);
     if (ssp_c_in_lds(E))
@@ -615,7 +674,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
             hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3(nblk), dim3(256), 0,
                                stream, s, T, E, w, scan, r, eps);
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
-                               E, k, w);
+                               E, k, w, r);
         }
         launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, stream);
         if (eps <= eps_end) break;

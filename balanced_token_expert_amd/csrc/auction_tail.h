@@ -120,38 +120,63 @@ BASE_DEV void wave_argmin_f64(double& v, int& i) {
 
 BASE_DEV float sani(float x, Sani sn) { return (sn.fix && !is_finite_f32(x)) ? sn.repl : x; }
 
-// C and Ct of every expert from its holders after the bulk rounds (one block
-// per expert; waves split the holders, lanes the columns), and the slot of
-// every holder.
+// C and Ct of every expert from its holders after the bulk rounds, and the
+// slot of every holder. One block per expert: the holders' ids are staged in
+// LDS (up to kSetupChunk at a time), then each wave takes groups of holders
+// whose rows it loads together (32 / NCH rows in flight), lanes over the
+// columns; the four waves' minima meet in LDS.
+constexpr int kSetupChunk = 4096;
+
 template <int NCH>
 __global__ __launch_bounds__(256) void auc_ssp_setup_kernel(const float* s, int64_t E, int64_t k,
                                                             AucWs w, const ScoreScan* scan) {
     extern __shared__ __attribute__((aligned(16))) char sm[];
     double* pv = (double*)sm;                   // 4 waves x E
     int32_t* pt = (int32_t*)(pv + 4 * E);       // 4 waves x E
+    int32_t* hl = pt + 4 * E;                   // kSetupChunk holder ids
     const AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->nbid[ctl->cur] == 0) return;
     const int a = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const Sani sn = read_sani(scan);
     const int n = w.cnt[a];
+    constexpr int U = NCH >= 16 ? 2 : 32 / NCH;
     double bv[NCH];
     int bt[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) { bv[c] = DBL_MAX; bt[c] = kNoTok; }
-    for (int i = wave; i < n; i += 4) {
-        const int h = w.stok[(int64_t)a * k + i];
-        if (lane == 0) w.slot_of[h] = i;
-        const float* row = s + (int64_t)h * E;
-        const double sa = (double)sani(row[a], sn);
+    for (int c0 = 0; c0 < n; c0 += kSetupChunk) {
+        const int cn = min(kSetupChunk, n - c0);
+        for (int i = threadIdx.x; i < cn; i += blockDim.x) {
+            const int h = w.stok[(int64_t)a * k + c0 + i];
+            hl[i] = h;
+            w.slot_of[h] = c0 + i;
+        }
+        __syncthreads();
+        for (int i0 = wave * U; i0 < cn; i0 += 4 * U) {
+            int h[U];
+            float v[U][NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int e = lane + 64 * c;
-            if (e < E) {
-                const double v = sa - (double)sani(row[e], sn);
-                argmin_merge(bv[c], bt[c], v, h);
+            for (int u = 0; u < U; ++u) {
+                h[u] = i0 + u < cn ? hl[i0 + u] : -1;
+                if (h[u] >= 0) load_row<NCH>(s, h[u], E, lane, sn, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (h[u] < 0) continue;
+                float ra = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    if (c == (a >> 6)) ra = v[u][c];
+                const double sa = (double)__builtin_bit_cast(float, readlane_i32(__builtin_bit_cast(int, ra), a & 63));
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int e = lane + 64 * c;
+                    if (e < E) argmin_merge(bv[c], bt[c], sa - (double)v[u][c], h[u]);
+                }
             }
         }
+        __syncthreads();
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
