@@ -29,8 +29,8 @@ BASE_MIX_RESIDUAL, BASE_MIX_CONVEX = 0, 1
 EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
             "base_assign_auction", "base_route_greedy", "base_layer_forward",
             "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
-            "base_workspace_bytes_ex", "base_set_phase_events")
-STATS_BYTES = 8 + 16 * 8 * 2
+            "base_workspace_bytes_ex", "base_set_phase_events", "base_set_auction_events")
+STATS_BYTES = 8 + 16 * 8 * 3
 
 
 class AuctionCfg(ctypes.Structure):
@@ -84,9 +84,10 @@ def load(path: str = LIB_PATH):
     lib.base_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i64, i32, i32]
     lib.base_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.base_set_phase_events.argtypes = [P, i32]
+    lib.base_set_auction_events.argtypes = [P, i32]
     for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
               "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
-              "base_set_phase_events"):
+              "base_set_phase_events", "base_set_auction_events"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,6 +190,7 @@ class AuctionStats:
     phases: int
     bids: list
     rounds: list
+    tail: list
 
 
 def read_stats(buf: torch.Tensor) -> AuctionStats:
@@ -197,7 +199,7 @@ def read_stats(buf: torch.Tensor) -> AuctionStats:
     tail = raw[8:STATS_BYTES].view(torch.int64).tolist()
     ph = head[1]
     n = min(ph, 16)
-    return AuctionStats(head[0], ph, tail[:16][:n], tail[16:32][:n])
+    return AuctionStats(head[0], ph, tail[:16][:n], tail[16:32][:n], tail[32:48][:n])
 
 
 def new_stats(device="cuda") -> torch.Tensor:
@@ -397,3 +399,9 @@ def base_layer_backward_ex(h, w, W1, W2, act: int, assign, scores, dy, mix: int 
 def base_set_phase_events(events, n: int):
     """events: a ctypes array of hipEvent_t handles (or None to stop)."""
     _check(load().base_set_phase_events(events, int(n)), "base_set_phase_events")
+
+
+def base_set_auction_events(events, n: int):
+    """events: a ctypes array of hipEvent_t handles, four per eps phase (or
+    None to stop)."""
+    _check(load().base_set_auction_events(events, int(n)), "base_set_auction_events")

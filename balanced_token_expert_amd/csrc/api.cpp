@@ -119,9 +119,17 @@ void mark(int i, hipStream_t st) {
     if (i < g_nevents && g_events[i]) hipEventRecord(g_events[i], st);
 }
 
+constexpr int kAucEvents = 64;
+thread_local hipEvent_t g_auc_events[kAucEvents];
+thread_local int g_auc_nevents = 0;
+
 int hip_rc(hipError_t e) { return e == hipSuccess ? BASE_OK : BASE_ERR_HIP; }
 
 }  // namespace
+
+void base::auction_mark(int i, hipStream_t st) {
+    if (i < g_auc_nevents && g_auc_events[i]) hipEventRecord(g_auc_events[i], st);
+}
 
 // Shared body of base_layer_forward (o == nullptr: eq. 1, plain experts)
 // and base_layer_forward_ex.
@@ -383,6 +391,14 @@ const char* base_strerror(int code) {
         case BASE_ERR_UNBALANCED: return "given assignment is not balanced";
         default: return "unknown error";
     }
+}
+
+int base_set_auction_events(void** events, int n) {
+    if (n < 0 || n > kAucEvents) return BASE_ERR_INVALID_ARG;
+    if (!events) n = 0;
+    for (int i = 0; i < kAucEvents; ++i) g_auc_events[i] = (events && i < n) ? (hipEvent_t)events[i] : nullptr;
+    g_auc_nevents = n;
+    return BASE_OK;
 }
 
 int base_set_phase_events(void** events, int n) {

@@ -245,7 +245,7 @@ __global__ void auc_init_kernel(AucWs w, int64_t E, const ScoreScan* scan, int64
     if (i == 0) {
         st->status = (scan->min_key == 0xffffffffu && n > 0) ? kErrNonfinite : 0;
         st->phases = 0;
-        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; }
+        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; st->tail[q] = 0; }
         w.ctl->bids_total = 0;
         w.ctl->abort = st->status != 0;
     }
@@ -642,8 +642,10 @@ template <int NCH>
 static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const AucWs& w,
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
                         AucStatsDev* st, hipStream_t stream) {
+    auction_mark(4 * phase + 1, stream);
     hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(256), 48 * E + 4 * kSetupChunk, stream, s,
                        E, k, w, scan);
+    auction_mark(4 * phase + 2, stream);
     const size_t lds = ssp_lds_bytes(E);
     if (ssp_c_in_lds(E))
         hipLaunchKernelGGL((auc_ssp_kernel<NCH, true>), dim3(1), dim3(kSspThreads), lds, stream, s,
@@ -666,6 +668,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     if (bid_blocks > 2048) bid_blocks = 2048;
     double eps = eps_start;
     for (int phase = 0;; ++phase) {
+        auction_mark(4 * phase, stream);
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
                            stream, w, T, E, st);
         for (int r = 0; r < rounds; ++r) {
@@ -677,6 +680,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
                                E, k, w, r);
         }
         launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, stream);
+        auction_mark(4 * phase + 3, stream);
         if (eps <= eps_end) break;
         eps = eps / eps_factor;
         if (eps < eps_end) eps = eps_end;

@@ -713,6 +713,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
         if (phase < 16) {
             st->bids[phase] = (long long)pb;
             st->rounds[phase] = ctl->rounds_phase + batches;
+            st->tail[phase] = placed;
         }
         st->phases = phase + 1;
         if (stop && !aborted) st->status = kErrNotConverged;

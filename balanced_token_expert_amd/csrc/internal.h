@@ -19,7 +19,11 @@ struct AucStatsDev {
     int32_t phases;
     int64_t bids[16];
     int64_t rounds[16];
+    int64_t tail[16];
 };
+
+// Optional event marks of the auction's parts (base_set_auction_events).
+void auction_mark(int i, hipStream_t st);
 
 // ---- gemm.cpp / gemm.hip
 // s = h w^T, fp32 out; also fills *scan (must be initialised by scan_init).

@@ -65,7 +65,7 @@ __global__ void stats_reset_kernel(AucStatsDev* st) {
     if (threadIdx.x == 0) {
         st->status = 0;
         st->phases = 0;
-        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; }
+        for (int q = 0; q < 16; ++q) { st->bids[q] = 0; st->rounds[q] = 0; st->tail[q] = 0; }
     }
 }
 

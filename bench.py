@@ -38,30 +38,36 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PHASES = ("affinity", "route", "ffn1", "ffn2")
 
-# HBM bytes per launch of the expert products at the large workload, from
-# two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
-# scaled by what the same counters read for a 1 GiB copy (--copy-probe):
-# fetched = FETCH_SIZE * 1024 * FETCH_SCALE, written = WRITE_SIZE * 1024.
-# They describe the kernel built from the sources whose hash is recorded;
-# after any change to those sources the figure is stale and reported as null.
-TRAFFIC_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
-                   "balanced_token_expert_amd/csrc/gemm_dma.h",
+# HBM bytes per launch of the step's kernels at the large workload, from
+# two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch,
+# mean over the dispatches of the profiled steps) scaled by what the same
+# counters read for a 1 GiB copy (--copy-probe): fetched = FETCH_SIZE * 1024
+# * FETCH_SCALE, written = WRITE_SIZE * 1024 * WRITE_SCALE. Each figure
+# describes the kernel built from the sources whose hash is recorded; after
+# any change to those sources it is stale and reported as null.
+GEMM_SOURCES = ("balanced_token_expert_amd/csrc/gemm.hip",
+                "balanced_token_expert_amd/csrc/gemm_dma.h",
+                "balanced_token_expert_amd/csrc/common.h")
+AUCTION_SOURCES = ("balanced_token_expert_amd/csrc/auction.hip",
+                   "balanced_token_expert_amd/csrc/auction_tail.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99994
+FETCH_SCALE = 1.99996
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
-    # kernel: (workload, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "ffn1": ("large_t64k_e128_d2048", "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d",
-             2504542.3, 1181884.7),
-    "ffn2": ("large_t64k_e128_d2048", "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d",
-             2918153.5, 353082.8),
+    # kernel: (workload, sources, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "ffn1": ("large_t64k_e128_d2048", GEMM_SOURCES,
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2787486.0, 1193201.8),
+    "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 3765091.3, 373307.1),
+    "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
+                     "89486a009772ee29d0221c21404e0eafc1b87ad3e046cd188afc9b0bd43a0f98", 7746.7, 40.0),
 }
 
 
-def sources_sha256():
+def sources_sha256(files):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -71,9 +77,9 @@ def measured_traffic(kernel, workload):
     """HBM bytes per launch from the recorded counters, or None when they
     were taken on another workload or on different kernel sources."""
     rec = MEASURED_TRAFFIC.get(kernel)
-    if rec is None or rec[0] != workload or rec[1] != sources_sha256():
+    if rec is None or rec[0] != workload or rec[2] != sources_sha256(rec[1]):
         return None
-    return rec[2] * 1024 * FETCH_SCALE + rec[3] * 1024 * WRITE_SCALE
+    return rec[3] * 1024 * FETCH_SCALE + rec[4] * 1024 * WRITE_SCALE
 
 
 def log(*a):
@@ -497,6 +503,256 @@ def copy_probe(nbytes=1 << 30, reps=4):
                       "GB/s_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def layer_bufs(T, E, D, F, dtype, hd):
+    import torch
+    from balanced_token_expert_amd import api
+    return dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+                scores=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+                out=torch.empty_like(hd), stats=api.new_stats(),
+                ws=api.workspace(api.BASE_OP_LAYER, T, E, D, F,
+                                 api.BASE_BF16 if dtype == "bf16" else api.BASE_F32))
+
+
+def route_parts(aev, base, nph):
+    """Bulk rounds, setup of the phase ends and the augmenting-path kernel,
+    summed over the eps phases of one call (ms), and the tail launches."""
+    bulk = sum(aev.ms(base + 4 * p, base + 4 * p + 1) for p in range(nph))
+    setup = sum(aev.ms(base + 4 * p + 1, base + 4 * p + 2) for p in range(nph))
+    tail = [aev.ms(base + 4 * p + 2, base + 4 * p + 3) for p in range(nph)]
+    return bulk, setup, tail
+
+
+def phase_rooflines(wl, ph, st, nph):
+    """Every phase of the step against the bound that limits it, with the
+    algorithmic bytes or flops of one call (per-unit figures: a score row
+    and an fp64 bid per auction bid, 4E + 8 bytes; T*D*b + E*D*b + 4TE for
+    the affinity; 4TE + 4T + 4E for greedy; 2TDF flops per expert product)."""
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    b = 2 if wl.dtype == "bf16" else 4
+    out = {}
+    if "affinity" in ph:
+        byt = T * D * b + E * D * b + 4 * T * E
+        out["affinity"] = {"bound": "hbm", "algorithmic_bytes": byt,
+                           "achieved_GBps": round(byt / (ph["affinity"] * 1e-3) / 1e9, 1),
+                           "frac": round(byt / (ph["affinity"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    nb = int(sum(st.bids))
+    byt = nb * (4 * E + 8) + 8 * T
+    out["route"] = {"bound": "hbm (latency-bound in practice)", "bids": nb,
+                    "algorithmic_bytes": byt,
+                    "achieved_GBps": round(byt / (ph["route"] * 1e-3) / 1e9, 2),
+                    "frac": round(byt / (ph["route"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                    "bids_per_s": round(nb / (ph["route"] * 1e-3), 1),
+                    "dependent_steps": int(sum(st.rounds)),
+                    "us_per_dependent_step": round(1e3 * ph["route"] / max(sum(st.rounds), 1), 3)}
+    nt = int(sum(st.tail))
+    if "auction_tail" in ph and ph["auction_tail"] > 0:
+        byt = nt * (4 * E + 8)
+        out["auction_tail"] = {"bound": "hbm (latency-bound in practice)", "tokens_placed": nt,
+                               "algorithmic_bytes": byt,
+                               "achieved_GBps": round(byt / (ph["auction_tail"] * 1e-3) / 1e9, 3),
+                               "frac": round(byt / (ph["auction_tail"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 6),
+                               "us_per_token_placed": round(1e3 * ph["auction_tail"] / max(nt, 1), 2)}
+    if F is not None:
+        fl = 2.0 * T * D * F
+        for k in ("ffn1", "ffn2"):
+            if k in ph:
+                out[k] = {"bound": "mfma", "algorithmic_flops": fl,
+                          "achieved_TFLOPs": round(fl / (ph[k] * 1e-3) / 1e12, 1),
+                          "frac": round(fl / (ph[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if "greedy" in ph:
+        byt = 4 * T * E + 4 * T + 4 * E
+        out["greedy"] = {"bound": "hbm", "algorithmic_bytes": byt,
+                         "achieved_GBps": round(byt / (ph["greedy"] * 1e-3) / 1e9, 1),
+                         "frac": round(byt / (ph["greedy"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def run_step(wid, steps, warmup):
+    """The timed step on one workload: base_layer_forward (BALANCED) plus
+    greedy routing of the same scores. Returns the step time, the mean time
+    of every phase (library events on the call's stream) and the auction's
+    counters."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    wl = W.workload(wid)
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    h, w, W1, W2 = gen_inputs(wl)
+    hd, wd = to_dev(h, wl.dtype), to_dev(w, wl.dtype)
+    W1d, W2d = stack_dev(W1, wl.dtype), stack_dev(W2, wl.dtype)
+    torch.cuda.synchronize()
+    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=100 * T * 5)
+    nph = n_phases(wl)
+    lay = layer_bufs(T, E, D, F, wl.dtype, hd)
+    gr = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+              counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+              ws=api.workspace(api.BASE_OP_GREEDY, T, E))
+    nsteps = warmup + steps
+    ev = HipEvents(6 * nsteps)
+    aev = HipEvents(4 * nph * nsteps)
+    gr_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(nsteps)]
+
+    def step(i):
+        api.base_set_phase_events(ev.block(6 * i), 6)
+        api.base_set_auction_events(aev.block(4 * nph * i), 4 * nph)
+        api.base_layer_forward(hd, wd, W1d, W2d, act, api.BASE_ROUTE_BALANCED, c, **lay)
+        gr_ev[i][0].record()
+        api.base_route_greedy(lay["scores"], **gr)
+        gr_ev[i][1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    wall0 = time.perf_counter()
+    for i in range(warmup, nsteps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    api.base_set_phase_events(None, 0)
+    api.base_set_auction_events(None, 0)
+    ms_step = t_start.elapsed_time(t_end) / steps
+    ph = {p: [] for p in PHASES + ("greedy", "bulk_rounds", "tail_setup", "auction_tail")}
+    tails = []
+    for i in range(warmup, nsteps):
+        b = 6 * i
+        for j, p in enumerate(PHASES):
+            ph[p].append(ev.ms(b + j, b + j + 1))
+        ph["greedy"].append(gr_ev[i][0].elapsed_time(gr_ev[i][1]))
+        bulk, setup, tail = route_parts(aev, 4 * nph * i, nph)
+        ph["bulk_rounds"].append(bulk)
+        ph["tail_setup"].append(setup)
+        ph["auction_tail"].append(sum(tail))
+        tails.extend(tail)
+    avg = {p: float(np.mean(v)) for p, v in ph.items()}
+    st = api.read_stats(lay["stats"])
+    a = lay["assign"].cpu().numpy()
+    balanced = bool((np.bincount(a, minlength=E) == T // E).all())
+    gcount = gr["counts"].cpu().numpy()
+    out = {"workload": wl.name, "T": T, "E": E, "D": D, "F": F, "dtype": wl.dtype, "act": wl.act,
+           "eps": f"{wl.eps_start}->{wl.eps_end} x1/{wl.eps_factor}",
+           "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
+           "tokens_per_s": round(T / (ms_step * 1e-3), 1), "wall_s_timed": round(wall, 3),
+           "phase_ms": {p: round(v, 4) for p, v in avg.items()},
+           "auction": {"status": st.status, "balanced": balanced, "bids_per_phase": st.bids,
+                       "depth_per_phase": st.rounds, "tail_tokens_per_phase": st.tail,
+                       "tail_launch_ms_mean": round(float(np.mean(tails)), 4)},
+           "greedy_load": {"max_over_mean": round(float(gcount.max() / (T / E)), 3)},
+           "rooflines": phase_rooflines(wl, avg, st, nph)}
+    extra = dict(wl=wl, h=h, w=w, W1=W1, W2=W2, hd=hd, wd=wd, W1d=W1d, W2d=W2d, act=act, c=c,
+                 lay=lay, avg=avg, st=st, tails=tails)
+    return out, extra
+
+
+def run_assign(wid, steps, warmup):
+    """The assignment-only workload: affinity, then base_assign_auction
+    (with grouping); median solve ms and its parts (library events)."""
+    import torch
+    from balanced_token_expert_amd import api
+    from balanced_token_expert_amd import workloads as W
+    wl = W.workload(wid)
+    T, E = wl.T, wl.E
+    h, w, _, _ = gen_inputs(wl)
+    hd, wd = to_dev(h, wl.dtype), to_dev(w, wl.dtype)
+    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=100 * T * 5)
+    nph = n_phases(wl)
+    bufs = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
+                perm=torch.empty(T, dtype=torch.int32, device="cuda"),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                prices=torch.empty(E, dtype=torch.float64, device="cuda"),
+                stats=api.new_stats(), ws=api.workspace(api.BASE_OP_AUCTION, T, E))
+    scores = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    nsteps = warmup + steps
+    aev = HipEvents(4 * nph * nsteps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
+    for i in range(nsteps):
+        api.base_set_auction_events(aev.block(4 * nph * i), 4 * nph)
+        evs[i][0].record()
+        api.base_affinity(hd, wd, scores)
+        evs[i][1].record()
+        api.base_assign_auction(scores, c, **bufs)
+        evs[i][2].record()
+        torch.cuda.synchronize()
+    api.base_set_auction_events(None, 0)
+    aff = [evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, nsteps)]
+    sol = [evs[i][1].elapsed_time(evs[i][2]) for i in range(warmup, nsteps)]
+    parts = [route_parts(aev, 4 * nph * i, nph) for i in range(warmup, nsteps)]
+    st = api.read_stats(bufs["stats"])
+    asg = bufs["assign"].cpu().numpy()
+    balanced = bool((np.bincount(asg, minlength=E) == T // E).all())
+    avg = {"affinity": float(np.mean(aff)), "route": float(np.median(sol)),
+           "bulk_rounds": float(np.mean([p[0] for p in parts])),
+           "tail_setup": float(np.mean([p[1] for p in parts])),
+           "auction_tail": float(np.mean([sum(p[2]) for p in parts]))}
+    return {"workload": wl.name, "T": T, "E": E, "D": wl.D, "dtype": wl.dtype,
+            "eps": f"{wl.eps_start}->{wl.eps_end} x1/{wl.eps_factor}", "reps": steps,
+            "auction_solve_ms_median": round(float(np.median(sol)), 4),
+            "auction_solve_ms_min": round(float(np.min(sol)), 4),
+            "tokens_per_s": round(T / (float(np.median(np.add(aff, sol))) * 1e-3), 1),
+            "phase_ms": {p: round(v, 4) for p, v in avg.items()},
+            "auction": {"status": st.status, "balanced": balanced, "bids_per_phase": st.bids,
+                        "depth_per_phase": st.rounds, "tail_tokens_per_phase": st.tail},
+            "rooflines": phase_rooflines(wl, avg, st, nph)}
+
+
+def n_phases(wl):
+    n, eps = 1, wl.eps_start
+    while eps > wl.eps_end:
+        eps = max(eps / wl.eps_factor, wl.eps_end)
+        n += 1
+    return n
+
+
+def dominant_roofline(wl, avg, st, tails):
+    """Roofline of the kernel with the most time in the step: the auction's
+    augmenting-path kernel (one launch per eps phase), an expert product or
+    the affinity product (one launch each)."""
+    T, E, D, F = wl.T, wl.E, wl.D, wl.F
+    per_step = {"auction_tail": avg["auction_tail"], "ffn1": avg["ffn1"], "ffn2": avg["ffn2"],
+                "affinity": avg["affinity"]}
+    kern = max(per_step, key=per_step.get)
+    if kern == "auction_tail":
+        nt = int(sum(st.tail))
+        launch_ms = float(np.mean(tails))
+        per_launch = nt * (4 * E + 8) / max(len(st.tail), 1)
+        ach = per_launch / (launch_ms * 1e-3) / 1e9
+        traffic = measured_traffic("auction_tail", wl.name)
+        return {"kernel": f"auc_ssp_kernel (augmenting paths that end each eps phase; "
+                          f"{len(st.tail)} launches per step, {avg['auction_tail']:.3f} ms per step)",
+                "bound": "hbm", "achieved": round(ach, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 7),
+                "traffic": None if traffic is None else round(traffic),
+                "algorithmic_bytes_per_launch": round(per_launch),
+                "per_unit": f"{4 * E + 8} bytes per token placed (a score row and an fp64 bid)",
+                "tokens_placed_per_step": nt, "avg_launch_ms": round(launch_ms, 4),
+                "us_per_token_placed": round(1e3 * avg["auction_tail"] / max(nt, 1), 2)}
+    if kern in ("ffn1", "ffn2"):
+        fl = 2.0 * T * D * F
+        ach = fl / (avg[kern] * 1e-3) / 1e12
+        traffic = measured_traffic(kern, wl.name)
+        return {"kernel": f"{kern} (expert GEMM {'1' if kern == 'ffn1' else '2'}, "
+                          f"{E} experts x [{T // E}x{D if kern == 'ffn1' else F}]"
+                          f"x[{D if kern == 'ffn1' else F}x{F if kern == 'ffn1' else D}])",
+                "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "algorithmic_flops": fl, "avg_launch_ms": round(avg[kern], 4)}
+    byt = T * D * 2 + E * D * 2 + 4 * T * E
+    ach = byt / (avg["affinity"] * 1e-3) / 1e9
+    return {"kernel": "affinity product", "bound": "hbm", "achieved": round(ach, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": None, "algorithmic_bytes": byt, "avg_launch_ms": round(avg["affinity"], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,6 +760,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=5, help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
     ap.add_argument("--no-auction", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -516,121 +773,65 @@ def main():
 
     import torch
     from balanced_token_expert_amd import api
-    from balanced_token_expert_amd import workloads as W
 
     if args.copy_probe:
         copy_probe()
         return
     api.load()
     torch.cuda.init()
-    wl = W.workload(args.workload)
-    T, E, D, F = wl.T, wl.E, wl.D, wl.F
-    h, w, W1, W2 = gen_inputs(wl)
-    hd, wd = to_dev(h, wl.dtype), to_dev(w, wl.dtype)
-    W1d, W2d = stack_dev(W1, wl.dtype), stack_dev(W2, wl.dtype)
-    torch.cuda.synchronize()
-    log(f"[bench] inputs on device: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
-
-    act = api.BASE_ACT_GELU if wl.act == "gelu" else api.BASE_ACT_RELU
-    c = api.cfg(wl.eps_start, wl.eps_end, wl.eps_factor, max_bids=100 * T * 5)
-    lay = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
-               scores=torch.empty((T, E), dtype=torch.float32, device="cuda"),
-               perm=torch.empty(T, dtype=torch.int32, device="cuda"),
-               out=torch.empty_like(hd), stats=api.new_stats(),
-               ws=api.workspace(api.BASE_OP_LAYER, T, E, D, F,
-                                api.BASE_BF16 if wl.dtype == "bf16" else api.BASE_F32))
-    gr = dict(assign=torch.empty(T, dtype=torch.int32, device="cuda"),
-              counts=torch.empty(E, dtype=torch.int32, device="cuda"),
-              perm=torch.empty(T, dtype=torch.int32, device="cuda"),
-              offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
-              ws=api.workspace(api.BASE_OP_GREEDY, T, E))
-
-    nsteps = args.warmup + args.steps
-    ev = HipEvents(6 * nsteps)
-    gr_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(nsteps)]
-
-    def step(i):
-        api.base_set_phase_events(ev.block(6 * i), 6)
-        api.base_layer_forward(hd, wd, W1d, W2d, act, api.BASE_ROUTE_BALANCED, c, **lay)
-        gr_ev[i][0].record()
-        api.base_route_greedy(lay["scores"], **gr)
-        gr_ev[i][1].record()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log("[bench] warmup done")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    wall0 = time.perf_counter()
-    for i in range(args.warmup, nsteps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    api.base_set_phase_events(None, 0)
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-
-    # per-phase kernel times over the timed steps
-    ph = {p: [] for p in PHASES}
-    ph["greedy"] = []
-    for i in range(args.warmup, nsteps):
-        b = 6 * i
-        for j, p in enumerate(PHASES):
-            ph[p].append(ev.ms(b + j, b + j + 1))
-        ph["greedy"].append(gr_ev[i][0].elapsed_time(gr_ev[i][1]))
-    avg = {p: float(np.mean(v)) for p, v in ph.items()}
-    st = api.read_stats(lay["stats"])
-    a = lay["assign"].cpu().numpy()
-    balanced = bool((np.bincount(a, minlength=E) == T // E).all())
-    gcount = gr["counts"].cpu().numpy()
-
-    # roofline of the dominant kernel (one launch per phase for the products)
-    # the dominant kernel: the longest single launch of the step (an expert
-    # product; the auction is many short latency-bound launches)
-    flops_ffn = 2.0 * T * D * F
-    kern = max(("ffn1", "ffn2"), key=lambda p: avg[p])
-    achieved = flops_ffn / (avg[kern] * 1e-3) / 1e12
-    traffic = measured_traffic(kern, wl.name)
-    roof = {"kernel": f"{kern} (expert GEMM {'1' if kern == 'ffn1' else '2'}, "
-                      f"{E} experts x [{T // E}x{D if kern == 'ffn1' else F}]"
-                      f"x[{D if kern == 'ffn1' else F}x{F if kern == 'ffn1' else D}])",
-            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "algorithmic_flops": flops_ffn, "avg_launch_ms": round(avg[kern], 4)}
-
+    head, x = run_step(args.workload, args.steps, args.warmup)
+    wl, avg, st = x["wl"], x["avg"], x["st"]
+    T, E = wl.T, wl.E
+    log(f"[bench] {wl.name}: {head['ms_per_step']} ms/step")
     res = {"metric": "BASE layer fwd tokens/s at 1 GPU + auction solve ms (T=16k, E=128)",
-           "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded numpy PCG64, shapes of the paper's setting)",
-           "config": {"workload": wl.name, "T": T, "E": E, "D": D, "F": F, "act": wl.act,
+           "config": {"workload": wl.name, "T": T, "E": E, "D": wl.D, "F": wl.F, "act": wl.act,
                       "route": "balanced auction eps 1.0->1e-4 (factor 10) + greedy on the "
                                "same scores", "parallelism": "single GPU, all experts resident"},
-           "phase_ms": {p: round(v, 4) for p, v in avg.items()},
-           "auction": {"status": st.status, "bids_per_phase": st.bids,
-                       "rounds_per_phase": st.rounds, "balanced": balanced},
-           "greedy_load": {"max_over_mean": round(float(gcount.max() / (T / E)), 3),
-                           "max_share": round(float(gcount.max() / T), 5),
-                           "uniform_share": round(1.0 / E, 5)},
-           "roofline": roof, "wall_s_timed": round(wall, 3)}
-    res["greedy_layer"] = greedy_layer(hd, wd, W1d, W2d, act, T, E)
+           "phase_ms": head["phase_ms"], "auction": head["auction"],
+           "greedy_load": head["greedy_load"],
+           "roofline": dominant_roofline(wl, avg, st, x["tails"]),
+           "phase_rooflines": head["rooflines"], "wall_s_timed": head["wall_s_timed"]}
+    res["greedy_layer"] = greedy_layer(x["hd"], x["wd"], x["W1d"], x["W2d"], x["act"], T, E)
     host = None
     if not args.no_cpu_baseline:  # the oracle beside each GPU leg, on eight experts' tokens
-        host = {"h64": W.as_f64(h, wl.dtype), "w64": W.as_f64(w, wl.dtype), "W1": W1, "W2": W2}
+        from balanced_token_expert_amd import workloads as W
+        host = {"h64": W.as_f64(x["h"], wl.dtype), "w64": W.as_f64(x["w"], wl.dtype),
+                "W1": x["W1"], "W2": x["W2"]}
     if not args.no_backward:
-        res["layer_backward"] = layer_backward(wl, hd, wd, W1d, W2d, act, lay, host)
-        res["layer_backward_blocks"] = layer_backward_blocks(wl, hd, wd, W1d, W2d, act, lay, host)
+        res["layer_backward"] = layer_backward(wl, x["hd"], x["wd"], x["W1d"], x["W2d"], x["act"],
+                                               x["lay"], host)
+        res["layer_backward_blocks"] = layer_backward_blocks(wl, x["hd"], x["wd"], x["W1d"],
+                                                             x["W2d"], x["act"], x["lay"], host)
     if not args.no_variants:
-        res["layer_variants"] = layer_variants(wl, hd, wd, W1d, W2d, act, c, host)
+        res["layer_variants"] = layer_variants(wl, x["hd"], x["wd"], x["W1d"], x["W2d"], x["act"],
+                                               x["c"], host)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, x["h"], x["w"], x["W1"], x["W2"])
+    del x, host
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        cfgs = {}
+        for wid in (1, 3, 4):
+            if wid == args.workload:
+                continue
+            o, _ = run_step(wid, 10, 2)
+            cfgs[o["workload"]] = o
+            log(f"[bench] {o['workload']}: {o['ms_per_step']} ms/step")
+            torch.cuda.empty_cache()
+        o = run_assign(2, 10, 2)
+        cfgs[o["workload"]] = o
+        log(f"[bench] {o['workload']}: solve {o['auction_solve_ms_median']} ms")
+        cfgs[head["workload"]] = {k: v for k, v in head.items()}
+        res["configs"] = cfgs
     if not args.no_auction:
         res["auction_solve_ms"] = auction_solve()
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, h, w, W1, W2)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -85,9 +85,9 @@ typedef enum {
  * the optimum itself when eps_end < gap / T, gap being the distance from the
  * optimum to the second-best balanced assignment. max_bids <= 0 means no cap;
  * otherwise the auction stops at its first check after that many bids (after
- * every parallel round, and every 8 bids of each wave of the single-workgroup
- * phase ends) and reports BASE_ERR_NOT_CONVERGED (a safety valve, not part of
- * the method). */
+ * every parallel round, and after every batch of augmenting paths of a
+ * phase's end) and reports BASE_ERR_NOT_CONVERGED (a safety valve, not part
+ * of the method). */
 typedef struct {
     double eps_start;
     double eps_end;
@@ -97,15 +97,18 @@ typedef struct {
 
 /* Written by the device (a DEVICE pointer); read it after the stream has
  * reached the call. status is BASE_OK or BASE_ERR_NOT_CONVERGED /
- * BASE_ERR_NONFINITE / BASE_ERR_UNBALANCED. bids[p] counts the bids of eps
- * phase p (p < 16); rounds[p] is that phase's sequential depth: its parallel
- * bidding rounds (all unassigned tokens bidding at once) plus the number of
- * bids in the longest displacement chain finished after them. */
+ * BASE_ERR_NONFINITE / BASE_ERR_UNBALANCED. For eps phase p (p < 16):
+ * bids[p] counts its bids -- one per token per parallel bidding round (all
+ * unassigned tokens bidding at once) plus one per token that the phase's end
+ * placed by an augmenting path; tail[p] is that last part alone; rounds[p]
+ * is the phase's sequential depth: its parallel rounds plus the batches of
+ * augmenting paths of its end. */
 typedef struct {
     int32_t status;
     int32_t phases;
     int64_t bids[16];
     int64_t rounds[16];
+    int64_t tail[16];
 } base_auction_stats;
 
 /* Workspace queries: the bytes of device scratch memory each entry point
@@ -358,6 +361,19 @@ size_t base_workspace_bytes_ex(int op, int64_t T, int64_t E, int64_t D,
  * Returns BASE_ERR_INVALID_ARG if n is outside [0, 6].
  */
 int base_set_phase_events(void **events, int n);
+
+/*
+ * base_set_auction_events -- optional tracing of the auction's parts. When
+ * `events` is non-NULL, every later auction on this host thread (in
+ * base_assign_auction, base_layer_forward(_ex) and base_layer_backward with
+ * BALANCED routing) records, for eps phase p while 4p + 3 < n (n <= 64), HIP
+ * events (hipEvent_t, created by the caller) on its stream: [4p] before the
+ * phase's parallel rounds, [4p+1] after them, [4p+2] after the setup of the
+ * phase's end (C and the holders' slots), [4p+3] after its augmenting paths.
+ * NULL turns tracing off. Returns BASE_ERR_INVALID_ARG if n is outside
+ * [0, 64].
+ */
+int base_set_auction_events(void **events, int n);
 
 #ifdef __cplusplus
 }

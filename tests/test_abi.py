@@ -24,6 +24,10 @@ def _declared():
 def test_phase_events_arg_check(lib):
     assert lib.base_set_phase_events(None, 0) == 0
     assert lib.base_set_phase_events(None, 9) == api.BASE_ERR_INVALID_ARG
+    assert lib.base_set_auction_events(None, 0) == 0
+    assert lib.base_set_auction_events(None, 64) == 0
+    assert lib.base_set_auction_events(None, 65) == api.BASE_ERR_INVALID_ARG
+    assert lib.base_set_auction_events(None, -1) == api.BASE_ERR_INVALID_ARG
 
 
 @pytest.fixture(scope="module")
@@ -56,9 +60,11 @@ def test_strerror(lib):
 def test_workspace_sizes(lib):
     T, E, D, F = 65536, 128, 2048, 8192
     lay = api.base_workspace_bytes(api.BASE_OP_LAYER, T, E, D, F, api.BASE_BF16)
-    # the hidden activations (T x F bf16) and the scores dominate
+    # the hidden activations (T x F bf16) and the scores dominate; the rest
+    # is per-token bookkeeping and per-expert scratch (the auction's bid bins
+    # take 40 KiB per expert)
     assert lay >= T * F * 2 + T * E * 4
-    assert lay < T * F * 2 + T * E * 4 + 64 * T + 4096 * E + (1 << 20)
+    assert lay < T * F * 2 + T * E * 4 + 64 * T + 48 * 1024 * E + (1 << 20)
     auc = api.base_workspace_bytes(api.BASE_OP_AUCTION, T, E)
     assert 0 < auc < lay
     assert api.base_workspace_bytes(api.BASE_OP_AFFINITY, T, E, D) == 0
