@@ -29,7 +29,8 @@ BASE_MIX_RESIDUAL, BASE_MIX_CONVEX = 0, 1
 EXPORTED = ("base_workspace_bytes", "base_strerror", "base_affinity",
             "base_assign_auction", "base_route_greedy", "base_layer_forward",
             "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
-            "base_workspace_bytes_ex", "base_set_phase_events", "base_set_auction_events")
+            "base_workspace_bytes_ex", "base_set_phase_events", "base_set_auction_events",
+            "base_route_greedy_noalloc")
 STATS_BYTES = 8 + 16 * 8 * 3
 
 
@@ -85,9 +86,10 @@ def load(path: str = LIB_PATH):
     lib.base_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.base_set_phase_events.argtypes = [P, i32]
     lib.base_set_auction_events.argtypes = [P, i32]
+    lib.base_route_greedy_noalloc.argtypes = [P, i64, i64, P, P, P, P, P]
     for f in ("base_affinity", "base_assign_auction", "base_route_greedy", "base_layer_forward",
               "base_layer_forward_ex", "base_layer_backward", "base_layer_backward_ex",
-              "base_set_phase_events", "base_set_auction_events"):
+              "base_set_phase_events", "base_set_auction_events", "base_route_greedy_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -260,6 +262,22 @@ def base_route_greedy(scores: torch.Tensor, assign=None, counts=None, perm=None,
     rc = load().base_route_greedy(_ptr(scores), T, E, _ptr(assign), _ptr(counts), _ptr(perm),
                                   _ptr(offsets), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "base_route_greedy")
+    return {"assign": assign, "counts": counts, "perm": perm, "offsets": offsets}
+
+
+def base_route_greedy_noalloc(scores: torch.Tensor, assign: torch.Tensor, counts=None, perm=None,
+                              offsets=None, stream=None):
+    """base_route_greedy without a workspace (the library's static device
+    scratch); the outputs are the caller's buffers: assign[T] int32, and
+    optionally counts[E], perm[T] and offsets[E+1] int32."""
+    _dev(scores, assign, counts, perm, offsets)
+    T, E = _score_shapes(scores, assign=assign, perm=perm, offsets=offsets)
+    _expect(counts, (E,), torch.int32, "counts")
+    if assign is None:
+        raise ValueError("assign is required")
+    rc = load().base_route_greedy_noalloc(_ptr(scores), T, E, _ptr(assign), _ptr(counts),
+                                          _ptr(perm), _ptr(offsets), _stream(stream))
+    _check(rc, "base_route_greedy_noalloc")
     return {"assign": assign, "counts": counts, "perm": perm, "offsets": offsets}
 
 

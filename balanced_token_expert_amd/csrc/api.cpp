@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace base;
@@ -473,6 +475,47 @@ int base_route_greedy(const float* scores, int64_t T, int64_t E, int32_t* assign
         e = launch_perm(assign, T, E, p, o, counts, 0, nullptr, W + L.permws, st);
     }
     return hip_rc(e);
+}
+
+// ---- greedy routing without a workspace argument. Its scratch (the score
+// scan, the grouping's chunk tables, and the permutation and offsets when
+// the caller does not want them) lives in a fixed device array; every GPU
+// the library runs on holds its own copy until the process ends. Host code
+// never passes the array's name to a kernel: it takes the array's device
+// address from hipGetSymbolAddress, once per device, and uses that.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use), or
+// nullptr if HIP fails.
+static void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+int base_route_greedy_noalloc(const float* scores, int64_t T, int64_t E, int32_t* assign,
+                              int32_t* counts, int32_t* perm, int32_t* offsets,
+                              base_stream_t stream) {
+    if (!scores || !assign || T <= 0 || E <= 0) return BASE_ERR_INVALID_ARG;
+    if ((perm == nullptr) != (offsets == nullptr)) return BASE_ERR_INVALID_ARG;
+    if (T > kMaxT || E > kMaxT) return BASE_ERR_UNSUPPORTED;
+    if ((counts || perm) && E > kPermMaxE) return BASE_ERR_UNSUPPORTED;
+    const Layout L = layout(BASE_OP_GREEDY, T, E, 0, 0, 0);
+    if (L.total > kNoAllocScratchBytes) return BASE_ERR_UNSUPPORTED;
+    void* ws = device_scratch();
+    if (!ws) return BASE_ERR_HIP;
+    return base_route_greedy(scores, T, E, assign, counts, perm, offsets, ws,
+                             kNoAllocScratchBytes, stream);
 }
 
 int base_layer_forward(const void* h, const void* w, const void* W1, const void* W2, int64_t T,

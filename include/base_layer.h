@@ -349,6 +349,25 @@ size_t base_workspace_bytes_ex(int op, int64_t T, int64_t E, int64_t D,
                                int64_t F, int dtype, int sublayers);
 
 /*
+ * base_route_greedy_noalloc -- base_route_greedy for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and results as
+ * base_route_greedy without ws/ws_bytes: its scratch is a static 8 MiB
+ * array in device memory that every GPU the library runs on holds until the
+ * process ends (the current device's copy is used; `stream` must belong to
+ * that device). The call allocates nothing. Every call on one GPU shares
+ * that array, so calls on one GPU must not overlap (use one stream, or
+ * order them); overlapping calls race.
+ * Errors: those of base_route_greedy, plus UNSUPPORTED when the scratch
+ * that T and E need exceeds 8 MiB (about T = 1M tokens at E = 128) and
+ * HIP when the array's device address cannot be obtained; nothing is
+ * enqueued then.
+ */
+int base_route_greedy_noalloc(const float *scores, int64_t T, int64_t E,
+                              int32_t *assign, int32_t *counts, int32_t *perm,
+                              int32_t *offsets, base_stream_t stream);
+
+/*
  * base_set_phase_events -- optional tracing. When `events` is non-NULL, every
  * later base_layer_forward(_ex) and base_layer_backward call on this host
  * thread records n (<= 6) HIP

@@ -91,6 +91,19 @@ def test_auction_host_errors(lib):
                                    1 << 30, None) == api.BASE_ERR_INVALID_ARG
 
 
+def test_greedy_noalloc_host_errors(lib):
+    # beyond the static 8 MiB scratch, and the usual argument checks; all
+    # refused before anything is enqueued
+    assert lib.base_route_greedy_noalloc(FAKE, 1 << 24, 128, FAKE, FAKE, FAKE, FAKE, None) == \
+        api.BASE_ERR_UNSUPPORTED
+    assert lib.base_route_greedy_noalloc(None, 16, 4, FAKE, None, None, None, None) == \
+        api.BASE_ERR_INVALID_ARG
+    assert lib.base_route_greedy_noalloc(FAKE, 16, 4, FAKE, None, FAKE, None, None) == \
+        api.BASE_ERR_INVALID_ARG
+    assert lib.base_route_greedy_noalloc(FAKE, 16, 8192, FAKE, FAKE, None, None, None) == \
+        api.BASE_ERR_UNSUPPORTED
+
+
 def test_layer_host_errors(lib):
     good = api.cfg(1.0, 1e-4, 10.0, 0)
 
