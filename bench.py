@@ -60,7 +60,7 @@ MEASURED_TRAFFIC = {
     "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
              "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 3765091.3, 373307.1),
     "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
-                     "89486a009772ee29d0221c21404e0eafc1b87ad3e046cd188afc9b0bd43a0f98", 7746.7, 40.0),
+                     "89486a009772ee29d0221c21404e0eafc1b87ad3e046cd188afc9b0bd43a0f98", 7601.9, 36.9),
 }
 
 
