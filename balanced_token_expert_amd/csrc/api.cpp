@@ -118,7 +118,7 @@ thread_local hipEvent_t g_events[6];
 thread_local int g_nevents = 0;
 
 void mark(int i, hipStream_t st) {
-    if (i < g_nevents && g_events[i]) hipEventRecord(g_events[i], st);
+    if (i < g_nevents && g_events[i]) (void)hipEventRecord(g_events[i], st);
 }
 
 constexpr int kAucEvents = 64;
@@ -130,7 +130,7 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? BASE_OK : BASE_ERR_HIP; }
 }  // namespace
 
 void base::auction_mark(int i, hipStream_t st) {
-    if (i < g_auc_nevents && g_auc_events[i]) hipEventRecord(g_auc_events[i], st);
+    if (i < g_auc_nevents && g_auc_events[i]) (void)hipEventRecord(g_auc_events[i], st);
 }
 
 // Shared body of base_layer_forward (o == nullptr: eq. 1, plain experts)

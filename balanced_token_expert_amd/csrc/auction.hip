@@ -37,14 +37,19 @@
 
 namespace base {
 
-// multi-CU rounds per phase (at most). Small capacities keep more bidders
-// in conflict for longer: at k = 128 (16k tokens, 128 experts) 32 rounds cut
-// the solve from 12.0 to 9.3 ms, while at k = 256 and 512 more than 16
-// rounds were neutral or slower (measured medians of 10 solves).
-constexpr int kBulkRounds = 16;
-constexpr int kBulkRoundsSmallK = 32;
+// Multi-CU rounds per phase (at most), and the bidders left when the phase
+// end takes over. A round costs 10-20 us whatever its size; the phase end
+// about 6 us per token it places. Small capacities keep more bidders in
+// conflict for longer. Measured (medians of 8 solves, 3 interleaved runs):
+// at k = 128 (16k tokens, 128 experts) 48 rounds and a hand-over at 16
+// bidders took the solve from 5.65 to 5.07 ms; at k = 512 (64k tokens) 20
+// rounds and a hand-over at 24 from 5.42 to 3.83 ms; at k = 256 from 6.83
+// to 6.01 ms (skewed scores) and 2.06 to 2.06 ms (64 experts).
+constexpr int kBulkRounds = 20;
+constexpr int kBulkRoundsSmallK = 48;
 constexpr int64_t kSmallK = 128;
-constexpr int kTailMax = 64;         // bidders left when the tail takes over
+constexpr int kTailMax = 24;
+constexpr int kTailMaxSmallK = 16;
 constexpr int kResolveCap = 2048;    // bidders sorted at once per expert
 constexpr int64_t kBinMax = 2048;    // rounds with at most this many bidders file bids by expert
 constexpr int kOvfCap = 6144;        // an expert's bidders beyond kResolveCap kept in its bin
@@ -276,12 +281,21 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
 template <int NCH>
 __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64_t T, int64_t E,
                                                            AucWs w, const ScoreScan* scan,
-                                                           int round, double eps) {
+                                                           int round, double eps, int tail_max) {
     AucCtl* ctl = w.ctl;
+    const int lane = threadIdx.x & 63;
+    // the round's prices do not change during the kernel: keep this lane's,
+    // loaded with the control word (one round trip)
+    double pv[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t e = lane + 64 * c;
+        pv[c] = (e < E) ? w.pi[e] : 0.0;
+    }
     if (ctl->abort || ctl->bulk_done) return;
     const int cur = round & 1;  // round r bids from list r % 2
     const int64_t nb = ctl->nbid[cur];
-    if (round > 0 && nb <= kTailMax) {
+    if (round > 0 && nb <= tail_max) {
         if (blockIdx.x == 0 && threadIdx.x == 0) ctl->bulk_done = 1;
         return;
     }
@@ -293,16 +307,8 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
     const bool binned = nb <= kBinMax;
     const int32_t* list = cur ? w.list1 : w.list0;
     const Sani sn = read_sani(scan);
-    const int lane = threadIdx.x & 63;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    // the round's prices do not change during the kernel: keep this lane's
-    double pv[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int64_t e = lane + 64 * c;
-        pv[c] = (e < E) ? w.pi[e] : 0.0;
-    }
     int64_t mine = 0;
     // each wave's tokens, the next token's row loaded while the current bids
     int64_t j = wave;
@@ -439,13 +445,17 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
     __shared__ int32_t ot[kBulkKMax];
     __shared__ int32_t ncand, nhold;
     AucCtl* ctl = w.ctl;
+    const int e = blockIdx.x;
+    // the expert's counts are loaded with the control word (one round trip;
+    // unused if the round has nothing to do)
+    const int c0 = w.cnt[e];
+    const int nbin = w.bcnt[e];
     if (ctl->abort || ctl->bulk_done) return;
     const int cur = round & 1;
     const int64_t nb = ctl->nbid[cur];
     const bool ident = round == 0;
     const int32_t* list = cur ? w.list1 : w.list0;
     int32_t* outl = cur ? w.list0 : w.list1;
-    const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     int32_t* stok = w.stok + (int64_t)e * k;
     double* sbid = w.sbid + (int64_t)e * k;
@@ -508,12 +518,11 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         __syncthreads();
     };
 
-    const int c0 = w.cnt[e];
     if (tid == 0) { ncand = 0; nhold = c0; }
     int nbe;  // this round's bidders for e
     if (nb <= kBinMax) {
         // as the bid kernel filed them (at most kBinMax <= kResolveCap)
-        nbe = w.bcnt[e];
+        nbe = nbin;
         if (nbe > 0) {
             for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
             for (int i = tid; i < nbe; i += blockDim.x) {
@@ -664,6 +673,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     const unsigned g1 = (unsigned)(((T > E ? T : E) + 255) / 256);
     hipLaunchKernelGGL(auc_init_kernel, dim3(g1), dim3(256), 0, stream, w, E, scan, T * E, st, assign, T);
     const int rounds = (k > kBulkKMax) ? 0 : (k <= kSmallK ? kBulkRoundsSmallK : kBulkRounds);
+    const int tail_max = k <= kSmallK ? kTailMaxSmallK : kTailMax;
     int64_t bid_blocks = (T + 15) / 16;
     if (bid_blocks > 2048) bid_blocks = 2048;
     double eps = eps_start;
@@ -675,7 +685,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
             // round 0: every token bids; later rounds: the returned few
             const unsigned nblk = (unsigned)(r == 0 ? bid_blocks : (bid_blocks < 256 ? bid_blocks : 256));
             hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3(nblk), dim3(256), 0,
-                               stream, s, T, E, w, scan, r, eps);
+                               stream, s, T, E, w, scan, r, eps, tail_max);
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
                                E, k, w, r);
         }
