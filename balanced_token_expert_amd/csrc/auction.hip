@@ -652,7 +652,9 @@ static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const A
                         const ScoreScan* scan, double eps, int phase, int64_t max_bids,
                         AucStatsDev* st, hipStream_t stream) {
     auction_mark(4 * phase + 1, stream);
-    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(256), 48 * E + 4 * kSetupChunk, stream, s,
+    const int sth = ssp_setup_threads(E);
+    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(sth),
+                       (size_t)(sth / 64) * 12 * E + 4 * kSetupChunk, stream, s,
                        E, k, w, scan);
     auction_mark(4 * phase + 2, stream);
     const size_t lds = ssp_lds_bytes(E);

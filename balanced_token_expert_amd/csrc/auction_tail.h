@@ -124,16 +124,19 @@ BASE_DEV float sani(float x, Sani sn) { return (sn.fix && !is_finite_f32(x)) ? s
 // slot of every holder. One block per expert: the holders' ids are staged in
 // LDS (up to kSetupChunk at a time), then each wave takes groups of holders
 // whose rows it loads together (32 / NCH rows in flight), lanes over the
-// columns; the four waves' minima meet in LDS.
+// columns; the waves' minima meet in LDS. 16 waves when E <= 256 (their
+// minima fit in LDS), else 4.
 constexpr int kSetupChunk = 4096;
+__host__ __device__ static inline int ssp_setup_threads(int64_t E) { return E <= 256 ? 1024 : 256; }
 
 template <int NCH>
-__global__ __launch_bounds__(256) void auc_ssp_setup_kernel(const float* s, int64_t E, int64_t k,
-                                                            AucWs w, const ScoreScan* scan) {
+__global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int64_t E, int64_t k,
+                                                             AucWs w, const ScoreScan* scan) {
     extern __shared__ __attribute__((aligned(16))) char sm[];
-    double* pv = (double*)sm;                   // 4 waves x E
-    int32_t* pt = (int32_t*)(pv + 4 * E);       // 4 waves x E
-    int32_t* hl = pt + 4 * E;                   // kSetupChunk holder ids
+    const int nwv = blockDim.x >> 6;
+    double* pv = (double*)sm;                   // waves x E
+    int32_t* pt = (int32_t*)(pv + nwv * E);     // waves x E
+    int32_t* hl = pt + nwv * E;                 // kSetupChunk holder ids
     const AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->nbid[ctl->cur] == 0) return;
     const int a = blockIdx.x;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(256) void auc_ssp_setup_kernel(const float* s, int6
             w.slot_of[h] = c0 + i;
         }
         __syncthreads();
-        for (int i0 = wave * U; i0 < cn; i0 += 4 * U) {
+        for (int i0 = wave * U; i0 < cn; i0 += nwv * U) {
             int h[U];
             float v[U][NCH];
 #pragma unroll
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void auc_ssp_setup_kernel(const float* s, int6
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         double v = pv[e];
         int t = pt[e];
-        for (int q = 1; q < 4; ++q) argmin_merge(v, t, pv[q * E + e], pt[q * E + e]);
+        for (int q = 1; q < nwv; ++q) argmin_merge(v, t, pv[q * E + e], pt[q * E + e]);
         w.C[(int64_t)a * E + e] = v;
         w.Ct[(int64_t)a * E + e] = t;
     }
