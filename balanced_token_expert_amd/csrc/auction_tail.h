@@ -261,6 +261,38 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
         else __hip_atomic_store(stg + (int64_t)a * nw + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto stale = [&](int a, int b) -> bool { return (sget(a, b >> 6) >> (b & 63)) & 1ull; };
+    // C[a][b] and Ct[a][b] over a's current holders, and the column's stale
+    // bit cleared (one wave; every holder's two scores loaded at once, up to
+    // 512 holders per pass)
+    auto recompute_col = [&](int a, int b) {
+        const int ha = first_lane_i32(cnt[a]);
+        double bv = DBL_MAX;
+        int bt = kNoTok;
+        for (int j0 = 0; j0 < ha; j0 += 8 * 64) {
+            int hh[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int j = j0 + v * 64 + lane;
+                hh[v] = (j < ha) ? ld_fresh_i32(w.stok + (int64_t)a * k + j) : -1;
+            }
+            float sa[8], sb[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
+                sa[v] = hh[v] >= 0 ? sani(row[a], sn) : 0.0f;
+                sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                if (hh[v] >= 0) argmin_merge(bv, bt, (double)sa[v] - (double)sb[v], hh[v]);
+        }
+        wave_argmin_f64(bv, bt);
+        if (lane == 0) {
+            cset(a, b, bv);
+            __hip_atomic_store(Ct + (int64_t)a * E + b, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sput(a, b >> 6, sget(a, b >> 6) & ~(1ull << (b & 63)));
+        }
+    };
 
     for (int64_t e = tid; e < E; e += kSspThreads) {
         p[e] = w.pi[e];
@@ -414,34 +446,8 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 const int32_t* sl = sarc + par * E;
                 for (int i = wave; i < ns; i += kSspWaves) {
                     const int code = first_lane_i32(sl[i]);
-                    const int a = code / (int)E, b = code - a * (int)E;
-                    const int ha = first_lane_i32(cnt[a]);
-                    double bv = DBL_MAX;
-                    int bt = kNoTok;
-                    for (int j0 = 0; j0 < ha; j0 += 8 * 64) {
-                        int hh[8];
-#pragma unroll
-                        for (int v = 0; v < 8; ++v) {
-                            const int j = j0 + v * 64 + lane;
-                            hh[v] = (j < ha) ? ld_fresh_i32(w.stok + (int64_t)a * k + j) : -1;
-                        }
-                        float sa[8], sb[8];
-#pragma unroll
-                        for (int v = 0; v < 8; ++v) {
-                            const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
-                            sa[v] = hh[v] >= 0 ? sani(row[a], sn) : 0.0f;
-                            sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
-                        }
-#pragma unroll
-                        for (int v = 0; v < 8; ++v)
-                            if (hh[v] >= 0) argmin_merge(bv, bt, (double)sa[v] - (double)sb[v], hh[v]);
-                    }
-                    wave_argmin_f64(bv, bt);
-                    if (lane == 0) {
-                        cset(a, b, bv);
-                        __hip_atomic_store(Ct + (int64_t)a * E + b, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        sput(a, b >> 6, sget(a, b >> 6) & ~(1ull << (b & 63)));
-                    }
+                    const int a = code / (int)E;
+                    recompute_col(a, code - a * (int)E);
                 }
                 __syncthreads();
                 relax(sl, ns, true, fle, fqe, nf, ln, par ^ 1);
@@ -697,6 +703,13 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 const unsigned long long nb_ = __ballot(bad[c] && in), nu = __ballot(upd[c] && in);
                 if (c < nw && lane == 0 && (nb_ | nu)) sput(x, c, (sget(x, c) & ~nu) | nb_);
             }
+            // the arc this expert's path left by: its mover was that column's
+            // cheapest holder, so the column is usually stale now, and the
+            // next batch's tree tends to use it again -- recompute it here,
+            // in parallel with the other touched experts, rather than in a
+            // repair step of the next batch's rounds
+            const int xb = first_lane_i32(nx[x]);
+            if (xb >= 0 && stale(x, xb)) recompute_col(x, xb);
             if (lane == 0) head[x] = -1;
         }
         __syncthreads();
