@@ -220,6 +220,74 @@ def test_auction_bid_cap_reports_not_converged():
     assert ((perm >= 0) & (perm < 4096)).all()
 
 
+def test_auction_one_expert_oversubscribed():
+    # every token's best expert is 0 when the first eps phase starts: its
+    # first round sends all 16384 bidders to one expert, more than the
+    # resolve kernel keeps in LDS plus the expert's bin (8192), which takes
+    # its re-scanning path (k = 2048 keeps the parallel rounds on)
+    rng = np.random.default_rng(21)
+    T, E = 16384, 8
+    s32 = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    s32[:, 0] += 3.0
+    res = api.base_assign_auction(to_dev(s32, "f32"), api.cfg(1.0, 1e-3, 10.0, 50_000_000))
+    _sync()
+    _, st = _check_auction(s32, res, 1e-3)
+    assert all(0 <= t <= b for t, b in zip(st.tail, st.bids)), st
+
+
+class _HipEvents:
+    """hipEvent_t handles for the library's optional timing marks."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        assert self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[a], self.ev[b]) == 0
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def test_auction_phase_events_and_tail_counts():
+    # three eps phases (1.0, 0.1, 0.01): four marks each, in stream order
+    wl = _wl(SMALL[2], wid=903)
+    host, dev = inputs(wl, experts=False)
+    s = api.base_affinity(dev["h"], dev["w"])
+    ev = _HipEvents(12)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        api.base_set_auction_events(ev.ct.addressof(ev.ev), 12)
+        t0.record()
+        res = api.base_assign_auction(s, api.cfg(1.0, 1e-2, 10.0, 50_000_000))
+        t1.record()
+        api.base_set_auction_events(None, 0)
+        _sync()
+        parts = [ev.ms(i, i + 1) for i in range(11)]
+        assert min(parts) >= 0.0, parts
+        assert ev.ms(0, 11) <= t0.elapsed_time(t1) * 1.01 + 0.05
+    finally:
+        api.base_set_auction_events(None, 0)
+        ev.close()
+    s32 = s.cpu().numpy()
+    _, st = _check_auction(s32, res, 1e-2)
+    assert st.phases == 3 and len(st.tail) == 3
+    assert all(0 <= t <= b for t, b in zip(st.tail, st.bids)), st
+
+
 # ------------------------------------------------------------------ layer
 
 def _layer_ref(wl, host, a, s32, experts=None):
