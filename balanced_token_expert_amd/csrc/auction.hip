@@ -56,6 +56,8 @@ constexpr int kOvfCap = 6144;        // an expert's bidders beyond kResolveCap k
 static_assert(kBinMax <= kResolveCap, "a round's bin for one expert must fit the resolve buffer");
 static_assert(kBinMax <= kOvfCap, "the bins hold either a round's bids or the overflow");
 constexpr int kBulkKMax = 2048;      // bulk rounds need k <= this
+constexpr int64_t kLateGWs = 8;      // late rounds (auction_late.h): workgroups,
+constexpr int64_t kLateCapWs = 256;  // and bids per (workgroup, expert) bin
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
 constexpr int32_t kNoTok = 0x7fffffff;
@@ -66,9 +68,13 @@ struct AucCtl {
     int32_t identity;     // the bidder list is 0..T-1 (round 0)
     int32_t nbid[2];
     int32_t abort;        // a device error is set: skip all work
+    int32_t pairs_done;   // the late-round launch owns the rest of the bulk rounds
     unsigned long long bids_total;
     unsigned long long bids_phase;
     long long rounds_phase;
+    unsigned lbar;        // late rounds: barrier arrivals this phase
+    int32_t lnb[2];       // late rounds: next bidders summed over workgroups
+    int32_t lcw[2][16];   // late rounds: each workgroup's next bidders
 };
 
 struct AucWs {
@@ -89,6 +95,10 @@ struct AucWs {
     int32_t* bcnt;     // E   bids filed for each expert this round
     int32_t* bin_t;    // E*kOvfCap  the bidders (few-bidder rounds), else the overflow
     double* bin_v;     // E*kBinMax  their bids (few-bidder rounds)
+    int32_t* llist;    // kLateG*2*T late rounds: each workgroup's bidder lists
+    int32_t* lbin_t;   // kLateG*E*kLateCap  late rounds: bids by (workgroup, expert)
+    double* lbin_v;    // kLateG*E*kLateCap
+    int32_t* lbc;      // kLateG*E  their counts
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -113,6 +123,10 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.bcnt = (int32_t*)p; p += align256(E * 4);
     w.bin_t = (int32_t*)p; p += align256(E * kOvfCap * 4);
     w.bin_v = (double*)p; p += align256(E * kBinMax * 8);
+    w.llist = (int32_t*)p; p += align256(kLateGWs * 2 * T * 4);
+    w.lbin_t = (int32_t*)p; p += align256(kLateGWs * E * kLateCapWs * 4);
+    w.lbin_v = (double*)p; p += align256(kLateGWs * E * kLateCapWs * 8);
+    w.lbc = (int32_t*)p; p += align256(kLateGWs * E * 4);
     return w;
 }
 
@@ -120,7 +134,9 @@ size_t auction_ws_bytes(int64_t T, int64_t E) {
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
            5 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
            align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
-           align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) + 256;
+           align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) +
+           align256(kLateGWs * 2 * T * 4) + align256(kLateGWs * E * kLateCapWs * 4) +
+           align256(kLateGWs * E * kLateCapWs * 8) + align256(kLateGWs * E * 4) + 256;
 }
 
 // ---------------------------------------------------------------- helpers
@@ -267,12 +283,16 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
         AucCtl* c = w.ctl;
         c->cur = 0;
         c->bulk_done = 0;
+        c->pairs_done = 0;
         c->identity = 1;
         c->nbid[0] = (int32_t)T;
         c->nbid[1] = 0;
         c->abort = st->status != 0;
         c->bids_phase = 0;
         c->rounds_phase = 0;
+        c->lbar = 0;
+        c->lnb[0] = 0;
+        c->lnb[1] = 0;
     }
 }
 
@@ -281,39 +301,48 @@ __global__ void auc_phase_start_kernel(AucWs w, int64_t T, int64_t E, const AucS
 template <int NCH>
 __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64_t T, int64_t E,
                                                            AucWs w, const ScoreScan* scan,
-                                                           int round, double eps, int tail_max) {
+                                                           int round, double eps, int tail_max,
+                                                           int late_enter) {
     AucCtl* ctl = w.ctl;
     const int lane = threadIdx.x & 63;
-    // the round's prices do not change during the kernel: keep this lane's,
-    // loaded with the control word (one round trip)
+    const int cur = round & 1;  // round r bids from list r % 2
+    const bool ident = round == 0;
+    const int32_t* list = cur ? w.list1 : w.list0;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    // One round trip for all the first bid needs but its score row: this
+    // lane's prices (fixed for the round), the control word, the score scan
+    // and the wave's first list entry. The entry is read before the count is
+    // known (the list holds T entries; one past the count is ignored).
     double pv[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int64_t e = lane + 64 * c;
         pv[c] = (e < E) ? w.pi[e] : 0.0;
     }
-    if (ctl->abort || ctl->bulk_done) return;
-    const int cur = round & 1;  // round r bids from list r % 2
+    const int32_t first = (!ident && wave < T) ? list[wave] : 0;
+    const Sani sn = read_sani(scan);
+    const int aborted = ctl->abort, done = ctl->bulk_done | ctl->pairs_done;
     const int64_t nb = ctl->nbid[cur];
+    if (aborted || done) return;
     if (round > 0 && nb <= tail_max) {
         if (blockIdx.x == 0 && threadIdx.x == 0) ctl->bulk_done = 1;
+        return;
+    }
+    if (round > 0 && nb <= late_enter) {  // few bidders left: the late launch takes over
+        if (blockIdx.x == 0 && threadIdx.x == 0) ctl->pairs_done = 1;
         return;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         ctl->nbid[cur ^ 1] = 0;
         ctl->bids_phase += (unsigned long long)nb;  // every listed token bids once
     }
-    const bool ident = round == 0;
     const bool binned = nb <= kBinMax;
-    const int32_t* list = cur ? w.list1 : w.list0;
-    const Sani sn = read_sani(scan);
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
     int64_t mine = 0;
     // each wave's tokens, the next token's row loaded while the current bids
     int64_t j = wave;
     float v[NCH], vn[NCH];
-    int64_t t = (j < nb) ? (ident ? j : list[j]) : -1;
+    int64_t t = (j < nb) ? (ident ? j : (int64_t)first) : -1;
     if (t >= 0) load_row<NCH>(s, t, E, lane, sn, v);
     while (t >= 0) {
         const int64_t jn = j + nw;
@@ -357,24 +386,24 @@ __global__ __launch_bounds__(256) void auc_bulk_bid_kernel(const float* s, int64
 // bidders plus the number of holders better than it (binary searches).
 BASE_DEV bool better(double ba, int ta, double bb, int tb) { return ba > bb || (ba == bb && ta < tb); }
 
-// Sort (bid, token) pairs across the wave, best first (bitonic network over
-// the 64 lanes by shuffles).
-BASE_DEV void wave_sort_best(double& b, int& t, int lane) {
-#pragma unroll
-    for (int k2 = 2; k2 <= 64; k2 <<= 1) {
-#pragma unroll
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            const double ob = shfl_xor_f64(b, j);
-            const int ot = __shfl_xor(t, j, 64);
-            const bool take_first = ((lane & j) == 0) == ((lane & k2) == 0);
-            const bool swap = take_first ? better(ob, ot, b, t) : better(b, t, ob, ot);
-            if (swap) { b = ob; t = ot; }
-        }
+// Rank of this lane's (bid, token) pair among those of lanes 0 .. n-1, best
+// first: the number of those lanes holding a better pair. The other lanes'
+// pairs arrive by readlane (a scalar broadcast, a few cycles each), so the
+// count is one short dependent chain; the pairs must be distinct.
+BASE_DEV int wave_rank_best(double b, int t, int n = 64) {
+    int r = 0;
+#pragma unroll 8
+    for (int m = 0; m < n; ++m) {
+        const double bm = readlane_f64(b, m);
+        const int tm = __builtin_amdgcn_readlane(t, m);
+        r += better(bm, tm, b, t) ? 1 : 0;
     }
+    return r;
 }
 
 // Sort cb/ct[0, n) best first (n <= 2048, arrays of the next power of two
-// at least 64): each wave sorts runs of 64 in registers, then runs are merged
+// at least 64): each wave ranks runs of 64 in registers and places them,
+// padded with distinct worst entries, then runs are merged
 // pairwise by rank (an element's place = its index in its run + the partner
 // run's elements ahead of it; ties between runs go to the left run),
 // ping-ponging with ob/ot. Called by every thread of the block.
@@ -382,15 +411,14 @@ BASE_DEV void block_sort_best(double* cb, int32_t* ct, double* ob, int32_t* ot, 
     const int tid = threadIdx.x, lane = tid & 63;
     int P = 64;
     while (P < n) P <<= 1;
-    for (int i = n + tid; i < P; i += blockDim.x) { cb[i] = -DBL_MAX; ct[i] = kNoTok; }
-    __syncthreads();
     const int wv = tid >> 6, nwv = blockDim.x >> 6;
     for (int r = wv; r < P / 64; r += nwv) {
-        double b = cb[r * 64 + lane];
-        int t = ct[r * 64 + lane];
-        wave_sort_best(b, t, lane);
-        cb[r * 64 + lane] = b;
-        ct[r * 64 + lane] = t;
+        const int i = r * 64 + lane;
+        const double b = i < n ? cb[i] : -DBL_MAX;
+        const int t = i < n ? ct[i] : kNoTok - i;
+        const int q = wave_rank_best(b, t);
+        cb[r * 64 + q] = b;
+        ct[r * 64 + q] = t;
     }
     __syncthreads();
     double* sb = cb;
@@ -435,85 +463,110 @@ BASE_DEV void publish_expert(AucWs& w, int e, int64_t k, int m, const double* hb
     }
 }
 
-__global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_t E, int64_t k,
-                                                               AucWs w, int round) {
+constexpr int kResolveThreads = 256;
+constexpr int kSpecHold = 2;  // holder slots prefetched per thread (k <= 512)
+
+__global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64_t T, int64_t E,
+                                                                           int64_t k, AucWs w,
+                                                                           int round) {
     __shared__ double cb[kResolveCap];   // bidders
     __shared__ int32_t ct[kResolveCap];
     __shared__ double hb[kBulkKMax];     // holders, best first
     __shared__ int32_t ht[kBulkKMax];
     __shared__ double ob[kBulkKMax];     // merged
     __shared__ int32_t ot[kBulkKMax];
-    __shared__ int32_t ncand, nhold;
+    __shared__ int32_t rej[kResolveCap];  // a merge's rejected tokens, by rank - k
+    __shared__ int32_t ncand, nhold, rbase;
+    static_assert(kResolveThreads <= kBinMax && kResolveThreads <= kOvfCap,
+                  "one prefetched bin entry per thread");
     AucCtl* ctl = w.ctl;
     const int e = blockIdx.x;
-    // the expert's counts are loaded with the control word (one round trip;
-    // unused if the round has nothing to do)
+    const int tid = threadIdx.x;
+    const int cur = round & 1;
+    int32_t* stok = w.stok + (int64_t)e * k;
+    double* sbid = w.sbid + (int64_t)e * k;
+    // One round trip for the expert's counts, the control word, its holder
+    // slots and the first entries of its bin. Slots and bin entries are read
+    // before their counts are known (those past the counts are ignored): a
+    // dependent round trip costs more than the bytes.
+    const bool spec_hold = k <= (int64_t)kSpecHold * kResolveThreads;
+    double phb[kSpecHold];
+    int32_t pht[kSpecHold];
+#pragma unroll
+    for (int u = 0; u < kSpecHold; ++u) {
+        const int i = tid + u * kResolveThreads;
+        phb[u] = 0.0;
+        pht[u] = 0;
+        if (spec_hold && i < k) { phb[u] = sbid[i]; pht[u] = stok[i]; }
+    }
+    const int32_t pbt = w.bin_t[(int64_t)e * kOvfCap + tid];
+    const double pbv = w.bin_v[(int64_t)e * kBinMax + tid];
     const int c0 = w.cnt[e];
     const int nbin = w.bcnt[e];
-    if (ctl->abort || ctl->bulk_done) return;
-    const int cur = round & 1;
+    const int aborted = ctl->abort, done = ctl->bulk_done | ctl->pairs_done;
     const int64_t nb = ctl->nbid[cur];
+    if (aborted || done) return;
     const bool ident = round == 0;
     const int32_t* list = cur ? w.list1 : w.list0;
     int32_t* outl = cur ? w.list0 : w.list1;
-    const int tid = threadIdx.x, lane = tid & 63;
-    int32_t* stok = w.stok + (int64_t)e * k;
-    double* sbid = w.sbid + (int64_t)e * k;
 
-    // append the token of each thread with rej set to the next bidder list
-    auto reject = [&](bool rej, int tok) {
-        const unsigned long long m = __ballot(rej);
-        int base = 0;
-        if (lane == 0 && m) base = atomicAdd(&ctl->nbid[cur ^ 1], (int)__popcll(m));
-        base = __shfl(base, 0, 64);
-        if (rej) {
-            const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-            outl[base + __popcll(m & below)] = tok;
+    // the holders into LDS (from the prefetch when it covered them)
+    auto load_holders = [&]() {
+        if (spec_hold) {
+#pragma unroll
+            for (int u = 0; u < kSpecHold; ++u) {
+                const int i = tid + u * kResolveThreads;
+                if (i < c0) { hb[i] = phb[u]; ht[i] = pht[u]; }
+            }
+        } else {
+            for (int i = tid; i < c0; i += kResolveThreads) { hb[i] = sbid[i]; ht[i] = stok[i]; }
         }
     };
-    // merge the n gathered bidders into the holders
+    // merge the n gathered bidders into the holders. The bidders are sorted,
+    // then every element's new rank is its rank in its own run plus the
+    // elements of the other run ahead of it (binary search); those ranked
+    // >= k are rejected, staged at rank - k, and leave for the next bidder
+    // list at a base reserved by one atomic per merge. The atomic's result
+    // stays in a register until the ranks are known, so its round trip
+    // overlaps the sort.
     auto merge = [&](int n) {
-        block_sort_best(cb, ct, ob, ot, n);
         const int c = nhold;
-        // holder i moves to i + (bidders better than it)
-        for (int i0 = 0; i0 < c; i0 += blockDim.x) {
-            const int i = i0 + tid;
-            bool rej = false;
-            int tok = 0;
-            if (i < c) {
-                int lo = 0, hi = n;  // first bidder not better than holder i
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (better(cb[mid], ct[mid], hb[i], ht[i])) lo = mid + 1;
-                    else hi = mid;
-                }
-                const int r = i + lo;
-                if (r < k) { ob[r] = hb[i]; ot[r] = ht[i]; }
-                else { rej = true; tok = ht[i]; }
+        const int nrej = c + n - (int)min<int64_t>(c + n, k);  // <= n, as c <= k
+        int my_base = 0;
+        if (tid == 0 && nrej > 0) my_base = atomicAdd(&ctl->nbid[cur ^ 1], nrej);
+        block_sort_best(cb, ct, ob, ot, n);
+        for (int i = tid; i < c; i += kResolveThreads) {
+            const double b = hb[i];
+            const int t = ht[i];
+            int lo = 0, hi = n;  // bidders better than holder i
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (better(cb[mid], ct[mid], b, t)) lo = mid + 1;
+                else hi = mid;
             }
-            reject(rej, tok);
+            const int r = i + lo;
+            if (r < k) { ob[r] = b; ot[r] = t; }
+            else rej[r - k] = t;
         }
-        // bidder j moves to j + (holders better than it)
-        for (int j0 = 0; j0 < n; j0 += blockDim.x) {
-            const int j = j0 + tid;
-            bool rej = false;
-            int tok = 0;
-            if (j < n) {
-                int lo = 0, hi = c;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (better(hb[mid], ht[mid], cb[j], ct[j])) lo = mid + 1;
-                    else hi = mid;
-                }
-                const int r = j + lo;
-                if (r < k) { ob[r] = cb[j]; ot[r] = ct[j]; }
-                else { rej = true; tok = ct[j]; }
+        for (int j = tid; j < n; j += kResolveThreads) {
+            const double b = cb[j];
+            const int t = ct[j];
+            int lo = 0, hi = c;  // holders better than bidder j
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (better(hb[mid], ht[mid], b, t)) lo = mid + 1;
+                else hi = mid;
             }
-            reject(rej, tok);
+            const int r = j + lo;
+            if (r < k) { ob[r] = b; ot[r] = t; }
+            else rej[r - k] = t;
         }
+        if (tid == 0) rbase = my_base;
         __syncthreads();
+        const int base = rbase;
+        for (int q = tid; q < nrej; q += kResolveThreads) outl[base + q] = rej[q];
         const int c2 = (int)min<int64_t>(c + n, k);
-        for (int i = tid; i < c2; i += blockDim.x) { hb[i] = ob[i]; ht[i] = ot[i]; }
+        for (int i = tid; i < c2; i += kResolveThreads) { hb[i] = ob[i]; ht[i] = ot[i]; }
         if (tid == 0) { nhold = c2; ncand = 0; }
         __syncthreads();
     };
@@ -524,8 +577,9 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         // as the bid kernel filed them (at most kBinMax <= kResolveCap)
         nbe = nbin;
         if (nbe > 0) {
-            for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
-            for (int i = tid; i < nbe; i += blockDim.x) {
+            load_holders();
+            if (tid < nbe) { ct[tid] = pbt; cb[tid] = pbv; }
+            for (int i = tid + kResolveThreads; i < nbe; i += kResolveThreads) {
                 ct[i] = w.bin_t[(int64_t)e * kOvfCap + i];
                 cb[i] = w.bin_v[(int64_t)e * kBinMax + i];
             }
@@ -537,7 +591,7 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
         // gather e's bidders from the round's list in one pass, 16 loads in
         // flight per thread (the bids were written by other XCDs: every load
         // is a far round trip); tokens first, their bids in a second sweep
-        for (int i = tid; i < c0; i += blockDim.x) { hb[i] = sbid[i]; ht[i] = stok[i]; }
+        load_holders();
         __syncthreads();
         {
             constexpr int U = 16;
@@ -632,6 +686,9 @@ __global__ __launch_bounds__(256) void auc_bulk_resolve_kernel(int64_t T, int64_
 }
 
 #include "auction_tail.h"
+#include "auction_late.h"
+static_assert(kLateG == kLateGWs && kLateCap == kLateCapWs && kLateG == 8,
+              "late-round workspace sizes");
 
 // ---------------------------------------------------------------- finalize
 
@@ -676,6 +733,12 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     hipLaunchKernelGGL(auc_init_kernel, dim3(g1), dim3(256), 0, stream, w, E, scan, T * E, st, assign, T);
     const int rounds = (k > kBulkKMax) ? 0 : (k <= kSmallK ? kBulkRoundsSmallK : kBulkRounds);
     const int tail_max = k <= kSmallK ? kTailMaxSmallK : kTailMax;
+    // the late rounds of a phase in one cooperative launch when the experts'
+    // holders fit the workgroups' LDS
+    const bool late = rounds > kLatePairs && late_ok(T, E, k);
+    const int pair_rounds = late ? kLatePairs : rounds;
+    const int late_enter = late ? kLateEnter : 0;
+    const size_t late_lds = late ? late_lds_bytes(E, k) : 0;
     int64_t bid_blocks = (T + 15) / 16;
     if (bid_blocks > 2048) bid_blocks = 2048;
     double eps = eps_start;
@@ -683,13 +746,26 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
         auction_mark(4 * phase, stream);
         hipLaunchKernelGGL(auc_phase_start_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
                            stream, w, T, E, st);
-        for (int r = 0; r < rounds; ++r) {
+        for (int r = 0; r < pair_rounds; ++r) {
             // round 0: every token bids; later rounds: the returned few
             const unsigned nblk = (unsigned)(r == 0 ? bid_blocks : (bid_blocks < 256 ? bid_blocks : 256));
             hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3(nblk), dim3(256), 0,
-                               stream, s, T, E, w, scan, r, eps, tail_max);
+                               stream, s, T, E, w, scan, r, eps, tail_max, late_enter);
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
                                E, k, w, r);
+        }
+        if (late) {
+            const float* sa = s;
+            int64_t Ta = T, Ea = E, ka = k;
+            AucWs wa = w;
+            double epsa = eps;
+            int tm = tail_max, mr = rounds;
+            AucStatsDev* sta = st;
+            void* args[] = {&sa, &Ta, &Ea, &ka, &wa, (void*)&scan, &epsa, &tm, &mr, &sta};
+            const hipError_t le = hipLaunchCooperativeKernel((const void*)auc_late_kernel<NCH>,
+                                                             dim3(kLateG), dim3(kLateThreads), args,
+                                                             (unsigned)late_lds, stream);
+            if (le != hipSuccess) return le;
         }
         launch_tail<NCH>(s, T, E, k, w, scan, eps, phase, max_bids, st, stream);
         auction_mark(4 * phase + 3, stream);

@@ -765,6 +765,9 @@ def main():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--solve-only", type=int, default=0, metavar="REPS",
+                    help="only the auction solve on the mixture workload, REPS timed solves "
+                         "(for profiling the auction's kernels)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this implementation runs on one GPU only (every expert resident on one "
@@ -776,6 +779,10 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.solve_only:
+        api.load()
+        print(json.dumps({"auction_solve_ms": auction_solve(reps=args.solve_only)}), flush=True)
         return
     api.load()
     torch.cuda.init()

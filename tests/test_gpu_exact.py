@@ -87,6 +87,36 @@ def test_exact_assignment_workloads(wid):
     assert (res["offsets"].cpu().numpy() == coff).all()
 
 
+@pytest.mark.parametrize("E", [128, 16])
+def test_exact_late_rounds(E):
+    """8192 tokens of the contested mixture recipe: after two bulk rounds
+    each phase's remaining rounds run in the cooperative late-round launch
+    (holders resident in the workgroups' LDS, two device-wide barriers per
+    round). Same bar: with eps_end = gap / (2T) the result is the optimum
+    (cycle cancelling from the default-schedule result, certified by the
+    minimum cycle)."""
+    wl = W.custom(8192, E, 256, None, dtype="bf16", kind="mixture", wid=993 + E)
+    w = W.gen_centroids(wl)
+    h = W.gen_tokens(wl, centroids=w)
+    scores = api.base_affinity(to_dev(h, wl.dtype), to_dev(w, wl.dtype))
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy().astype(np.float64)
+    res0, st0 = _solve(scores, wl.eps_end, wl.eps_start)
+    a0 = res0["assign"].cpu().numpy()
+    assert (np.bincount(a0, minlength=E) == wl.T // E).all()
+    p0 = res0["prices"].cpu().numpy()
+    assert oracle.eps_cs_violation(s, a0, p0) <= wl.eps_end * (1 + 1e-9)
+    opt, _ = oracle.cycle_cancel(s, a0)
+    gap = oracle.min_cycle_gap(s, opt)
+    assert gap > 0, gap
+    eps = gap / (2 * wl.T)
+    res, st = _solve(scores, eps, wl.eps_start)
+    a = res["assign"].cpu().numpy()
+    print(f"T=8192 E={E}: gap {gap:.3e} eps_end {eps:.3e} bids/phase {st.bids} "
+          f"depth/phase {st.rounds}")
+    assert (a == opt).all()
+
+
 def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
 
