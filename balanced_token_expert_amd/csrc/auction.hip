@@ -102,6 +102,11 @@ struct AucWs {
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+static bool late_ok(int64_t T, int64_t E, int64_t k);  // auction_late.h
+
+// the late-round launch's buffers, reserved only when a solve of this size
+// uses it
+static int64_t late_ws_g(int64_t T, int64_t E) { return (E > 0 && late_ok(T, E, T / E)) ? kLateGWs : 0; }
 
 static AucWs carve(void* ws, int64_t T, int64_t E) {
     char* p = (char*)ws;
@@ -123,10 +128,11 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.bcnt = (int32_t*)p; p += align256(E * 4);
     w.bin_t = (int32_t*)p; p += align256(E * kOvfCap * 4);
     w.bin_v = (double*)p; p += align256(E * kBinMax * 8);
-    w.llist = (int32_t*)p; p += align256(kLateGWs * 2 * T * 4);
-    w.lbin_t = (int32_t*)p; p += align256(kLateGWs * E * kLateCapWs * 4);
-    w.lbin_v = (double*)p; p += align256(kLateGWs * E * kLateCapWs * 8);
-    w.lbc = (int32_t*)p; p += align256(kLateGWs * E * 4);
+    const int64_t lg = late_ws_g(T, E);
+    w.llist = (int32_t*)p; p += align256(lg * 2 * T * 4);
+    w.lbin_t = (int32_t*)p; p += align256(lg * E * kLateCapWs * 4);
+    w.lbin_v = (double*)p; p += align256(lg * E * kLateCapWs * 8);
+    w.lbc = (int32_t*)p; p += align256(lg * E * 4);
     return w;
 }
 
@@ -135,8 +141,8 @@ size_t auction_ws_bytes(int64_t T, int64_t E) {
            5 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
            align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
            align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) +
-           align256(kLateGWs * 2 * T * 4) + align256(kLateGWs * E * kLateCapWs * 4) +
-           align256(kLateGWs * E * kLateCapWs * 8) + align256(kLateGWs * E * 4) + 256;
+           align256(late_ws_g(T, E) * 2 * T * 4) + align256(late_ws_g(T, E) * E * kLateCapWs * 4) +
+           align256(late_ws_g(T, E) * E * kLateCapWs * 8) + align256(late_ws_g(T, E) * E * 4) + 256;
 }
 
 // ---------------------------------------------------------------- helpers
