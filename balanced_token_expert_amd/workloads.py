@@ -45,7 +45,7 @@ class Workload:
     kind: str           # "iid", "mixture" or "skew"
     eps_start: float
     eps_end: float
-    eps_factor: float = 10.0
+    eps_factor: float = 10.0   # eps-scaling: eps_start, eps_start/f, ..., eps_end
     note: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -63,14 +63,14 @@ WORKLOADS = {
                 note="h from a 16-component Gaussian mixture (means N(0,I), "
                      "std 0.3), w~N(0,1/D); assignment only"),
     3: Workload(3, "layer_t16k_e64_d1536", 16384, 64, 1536, 6144, "bf16",
-                "gelu", "iid", 1.0, 1e-4,
+                "gelu", "iid", 1.0, 1e-4, 100.0,
                 note="h~N(0,1), w,W1~N(0,1/D), W2~N(0,1/F); GELU"),
     4: Workload(4, "skew_t32k_e128_d1024", 32768, 128, 1024, 4096, "bf16",
-                "gelu", "skew", 1.0, 1e-4,
+                "gelu", "skew", 1.0, 1e-4, 30.0,
                 note="80% of tokens at 3*w0/|w0| + N(0,0.1), rest N(0,1); "
                      "w,W1~N(0,1/D), W2~N(0,1/F); GELU"),
     5: Workload(5, "large_t64k_e128_d2048", 65536, 128, 2048, 8192, "bf16",
-                "gelu", "iid", 1.0, 1e-4,
+                "gelu", "iid", 1.0, 1e-4, 100.0,
                 note="h~N(0,1), w,W1~N(0,1/D), W2~N(0,1/F); GELU; "
                      "about 8.6 GB of expert weights"),
 }

@@ -2,7 +2,7 @@
 """Benchmark of the BASE-layer forward on one MI355X.
 
 One step = one pass of the whole hot path over one batch: affinities, the
-balanced assignment (auction, eps 1.0 -> 1e-4, factor 10), the expert
+balanced assignment (auction, eps 1.0 -> 1e-4), the expert
 grouping, both expert products with the fused gate/residual/scatter
 (``base_layer_forward``, BALANCED) plus greedy test-time routing of the same
 scores (``base_route_greedy``), on the large workload: T=65536 tokens
@@ -796,7 +796,8 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded numpy PCG64, shapes of the paper's setting)",
            "config": {"workload": wl.name, "T": T, "E": E, "D": wl.D, "F": wl.F, "act": wl.act,
-                      "route": "balanced auction eps 1.0->1e-4 (factor 10) + greedy on the "
+                      "route": f"balanced auction eps {wl.eps_start}->{wl.eps_end} (factor "
+                               f"{wl.eps_factor:g}) + greedy on the "
                                "same scores", "parallelism": "single GPU, all experts resident"},
            "phase_ms": head["phase_ms"], "auction": head["auction"],
            "greedy_load": head["greedy_load"],
