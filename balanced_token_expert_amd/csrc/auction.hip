@@ -482,7 +482,8 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
     __shared__ double ob[kBulkKMax];     // merged
     __shared__ int32_t ot[kBulkKMax];
     __shared__ int32_t rej[kResolveCap];  // a merge's rejected tokens, by rank - k
-    __shared__ int32_t ncand, nhold, rbase;
+    __shared__ int32_t frj[kResolveCap];  // bidders rejected before any merge (below)
+    __shared__ int32_t ncand, nhold, rbase, nfrj, nsurv;
     static_assert(kResolveThreads <= kBinMax && kResolveThreads <= kOvfCap,
                   "one prefetched bin entry per thread");
     AucCtl* ctl = w.ctl;
@@ -577,7 +578,24 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
         __syncthreads();
     };
 
-    if (tid == 0) { ncand = 0; nhold = c0; }
+    // Once e is full, a bidder not better than its worst holder would be
+    // ranked >= k by any merge: in rounds with many bidders for e it goes
+    // straight back to the bidder list (staged in frj, one atomic per
+    // flush) and only the others are sorted. Holders only get better, so
+    // the result is the same as merging everyone.
+    auto flush_frj = [&]() {  // every thread, with nfrj read after a barrier
+        const int n = nfrj;
+        if (n > 0) {
+            if (tid == 0) rbase = atomicAdd(&ctl->nbid[cur ^ 1], n);
+            __syncthreads();
+            const int b = rbase;
+            for (int q = tid; q < n; q += kResolveThreads) outl[b + q] = frj[q];
+            __syncthreads();
+            if (tid == 0) nfrj = 0;
+            __syncthreads();
+        }
+    };
+    if (tid == 0) { ncand = 0; nhold = c0; nfrj = 0; }
     int nbe;  // this round's bidders for e
     if (nb <= kBinMax) {
         // as the bid kernel filed them (at most kBinMax <= kResolveCap)
@@ -630,15 +648,42 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
         if (nbe > 0 && nbe <= kResolveCap + kOvfCap) {
             // the first kResolveCap from LDS, the rest from the bin, merged
             // kResolveCap at a time
+            constexpr int UC = kResolveCap / kResolveThreads;
             for (int c0 = 0; c0 < nbe; c0 += kResolveCap) {
                 const int cn = min(kResolveCap, nbe - c0);
-                if (c0 > 0)
-                    for (int i = tid; i < cn; i += blockDim.x)
-                        ct[i] = __hip_atomic_load(w.bin_t + (int64_t)e * kOvfCap + (c0 - kResolveCap) + i,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int i = tid; i < cn; i += blockDim.x) cb[i] = w.bval[ct[i]];
+                const bool full = nhold == k;
+                const double thb = full ? hb[k - 1] : 0.0;
+                const int tht = full ? ht[k - 1] : 0;
+                int32_t tk[UC];
+                double bk[UC];
+#pragma unroll
+                for (int u = 0; u < UC; ++u) {
+                    const int i = tid + u * kResolveThreads;
+                    tk[u] = -1;
+                    if (i < cn)
+                        tk[u] = c0 == 0 ? ct[i]
+                                        : __hip_atomic_load(w.bin_t + (int64_t)e * kOvfCap + (c0 - kResolveCap) + i,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < UC; ++u) bk[u] = tk[u] >= 0 ? w.bval[tk[u]] : 0.0;
+                if (tid == 0) nsurv = 0;
+                __syncthreads();  // every thread has read ct before the survivors overwrite it
+#pragma unroll
+                for (int u = 0; u < UC; ++u) {
+                    if (tk[u] < 0) continue;
+                    if (full && !better(bk[u], tk[u], thb, tht)) {
+                        frj[atomicAdd(&nfrj, 1)] = tk[u];
+                    } else {
+                        const int q = atomicAdd(&nsurv, 1);
+                        cb[q] = bk[u];
+                        ct[q] = tk[u];
+                    }
+                }
                 __syncthreads();
-                merge(cn);
+                const int ns = nsurv;
+                flush_frj();
+                if (ns > 0) merge(ns);
             }
         } else if (nbe > 0) {
             // more than the buffer holds (rare): gather again, four loads in
@@ -650,6 +695,9 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
             __syncthreads();
             constexpr int U = 4;
             for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
+                const bool full = nhold == k;
+                const double thb = full ? hb[k - 1] : 0.0;
+                const int tht = full ? ht[k - 1] : 0;
                 int64_t tt[U];
                 int ee[U];
 #pragma unroll
@@ -662,17 +710,25 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     if (ee[u] == e) {
-                        const int pos = atomicAdd(&ncand, 1);
-                        cb[pos] = w.bval[tt[u]];
-                        ct[pos] = (int32_t)tt[u];
+                        const double b = w.bval[tt[u]];
+                        if (full && !better(b, (int)tt[u], thb, tht)) {
+                            frj[atomicAdd(&nfrj, 1)] = (int32_t)tt[u];
+                        } else {
+                            const int pos = atomicAdd(&ncand, 1);
+                            cb[pos] = b;
+                            ct[pos] = (int32_t)tt[u];
+                        }
                     }
                 __syncthreads();
                 const int n = ncand;
+                const int nf = nfrj;
                 __syncthreads();
+                if (nf > kResolveCap - U * (int)blockDim.x) flush_frj();
                 if (n > kResolveCap - U * (int)blockDim.x) merge(n);
             }
             const int n = ncand;
             __syncthreads();
+            flush_frj();
             if (n > 0) merge(n);
         }
     }
