@@ -52,17 +52,17 @@ AUCTION_SOURCES = ("balanced_token_expert_amd/csrc/auction.hip",
                    "balanced_token_expert_amd/csrc/auction_tail.h",
                    "balanced_token_expert_amd/csrc/auction_late.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99992
+FETCH_SCALE = 1.99990
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB), means over
     # the dispatches of the balanced step
     "ffn1": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2505063.6, 1182996.6),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2504745.7, 1184848.7),
     "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2880893.8, 353294.8),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2924269.1, 353130.2),
     "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
-                     "c0acd2d7e69f25cb3a0dbbf39e36a9c76c54323cccf864c845e84a6ba8b886ac", 8247.2, 32.7),
+                     "ac24f11127662d579d2374fabee18e514df88ee377a89050abaebb7ac6cb292c", 8240.1, 32.7),
 }
 
 
