@@ -507,6 +507,10 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 rank += (lr < lq || (lr == lq && r < lane)) ? 1 : 0;
             }
             if (mine) order[rank] = lane;
+            // the same order in registers: lane r receives the lane ranked r
+            // (a cross-lane push; lanes past nc push to themselves and are
+            // never read)
+            const int order_r = __builtin_amdgcn_ds_permute((mine ? rank : lane) * 4, lane);
             // the experts of this lane's path, and its free expert
             unsigned long long msk[NCH];
 #pragma unroll
@@ -539,8 +543,9 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             for (int c = 0; c < NCH; ++c) used[c] = 0;
             int nacc = 0;
             double Lmax = 0.0;
+            unsigned long long accm = 0;  // the paths applied, by candidate
             for (int r = 0; r < nc; ++r) {
-                const int q = first_lane_i32(order[r]);
+                const int q = readlane_i32(order_r, r);
                 const int fq_ = readlane_i32(f, q);
                 if (fq_ < 0) continue;
                 int capq = 0;
@@ -564,6 +569,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                     if (c == (fq_ >> 6) && lane == (fq_ & 63)) --capc[c];
                 }
                 if (lane == 0) alist[nacc] = q;
+                accm |= 1ull << q;
                 ++nacc;
                 Lmax = fmax(Lmax, readlane_f64(lq, q));
             }
@@ -573,8 +579,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             // tokens not placed search again next batch (in candidate order)
-            bool placedq = false;
-            for (int j = 0; j < nacc; ++j) placedq = placedq || alist[j] == lane;
+            const bool placedq = (accm >> lane) & 1ull;
             const unsigned long long rej = __ballot(mine && !placedq);
             if (mine && !placedq) {
                 const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
