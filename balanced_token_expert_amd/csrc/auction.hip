@@ -89,6 +89,7 @@ struct AucWs {
     int32_t* stok;     // E*k slot tokens (slots 0 .. cnt-1 of each expert are held)
     double* sbid;      // E*k slot bids
     int32_t* slot_of;  // T   slot of each held token (tail)
+    float* sown;       // E*k tail: each slot's holder's score at the slot's expert
     double* C;         // E*E tail: cheapest move of a holder of a to b
     int32_t* Ct;       // E*E tail: the holder that makes it
     unsigned long long* stale;  // E*ceil(E/64) tail: C entries whose holder left
@@ -122,6 +123,7 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.stok = (int32_t*)p; p += align256(T * 4);
     w.sbid = (double*)p; p += align256(T * 8);
     w.slot_of = (int32_t*)p; p += align256(T * 4);
+    w.sown = (float*)p; p += align256(T * 4);
     w.C = (double*)p; p += align256(E * E * 8);
     w.Ct = (int32_t*)p; p += align256(E * E * 4);
     w.stale = (unsigned long long*)p; p += align256(E * ((E + 63) / 64) * 8);
@@ -138,7 +140,7 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
 
 size_t auction_ws_bytes(int64_t T, int64_t E) {
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
-           5 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
+           6 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
            align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
            align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) +
            align256(late_ws_g(T, E) * 2 * T * 4) + align256(late_ws_g(T, E) * E * kLateCapWs * 4) +

@@ -171,7 +171,9 @@ __global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int
 #pragma unroll
                 for (int c = 0; c < NCH; ++c)
                     if (c == (a >> 6)) ra = v[u][c];
-                const double sa = (double)__builtin_bit_cast(float, readlane_i32(__builtin_bit_cast(int, ra), a & 63));
+                const float sa32 = __builtin_bit_cast(float, readlane_i32(__builtin_bit_cast(int, ra), a & 63));
+                if (lane == 0) w.sown[(int64_t)a * k + c0 + i0 + u] = sa32;
+                const double sa = (double)sa32;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const int e = lane + 64 * c;
@@ -275,11 +277,17 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 const int j = j0 + v * 64 + lane;
                 hh[v] = (j < ha) ? ld_fresh_i32(w.stok + (int64_t)a * k + j) : -1;
             }
+            // a holder's score at a is kept beside its slot (sown): only
+            // the score at b is a scattered load
             float sa[8], sb[8];
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
+                const int j = j0 + v * 64 + lane;
+                sa[v] = (j < ha) ? __int_as_float(ld_fresh_i32((const int32_t*)w.sown + (int64_t)a * k + j)) : 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
                 const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
-                sa[v] = hh[v] >= 0 ? sani(row[a], sn) : 0.0f;
                 sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
             }
 #pragma unroll
@@ -613,15 +621,18 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                         x = nx[x];
                     }
                 int jn = 0, lv = -1, slot = 0;
+                float sj = 0.0f;  // the joiner's score at x, kept beside its slot
                 if (i <= m) {
                     jn = i == 0 ? u : otok[prv];
                     lv = i < m ? otok[x] : -1;
                     if (i < m) slot = ld_fresh_i32(w.slot_of + lv);
+                    sj = s[(int64_t)jn * E + x];
                 }
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
                 if (i == m) slot = atomicAdd(&cnt[x], 1);
                 if (i <= m) {
                     w.stok[(int64_t)x * k + slot] = jn;
+                    w.sown[(int64_t)x * k + slot] = sani(sj, sn);
                     w.slot_of[jn] = slot;
                     const int id = atomicAdd(&nitem, 1);
                     ij[id] = jn;
