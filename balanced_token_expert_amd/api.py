@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libbase_layer.so")
 
 BASE_OK, BASE_ERR_INVALID_ARG, BASE_ERR_INDIVISIBLE = 0, -1, -2
 BASE_ERR_UNSUPPORTED, BASE_ERR_HIP, BASE_ERR_NOT_CONVERGED = -3, -4, -5
-BASE_ERR_NONFINITE, BASE_ERR_UNBALANCED = -6, -8
+BASE_ERR_NONFINITE, BASE_ERR_UNBALANCED, BASE_ERR_INVARIANT = -6, -8, -9
 BASE_F32, BASE_BF16 = 0, 1
 BASE_ACT_RELU, BASE_ACT_GELU = 0, 1
 BASE_ROUTE_BALANCED, BASE_ROUTE_GREEDY, BASE_ROUTE_GIVEN = 0, 1, 2

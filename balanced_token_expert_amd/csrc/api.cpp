@@ -391,6 +391,7 @@ const char* base_strerror(int code) {
         case BASE_ERR_NOT_CONVERGED: return "auction stopped at its bid cap";
         case BASE_ERR_NONFINITE: return "no finite affinity";
         case BASE_ERR_UNBALANCED: return "given assignment is not balanced";
+        case BASE_ERR_INVARIANT: return "an auction invariant failed (checking build)";
         default: return "unknown error";
     }
 }

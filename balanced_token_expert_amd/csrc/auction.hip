@@ -60,6 +60,20 @@ constexpr int64_t kLateGWs = 8;      // late rounds (auction_late.h): workgroups
 constexpr int64_t kLateCapWs = 256;  // and bids per (workgroup, expert) bin
 constexpr int32_t kErrNotConverged = -5;
 constexpr int32_t kErrNonfinite = -6;
+constexpr int32_t kErrInvariant = -9;
+
+// Checking build (BASE_CHECKS): the auction's kernels verify its invariants
+// on the device and report a failure through the status word (never by a
+// trap): every expert holds at most k tokens, sorted best first during the
+// bulk rounds, and after the solve exactly k distinct ones.
+#ifdef BASE_CHECKS
+constexpr bool kChecks = true;
+#else
+constexpr bool kChecks = false;
+#endif
+BASE_DEV void report_invariant(AucStatsDev* st) {
+    __hip_atomic_store(&st->status, kErrInvariant, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 constexpr int32_t kNoTok = 0x7fffffff;
 
 struct AucCtl {
@@ -476,7 +490,8 @@ constexpr int kSpecHold = 2;  // holder slots prefetched per thread (k <= 512)
 
 __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64_t T, int64_t E,
                                                                            int64_t k, AucWs w,
-                                                                           int round) {
+                                                                           int round,
+                                                                           AucStatsDev* st) {
     __shared__ double cb[kResolveCap];   // bidders
     __shared__ int32_t ct[kResolveCap];
     __shared__ double hb[kBulkKMax];     // holders, best first
@@ -739,6 +754,12 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
         const int m = nhold;
         for (int i = tid; i < m; i += blockDim.x) { sbid[i] = hb[i]; stok[i] = ht[i]; }
         publish_expert(w, e, k, m, hb);
+        if constexpr (kChecks) {
+            bool bad = (tid == 0) && (m < 0 || m > k);
+            for (int i = tid + 1; i < m && i < k; i += blockDim.x)
+                bad = bad || better(hb[i], ht[i], hb[i - 1], ht[i - 1]) || ht[i] == ht[i - 1];
+            if (bad) report_invariant(st);
+        }
     }
     // where the tail finds the bidders if it takes over after this round
     // (no block of this kernel reads these fields)
@@ -764,6 +785,24 @@ __global__ void auc_finalize_kernel(AucWs w, int64_t E, int64_t k, int32_t* assi
         assign[t] = e;
     }
     if (threadIdx.x == 0) prices[e] = w.floor_[e];
+}
+
+// Checking build: after the solve every expert holds exactly k tokens and
+// no token is held twice (bexp, free by then, counts each token's holders).
+__global__ void auc_check_zero_kernel(AucWs w, int64_t T) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < T) w.bexp[t] = 0;
+}
+__global__ void auc_check_final_kernel(AucWs w, int64_t T, int64_t k, AucStatsDev* st) {
+    const int e = blockIdx.x;
+    if (w.ctl->abort) return;  // an error is already reported
+    const int n = w.cnt[e];
+    bool bad = threadIdx.x == 0 && n != k;
+    for (int64_t i = threadIdx.x; i < n && i < k; i += blockDim.x) {
+        const int32_t t = w.stok[(int64_t)e * k + i];
+        bad = bad || t < 0 || t >= T || atomicAdd(&w.bexp[t], 1) != 0;
+    }
+    if (bad) report_invariant(st);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -816,7 +855,7 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
             hipLaunchKernelGGL(auc_bulk_bid_kernel<NCH>, dim3(nblk), dim3(256), 0,
                                stream, s, T, E, w, scan, r, eps, tail_max, late_enter);
             hipLaunchKernelGGL(auc_bulk_resolve_kernel, dim3((unsigned)E), dim3(256), 0, stream, T,
-                               E, k, w, r);
+                               E, k, w, r, st);
         }
         if (late) {
             const float* sa = s;
@@ -839,6 +878,12 @@ static hipError_t run_auction(const float* s, int64_t T, int64_t E, double eps_s
     }
     hipLaunchKernelGGL(auc_finalize_kernel, dim3((unsigned)E), dim3(256), 0, stream, w, E, k, assign,
                        prices);
+    if (kChecks) {
+        hipLaunchKernelGGL(auc_check_zero_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0,
+                           stream, w, T);
+        hipLaunchKernelGGL(auc_check_final_kernel, dim3((unsigned)E), dim3(256), 0, stream, w, T, k,
+                           st);
+    }
     return hipGetLastError();
 }
 

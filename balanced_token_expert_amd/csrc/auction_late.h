@@ -392,6 +392,15 @@ __global__ __launch_bounds__(kLateThreads) void auc_late_kernel(const float* s, 
         const int64_t e = g + (int64_t)kLateG * q;
         if (e < E) w.cnt[e] = hc[q];
     }
+    if constexpr (kChecks) {
+        for (int64_t x = tid; x < (int64_t)ne * k; x += kLateThreads) {
+            const int q = (int)(x / k);
+            const int64_t i = x - (int64_t)q * k;
+            const bool bad = hc[q] > k ||
+                             (i > 0 && i < hc[q] && (better(hb[x], ht[x], hb[x - 1], ht[x - 1]) || ht[x] == ht[x - 1]));
+            if (bad) report_invariant(st);
+        }
+    }
     const int nl = nl_cur;
     if (tid == 0) {
         base_s = nl > 0 ? atomicAdd(&ctl->nbid[X], nl) : 0;

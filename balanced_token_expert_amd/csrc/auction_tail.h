@@ -729,6 +729,10 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             if (lane == 0) head[x] = -1;
         }
         __syncthreads();
+        if constexpr (kChecks) {
+            for (int64_t e = tid; e < E; e += kSspThreads)
+                if (cnt[e] > k) report_invariant(st);
+        }
         if (tid == 0) {
             placed += nacc;
             ++batches;

@@ -59,6 +59,11 @@ typedef enum {
     BASE_ERR_HIP = -4,           /* a HIP launch or query failed */
     BASE_ERR_NOT_CONVERGED = -5, /* device: the auction hit cfg.max_bids */
     BASE_ERR_NONFINITE = -6,     /* device: no finite affinity at all */
+    BASE_ERR_INVARIANT = -9,     /* device, checking build only (libbase_layer_checks.so,
+                                    compiled with BASE_CHECKS): an auction invariant
+                                    failed (an expert holding more than T/E tokens or
+                                    holders out of order, or at the end an expert
+                                    without exactly T/E distinct tokens) */
     BASE_ERR_UNBALANCED = -8     /* device: a given assignment is not balanced
                                     or holds an expert id outside [0, E) */
 } base_status;

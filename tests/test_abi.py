@@ -42,6 +42,17 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(api.EXPORTED)
 
 
+def test_checking_build_exports_every_declared_symbol(lib):
+    """The checking variant (BASE_CHECKS) exposes the same C ABI."""
+    import balanced_token_expert_amd.build as b
+    assert os.path.exists(b.LIB_CHECKS), "libbase_layer_checks.so not built"
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_CHECKS], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (base_\w+)$", out, re.M))
+    for name in _declared():
+        assert name in exported, name
+
+
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
