@@ -52,17 +52,17 @@ AUCTION_SOURCES = ("balanced_token_expert_amd/csrc/auction.hip",
                    "balanced_token_expert_amd/csrc/auction_tail.h",
                    "balanced_token_expert_amd/csrc/auction_late.h",
                    "balanced_token_expert_amd/csrc/common.h")
-FETCH_SCALE = 1.99990
+FETCH_SCALE = 1.99992
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # kernel: (workload, sources, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB), means over
     # the dispatches of the balanced step
     "ffn1": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2504745.7, 1184848.7),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2510888.2, 1187331.0),
     "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2924269.1, 353130.2),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2919623.2, 353151.3),
     "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
-                     "ac24f11127662d579d2374fabee18e514df88ee377a89050abaebb7ac6cb292c", 8240.1, 32.7),
+                     "1d4cd75ce2f7b3fdaaffa97929a5fa2fe40f4985f6e7f71d8a271fe560423237", 5384.8, 38.3),
 }
 
 
