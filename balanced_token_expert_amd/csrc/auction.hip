@@ -703,45 +703,53 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
                 if (ns > 0) merge(ns);
             }
         } else if (nbe > 0) {
-            // more than the buffer holds (rare): gather again, four loads in
-            // flight, merging whenever the buffer may not hold another pass.
-            // Every thread reads the count between two barriers, so all take
-            // the same branch.
+            // more than the buffer and the bin hold (a crowded expert in a
+            // phase's first round): gather again, 16 loads in flight per
+            // thread, the candidates appended four loads' worth at a time so
+            // the buffer may always take another group, merging (which
+            // raises the threshold that filters the rest) whenever it may
+            // not. Every thread reads the counts between two barriers, so
+            // all take the same branch.
             __syncthreads();
             if (tid == 0) ncand = 0;
             __syncthreads();
-            constexpr int U = 4;
+            constexpr int U = 16, G = 4;
             for (int64_t j0 = 0; j0 < nb; j0 += U * (int64_t)blockDim.x) {
-                const bool full = nhold == k;
-                const double thb = full ? hb[k - 1] : 0.0;
-                const int tht = full ? ht[k - 1] : 0;
-                int64_t tt[U];
+                int32_t tt[U];
                 int ee[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t j = j0 + (int64_t)u * blockDim.x + tid;
-                    tt[u] = (j < nb) ? (ident ? j : (int64_t)list[j]) : -1;
+                    tt[u] = (j < nb) ? (ident ? (int32_t)j : list[j]) : -1;
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) ee[u] = (tt[u] >= 0) ? w.bexp[tt[u]] : -1;
+                double bv[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (ee[u] == e) {
-                        const double b = w.bval[tt[u]];
-                        if (full && !better(b, (int)tt[u], thb, tht)) {
-                            frj[atomicAdd(&nfrj, 1)] = (int32_t)tt[u];
-                        } else {
-                            const int pos = atomicAdd(&ncand, 1);
-                            cb[pos] = b;
-                            ct[pos] = (int32_t)tt[u];
+                for (int u = 0; u < U; ++u) bv[u] = (ee[u] == e) ? w.bval[tt[u]] : 0.0;
+#pragma unroll
+                for (int g0 = 0; g0 < U; g0 += G) {
+                    const bool full = nhold == k;
+                    const double thb = full ? hb[k - 1] : 0.0;
+                    const int tht = full ? ht[k - 1] : 0;
+#pragma unroll
+                    for (int u = g0; u < g0 + G; ++u)
+                        if (ee[u] == e) {
+                            if (full && !better(bv[u], tt[u], thb, tht)) {
+                                frj[atomicAdd(&nfrj, 1)] = tt[u];
+                            } else {
+                                const int pos = atomicAdd(&ncand, 1);
+                                cb[pos] = bv[u];
+                                ct[pos] = tt[u];
+                            }
                         }
-                    }
-                __syncthreads();
-                const int n = ncand;
-                const int nf = nfrj;
-                __syncthreads();
-                if (nf > kResolveCap - U * (int)blockDim.x) flush_frj();
-                if (n > kResolveCap - U * (int)blockDim.x) merge(n);
+                    __syncthreads();
+                    const int n = ncand;
+                    const int nf = nfrj;
+                    __syncthreads();
+                    if (nf > kResolveCap - G * (int)blockDim.x) flush_frj();
+                    if (n > kResolveCap - G * (int)blockDim.x) merge(n);
+                }
             }
             const int n = ncand;
             __syncthreads();
