@@ -103,7 +103,8 @@ struct AucWs {
     int32_t* stok;     // E*k slot tokens (slots 0 .. cnt-1 of each expert are held)
     double* sbid;      // E*k slot bids
     int32_t* slot_of;  // T   slot of each held token (tail)
-    float* sown;       // E*k tail: each slot's holder's score at the slot's expert
+    float* sown;       // E*k tail: each slot's holder's score at the slot's expert (E > 128)
+    float* xt;         // E*E*k tail, E <= 128: xt[(a E + b) k + i] = score at b of a's holder i
     double* C;         // E*E tail: cheapest move of a holder of a to b
     int32_t* Ct;       // E*E tail: the holder that makes it
     unsigned long long* stale;  // E*ceil(E/64) tail: C entries whose holder left
@@ -118,6 +119,9 @@ struct AucWs {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static bool late_ok(int64_t T, int64_t E, int64_t k);  // auction_late.h
+// the phase end's expert-major copy of its holders' scores (E <= 128, exactly when
+// its C matrix lives in LDS: ssp_c_in_lds in auction_tail.h)
+static int64_t xt_floats(int64_t T, int64_t E) { return E <= 128 ? E * T : 0; }
 
 // the late-round launch's buffers, reserved only when a solve of this size
 // uses it
@@ -138,6 +142,7 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.sbid = (double*)p; p += align256(T * 8);
     w.slot_of = (int32_t*)p; p += align256(T * 4);
     w.sown = (float*)p; p += align256(T * 4);
+    w.xt = (float*)p; p += align256(xt_floats(T, E) * 4);
     w.C = (double*)p; p += align256(E * E * 8);
     w.Ct = (int32_t*)p; p += align256(E * E * 4);
     w.stale = (unsigned long long*)p; p += align256(E * ((E + 63) / 64) * 8);
@@ -155,6 +160,7 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
 size_t auction_ws_bytes(int64_t T, int64_t E) {
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
            6 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
+           align256(xt_floats(T, E) * 4) +
            align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
            align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) +
            align256(late_ws_g(T, E) * 2 * T * 4) + align256(late_ws_g(T, E) * E * kLateCapWs * 4) +
@@ -822,7 +828,8 @@ static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const A
     auction_mark(4 * phase + 1, stream);
     const int sth = ssp_setup_threads(E);
     hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(sth),
-                       (size_t)(sth / 64) * 12 * E + 4 * kSetupChunk, stream, s,
+                       (size_t)(sth / 64) * 12 * E + 4 * kSetupChunk +
+                           (E <= 128 ? (size_t)(sth / 64) * 8 * E * 4 : 0), stream, s,
                        E, k, w, scan);
     auction_mark(4 * phase + 2, stream);
     const size_t lds = ssp_lds_bytes(E);

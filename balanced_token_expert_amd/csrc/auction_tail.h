@@ -137,6 +137,8 @@ __global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int
     double* pv = (double*)sm;                   // waves x E
     int32_t* pt = (int32_t*)(pv + nwv * E);     // waves x E
     int32_t* hl = pt + nwv * E;                 // kSetupChunk holder ids
+    float* tl = (float*)(hl + kSetupChunk);     // E <= 128: 8 x E scores per wave (xt staging)
+    const bool xtl = ssp_c_in_lds(E);  // the phase end keeps xt exactly when C is in LDS
     const AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->nbid[ctl->cur] == 0) return;
     const int a = blockIdx.x;
@@ -172,12 +174,39 @@ __global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int
                 for (int c = 0; c < NCH; ++c)
                     if (c == (a >> 6)) ra = v[u][c];
                 const float sa32 = __builtin_bit_cast(float, readlane_i32(__builtin_bit_cast(int, ra), a & 63));
-                if (lane == 0) w.sown[(int64_t)a * k + c0 + i0 + u] = sa32;
+                if (!xtl && lane == 0) w.sown[(int64_t)a * k + c0 + i0 + u] = sa32;
                 const double sa = (double)sa32;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const int e = lane + 64 * c;
                     if (e < E) argmin_merge(bv[c], bt[c], sa - (double)v[u][c], h[u]);
+                }
+            }
+            // the group's rows into xt, expert-major: eight rows at a time
+            // through the wave's LDS tile, so that each store writes 32-byte
+            // runs of consecutive slots (8 columns x 8 slots per instruction)
+            if (xtl) {
+                float* tw = tl + (int64_t)wave * 8 * E;
+#pragma unroll
+                for (int h0 = 0; h0 < U; h0 += 8) {
+#pragma unroll
+                    for (int uu = 0; uu < 8; ++uu) {
+                        if (h0 + uu >= U || h[h0 + uu] < 0) continue;
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) {
+                            const int e = lane + 64 * c;
+                            if (e < E) tw[uu * E + e] = v[h0 + uu][c];
+                        }
+                    }
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __builtin_amdgcn_wave_barrier();
+                    const int j = lane & 7, eo = lane >> 3;
+                    const int iu = i0 + h0 + j;
+                    if (h0 + j < U && iu < cn)
+                        for (int e = eo; e < E; e += 8)
+                            w.xt[((int64_t)a * E + e) * k + c0 + iu] = tw[j * E + e];
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __builtin_amdgcn_wave_barrier();
                 }
             }
         }
@@ -277,18 +306,31 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 const int j = j0 + v * 64 + lane;
                 hh[v] = (j < ha) ? ld_fresh_i32(w.stok + (int64_t)a * k + j) : -1;
             }
-            // a holder's score at a is kept beside its slot (sown): only
-            // the score at b is a scattered load
+            // E <= 128: both scores come from the expert-major copy xt,
+            // read contiguously with the holder ids; else a holder's score at
+            // a is kept beside its slot (sown) and only the one at b is a
+            // scattered load
             float sa[8], sb[8];
+            if constexpr (CL) {
+                const int32_t* xa = (const int32_t*)w.xt + ((int64_t)a * E + a) * k;
+                const int32_t* xb = (const int32_t*)w.xt + ((int64_t)a * E + b) * k;
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const int j = j0 + v * 64 + lane;
-                sa[v] = (j < ha) ? __int_as_float(ld_fresh_i32((const int32_t*)w.sown + (int64_t)a * k + j)) : 0.0f;
-            }
+                for (int v = 0; v < 8; ++v) {
+                    const int j = j0 + v * 64 + lane;
+                    sa[v] = (j < ha) ? __int_as_float(ld_fresh_i32(xa + j)) : 0.0f;
+                    sb[v] = (j < ha) ? __int_as_float(ld_fresh_i32(xb + j)) : 0.0f;
+                }
+            } else {
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
-                sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
+                for (int v = 0; v < 8; ++v) {
+                    const int j = j0 + v * 64 + lane;
+                    sa[v] = (j < ha) ? __int_as_float(ld_fresh_i32((const int32_t*)w.sown + (int64_t)a * k + j)) : 0.0f;
+                }
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const float* row = s + (int64_t)(hh[v] < 0 ? 0 : hh[v]) * E;
+                    sb[v] = hh[v] >= 0 ? sani(row[b], sn) : 0.0f;
+                }
             }
 #pragma unroll
             for (int v = 0; v < 8; ++v)
@@ -626,13 +668,13 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                     jn = i == 0 ? u : otok[prv];
                     lv = i < m ? otok[x] : -1;
                     if (i < m) slot = ld_fresh_i32(w.slot_of + lv);
-                    sj = s[(int64_t)jn * E + x];
+                    if (!CL) sj = s[(int64_t)jn * E + x];
                 }
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
                 if (i == m) slot = atomicAdd(&cnt[x], 1);
                 if (i <= m) {
                     w.stok[(int64_t)x * k + slot] = jn;
-                    w.sown[(int64_t)x * k + slot] = sani(sj, sn);
+                    if (!CL) w.sown[(int64_t)x * k + slot] = sani(sj, sn);
                     w.slot_of[jn] = slot;
                     const int id = atomicAdd(&nitem, 1);
                     ij[id] = jn;
@@ -672,14 +714,30 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 cv[c] = e < E ? cget(x, e) : 0.0;
                 upd[c] = false;
             }
-            // joiners (their rows four at a time)
+            // joiners (their rows four at a time; with E <= 128 each row also
+            // goes into xt at the joiner's slot)
             for (int j0 = 0; j0 < nit; j0 += 4) {
                 float r[4][NCH];
-                int jt[4];
+                int jt[4], js[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     jt[q] = (j0 + q < nit) ? readlane_i32(myj, (j0 + q) & 63) : -1;
-                    if (jt[q] >= 0) load_row<NCH>(s, jt[q], E, lane, sn, r[q]);
+                    js[q] = 0;
+                    if (jt[q] >= 0) {
+                        load_row<NCH>(s, jt[q], E, lane, sn, r[q]);
+                        if (CL) js[q] = ld_fresh_i32(w.slot_of + jt[q]);
+                    }
+                }
+                if constexpr (CL) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (jt[q] < 0) continue;
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) {
+                            const int e = lane + 64 * c;
+                            if (e < E) w.xt[((int64_t)x * E + e) * k + js[q]] = r[q][c];
+                        }
+                    }
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -725,6 +783,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             // in parallel with the other touched experts, rather than in a
             // repair step of the next batch's rounds
             const int xb = first_lane_i32(nx[x]);
+            if (CL) __builtin_amdgcn_s_waitcnt(0);  // this wave's xt stores, before it reads them
             if (xb >= 0 && stale(x, xb)) recompute_col(x, xb);
             if (lane == 0) head[x] = -1;
         }
