@@ -71,11 +71,12 @@ def test_strerror(lib):
 def test_workspace_sizes(lib):
     T, E, D, F = 65536, 128, 2048, 8192
     lay = api.base_workspace_bytes(api.BASE_OP_LAYER, T, E, D, F, api.BASE_BF16)
-    # the hidden activations (T x F bf16) and the scores dominate; the rest
-    # is per-token bookkeeping and per-expert scratch (the auction's bid bins
-    # take 40 KiB per expert)
-    assert lay >= T * F * 2 + T * E * 4
-    assert lay < T * F * 2 + T * E * 4 + 64 * T + 48 * 1024 * E + (1 << 20)
+    # the hidden activations (T x F bf16) and the scores dominate, then the
+    # phase end's expert-major copy of the holders' scores (T x E fp32, for
+    # E <= 128); the rest is per-token bookkeeping and per-expert scratch
+    # (the auction's bid bins take 40 KiB per expert)
+    assert lay >= T * F * 2 + 2 * T * E * 4
+    assert lay < T * F * 2 + 2 * T * E * 4 + 64 * T + 48 * 1024 * E + (1 << 20)
     auc = api.base_workspace_bytes(api.BASE_OP_AUCTION, T, E)
     assert 0 < auc < lay
     assert api.base_workspace_bytes(api.BASE_OP_AFFINITY, T, E, D) == 0
