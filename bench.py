@@ -58,11 +58,11 @@ MEASURED_TRAFFIC = {
     # kernel: (workload, sources, sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB), means over
     # the dispatches of the balanced step
     "ffn1": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2510888.2, 1187331.0),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2513144.5, 1185996.9),
     "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
-             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2919623.2, 353151.3),
+             "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2907136.1, 353352.6),
     "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
-                     "1d4cd75ce2f7b3fdaaffa97929a5fa2fe40f4985f6e7f71d8a271fe560423237", 5384.8, 38.3),
+                     "74cd0ddf67193aecec5b5201c15bce21d933f8c461183d1a1df50e6e15002483", 519.9, 719.0),
 }
 
 
