@@ -57,6 +57,7 @@
 // that bound stops the phase with an error status instead of looping.
 
 constexpr int kSspWaves = 16;
+constexpr int kJq = 2;  // joiner rows a C update loads at once
 constexpr int kSspThreads = 64 * kSspWaves;
 constexpr int kSspCand = 64;  // unassigned tokens a batch considers (one per lane of wave 0)
 
@@ -694,6 +695,28 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
         // exact); every other column whose cheapest holder left is marked
         // stale and keeps its old value, which can only underestimate it.
         const int nx_ = first_lane_i32(nux);
+        // A wave with several touched experts defers each one's arc
+        // recompute (E <= 128, at most 512 holders: one pass of loads) to
+        // after the next expert's joiner and leaver work, so the recompute's
+        // loads are in flight while that work runs. The deferred arc is in
+        // a row no other part of this loop touches.
+        int pa = -1, pb = 0;
+        int phh[8];
+        float psa[8], psb[8];
+        auto finish_pending = [&]() {
+            double bv = DBL_MAX;
+            int bt = kNoTok;
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                if (phh[v] >= 0) argmin_merge(bv, bt, (double)psa[v] - (double)psb[v], phh[v]);
+            wave_argmin_f64(bv, bt);
+            if (lane == 0) {
+                cset(pa, pb, bv);
+                __hip_atomic_store(Ct + (int64_t)pa * E + pb, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sput(pa, pb >> 6, sget(pa, pb >> 6) & ~(1ull << (pb & 63)));
+            }
+            pa = -1;
+        };
         for (int uu = wave; uu < nx_; uu += kSspWaves) {
             const int x = first_lane_i32(ux[uu]);
             // this expert's items: lane j holds item j's joiner and leaver
@@ -716,11 +739,11 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             }
             // joiners (their rows four at a time; with E <= 128 each row also
             // goes into xt at the joiner's slot)
-            for (int j0 = 0; j0 < nit; j0 += 4) {
-                float r[4][NCH];
-                int jt[4], js[4];
+            for (int j0 = 0; j0 < nit; j0 += kJq) {
+                float r[kJq][NCH];
+                int jt[kJq], js[kJq];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < kJq; ++q) {
                     jt[q] = (j0 + q < nit) ? readlane_i32(myj, (j0 + q) & 63) : -1;
                     js[q] = 0;
                     if (jt[q] >= 0) {
@@ -730,7 +753,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                 }
                 if constexpr (CL) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < kJq; ++q) {
                         if (jt[q] < 0) continue;
 #pragma unroll
                         for (int c = 0; c < NCH; ++c) {
@@ -740,7 +763,7 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
                     }
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < kJq; ++q) {
                     if (jt[q] < 0) continue;
                     float rx = 0.0f;
 #pragma unroll
@@ -784,9 +807,28 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             // repair step of the next batch's rounds
             const int xb = first_lane_i32(nx[x]);
             if (CL) __builtin_amdgcn_s_waitcnt(0);  // this wave's xt stores, before it reads them
-            if (xb >= 0 && stale(x, xb)) recompute_col(x, xb);
+            if (pa >= 0) finish_pending();
+            if (xb >= 0 && stale(x, xb)) {
+                const int hx = first_lane_i32(cnt[x]);
+                if (CL && hx <= 8 * 64) {
+                    const int32_t* xa = (const int32_t*)w.xt + ((int64_t)x * E + x) * k;
+                    const int32_t* xc = (const int32_t*)w.xt + ((int64_t)x * E + xb) * k;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        const int j = v * 64 + lane;
+                        phh[v] = (j < hx) ? ld_fresh_i32(w.stok + (int64_t)x * k + j) : -1;
+                        psa[v] = (j < hx) ? __int_as_float(ld_fresh_i32(xa + j)) : 0.0f;
+                        psb[v] = (j < hx) ? __int_as_float(ld_fresh_i32(xc + j)) : 0.0f;
+                    }
+                    pa = x;
+                    pb = xb;
+                } else {
+                    recompute_col(x, xb);
+                }
+            }
             if (lane == 0) head[x] = -1;
         }
+        if (pa >= 0) finish_pending();
         __syncthreads();
         if constexpr (kChecks) {
             for (int64_t e = tid; e < E; e += kSspThreads)
