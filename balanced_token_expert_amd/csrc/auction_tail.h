@@ -257,8 +257,10 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
     int32_t* il = ij + (E + kSspCand);                           //               item leaver
     int32_t* inext = il + (E + kSspCand);                        //               item next
     __shared__ int32_t cand[kSspCand], ce1[kSspCand], cf[kSspCand], clen[kSspCand],
-        order[kSspCand], alist[kSspCand], ring[kSspCand];
+        alist[kSspCand], ring[kSspCand];
     __shared__ double cL[kSspCand];
+    __shared__ unsigned long long cmk[kSspCand * NCH], cfl[kSspCand], csf[kSspCand];
+    __shared__ int32_t crk[kSspCand];
     __shared__ int32_t nring, nc_s, nacc_s, nux, nitem, stop, nrows, nsarc[2], fn[3];
     __shared__ double Lmax_s;
     __shared__ int64_t ghead;
@@ -548,21 +550,13 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
         __syncthreads();
 
         // ---- apply, in order of L_u, the paths whose full experts no
-        // earlier applied path uses and whose free expert has a slot left
+        // earlier applied path uses and whose free expert has a slot left.
+        // Wave 0 walks each candidate's path; then all waves compare every
+        // candidate with a share of the others (rank by L, path overlap,
+        // same free expert) into per-candidate bitmasks; then wave 0 takes
+        // the candidates in rank order, each a few reads of those masks.
         if (wave == 0) {
             const bool mine = lane < nc;
-            const double lq = mine ? cL[lane] : DBL_MAX;
-            int rank = 0;
-            for (int r = 0; r < nc; ++r) {
-                const double lr = readlane_f64(lq, r);
-                rank += (lr < lq || (lr == lq && r < lane)) ? 1 : 0;
-            }
-            if (mine) order[rank] = lane;
-            // the same order in registers: lane r receives the lane ranked r
-            // (a cross-lane push; lanes past nc push to themselves and are
-            // never read)
-            const int order_r = __builtin_amdgcn_ds_permute((mine ? rank : lane) * 4, lane);
-            // the experts of this lane's path, and its free expert
             unsigned long long msk[NCH];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) msk[c] = 0;
@@ -581,48 +575,78 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
             if (mine) {
                 cf[lane] = f;
                 clen[lane] = steps;
-            }
-            int capc[NCH];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int e = lane + 64 * c;
-                capc[c] = e < E ? (int)(k - cnt[e]) : 0;
+                for (int c = 0; c < NCH; ++c) cmk[lane * NCH + c] = msk[c];
+                crk[lane] = 0;
+                cfl[lane] = 0;
+                csf[lane] = 0;
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            unsigned long long used[NCH];
+        }
+        __syncthreads();
+        {
+            const bool mine = lane < nc;
+            const double li = mine ? cL[lane] : 0.0;
+            const int fi = mine ? cf[lane] : -1;
+            unsigned long long mi[NCH];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) used[c] = 0;
+            for (int c = 0; c < NCH; ++c) mi[c] = mine ? cmk[lane * NCH + c] : 0ull;
+            unsigned long long conf = 0, same = 0;
+            int before = 0;
+            for (int j = wave; j < nc; j += kSspWaves) {
+                const double lj = cL[j];
+                const int fj = cf[j];
+                bool cj = false;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) cj = cj || (cmk[j * NCH + c] & mi[c]) != 0;
+                before += (lj < li || (lj == li && j < lane)) ? 1 : 0;
+                if (cj) conf |= 1ull << j;
+                if (fj >= 0 && fj == fi) same |= 1ull << j;
+            }
+            if (mine) {
+                if (before) atomicAdd(&crk[lane], before);
+                if (conf) atomicOr(&cfl[lane], conf);
+                if (same) atomicOr(&csf[lane], same);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const bool mine = lane < nc;
+            const int rank = mine ? crk[lane] : lane;
+            // lane r receives the lane ranked r (a cross-lane push; lanes past
+            // nc push to themselves and are never read)
+            const int order_r = __builtin_amdgcn_ds_permute(rank * 4, lane);
+            const int fi = mine ? cf[lane] : -1;
+            const int capi = fi >= 0 ? (int)(k - cnt[fi]) : 0;
+            const unsigned long long conf = mine ? cfl[lane] : 0ull, same = mine ? csf[lane] : 0ull;
+            const double lq = mine ? cL[lane] : 0.0;
+            const unsigned long long lqb = __builtin_bit_cast(unsigned long long, lq);
+            // every candidate's fields pulled into the lane of its rank
+            const int capr = __builtin_amdgcn_ds_bpermute(order_r * 4, capi);
+            const unsigned cfl_lo = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)conf);
+            const unsigned cfl_hi = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)(conf >> 32));
+            const unsigned csf_lo = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)same);
+            const unsigned csf_hi = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)(same >> 32));
+            const unsigned lql = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)lqb);
+            const unsigned lqh = (unsigned)__builtin_amdgcn_ds_bpermute(order_r * 4, (int)(unsigned)(lqb >> 32));
+            const double lqr = __builtin_bit_cast(double, ((unsigned long long)lqh << 32) | lql);
             int nacc = 0;
             double Lmax = 0.0;
             unsigned long long accm = 0;  // the paths applied, by candidate
             for (int r = 0; r < nc; ++r) {
+                const int cap = readlane_i32(capr, r);
+                if (cap <= 0) continue;  // no free expert, or one with no slot
+                const unsigned long long cr = ((unsigned long long)(unsigned)readlane_i32((int)cfl_hi, r) << 32) |
+                                              (unsigned)readlane_i32((int)cfl_lo, r);
+                const unsigned long long sr = ((unsigned long long)(unsigned)readlane_i32((int)csf_hi, r) << 32) |
+                                              (unsigned)readlane_i32((int)csf_lo, r);
+                // a path overlapping an applied one, or a free expert whose
+                // slots the applied paths took
+                if ((cr & accm) != 0 || __popcll(sr & accm) >= cap) continue;
                 const int q = readlane_i32(order_r, r);
-                const int fq_ = readlane_i32(f, q);
-                if (fq_ < 0) continue;
-                int capq = 0;
-#pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    if (c == (fq_ >> 6)) capq = capc[c];
-                capq = readlane_i32(capq, fq_ & 63);
-                bool ok = capq > 0;
-                unsigned long long mq[NCH];
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    const unsigned lo = (unsigned)readlane_i32((int)(unsigned)msk[c], q);
-                    const unsigned hi = (unsigned)readlane_i32((int)(unsigned)(msk[c] >> 32), q);
-                    mq[c] = ((unsigned long long)hi << 32) | lo;
-                    ok = ok && (mq[c] & used[c]) == 0;
-                }
-                if (!ok) continue;
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    used[c] |= mq[c];
-                    if (c == (fq_ >> 6) && lane == (fq_ & 63)) --capc[c];
-                }
                 if (lane == 0) alist[nacc] = q;
                 accm |= 1ull << q;
                 ++nacc;
-                Lmax = fmax(Lmax, readlane_f64(lq, q));
+                Lmax = fmax(Lmax, readlane_f64(lqr, r));
             }
             if (lane == 0) {
                 nacc_s = nacc;
