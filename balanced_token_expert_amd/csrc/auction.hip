@@ -506,7 +506,8 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
     __shared__ int32_t ot[kBulkKMax];
     __shared__ int32_t rej[kResolveCap];  // a merge's rejected tokens, by rank - k
     __shared__ int32_t frj[kResolveCap];  // bidders rejected before any merge (below)
-    __shared__ int32_t ncand, nhold, rbase, nfrj, nsurv;
+    __shared__ int32_t ncand, nhold, rbase, nfrj, nsurv, ncut;
+    __shared__ double cut_s;
     static_assert(kResolveThreads <= kBinMax && kResolveThreads <= kOvfCap,
                   "one prefetched bin entry per thread");
     AucCtl* ctl = w.ctl;
@@ -690,12 +691,40 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
                 }
 #pragma unroll
                 for (int u = 0; u < UC; ++u) bk[u] = tk[u] >= 0 ? w.bval[tk[u]] : 0.0;
-                if (tid == 0) nsurv = 0;
+                if (tid == 0) { nsurv = 0; ncut = 0; }
                 __syncthreads();  // every thread has read ct before the survivors overwrite it
+                // A large chunk for an expert not yet full (a crowded expert
+                // in a phase's first round): a cut from a sample of its bids.
+                // When at least k of the chunk's bids are at or above it, a
+                // bid below it is ranked >= k by any merge, so it leaves at
+                // once and only the ~k others are sorted.
+                double cut = -DBL_MAX;
+                if (!full && cn >= 2 * k && cn > 512) {
+                    const int nsm = min(cn, kResolveThreads);
+                    if (tid < nsm) ob[tid] = bk[0];
+                    __syncthreads();
+                    const int want = min(nsm - 1, (int)((int64_t)nsm * k * 5 / (4 * (int64_t)cn)) + 4);
+                    if (tid < nsm) {
+                        int r = 0;  // samples ahead of this one (index breaks ties)
+                        for (int j = 0; j < nsm; ++j) {
+                            const double o = ob[j];
+                            r += (o > bk[0] || (o == bk[0] && j < tid)) ? 1 : 0;
+                        }
+                        if (r == want) cut_s = bk[0];
+                    }
+                    __syncthreads();
+                    const double cv = cut_s;
+                    int mc = 0;
+#pragma unroll
+                    for (int u = 0; u < UC; ++u) mc += (tk[u] >= 0 && bk[u] >= cv) ? 1 : 0;
+                    if (mc > 0) atomicAdd(&ncut, mc);
+                    __syncthreads();
+                    if (ncut >= k) cut = cv;
+                }
 #pragma unroll
                 for (int u = 0; u < UC; ++u) {
                     if (tk[u] < 0) continue;
-                    if (full && !better(bk[u], tk[u], thb, tht)) {
+                    if ((full && !better(bk[u], tk[u], thb, tht)) || bk[u] < cut) {
                         frj[atomicAdd(&nfrj, 1)] = tk[u];
                     } else {
                         const int q = atomicAdd(&nsurv, 1);
