@@ -152,6 +152,35 @@ def test_exact_rank1_closed_form_full_size():
     assert (res["assign"].cpu().numpy() == expect).all()
 
 
+def test_exact_rank1_crowded_first_round():
+    """The rank-1 closed form at T = 4096, E = 8 (k = 512): every token's
+    first bid goes to the expert of largest y, 4096 bidders for 512 slots,
+    so the resolve takes its chunked path and the sampled cut on a chunk of
+    2048 (at least 2k bids) decides which bids leave before the sort.
+    a_t in 128..255, b_t in 128..159 (every pair once), y_e = (128 + e)/128:
+    exact fp32 products, gap at least 2^-15, eps_end = 2^-31 below gap / T."""
+    T, E, D = 4096, 8, 8
+    k = T // E
+    rng = np.random.default_rng(12)
+    pairs = rng.permutation(T)
+    a_t = 128 + pairs // 32
+    b_t = 128 + pairs % 32
+    h = np.zeros((T, D), np.float32)
+    h[:, 0], h[:, 1] = a_t, b_t
+    ye = (128 + rng.permutation(E)) / 128.0
+    w = np.zeros((E, D), np.float32)
+    w[:, 0], w[:, 1] = ye, ye / 256.0
+    scores = api.base_affinity(_bf16(h), _bf16(w))
+    torch.cuda.synchronize()
+    x = a_t + b_t / 256.0
+    assert (scores.cpu().numpy().astype(np.float64) == np.outer(x, ye)).all()
+    expect = np.empty(T, np.int64)
+    expect[np.argsort(x)] = np.repeat(np.argsort(ye), k)
+    res, st = _solve(scores, 2.0 ** -31)
+    assert st.bids[0] >= T  # the first phase's first round: every token bids
+    assert (res["assign"].cpu().numpy() == expect).all()
+
+
 def test_exact_two_experts_closed_form_full_size():
     """E = 2: expert 0 takes the k tokens with the largest s[t,0] - s[t,1]
     (every balanced assignment scores sum_t s[t,1] + sum_{t in expert 0}
