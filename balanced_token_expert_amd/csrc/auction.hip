@@ -700,18 +700,17 @@ __global__ __launch_bounds__(kResolveThreads) void auc_bulk_resolve_kernel(int64
                 // once and only the ~k others are sorted.
                 double cut = -DBL_MAX;
                 if (!full && cn >= 2 * k && cn > 512) {
-                    const int nsm = min(cn, kResolveThreads);
-                    if (tid < nsm) ob[tid] = bk[0];
+                    // one sample per thread (cn > 512 >= kResolveThreads)
+                    constexpr int nsm = kResolveThreads;
+                    ob[tid] = bk[0];
                     __syncthreads();
                     const int want = min(nsm - 1, (int)((int64_t)nsm * k * 5 / (4 * (int64_t)cn)) + 4);
-                    if (tid < nsm) {
-                        int r = 0;  // samples ahead of this one (index breaks ties)
-                        for (int j = 0; j < nsm; ++j) {
-                            const double o = ob[j];
-                            r += (o > bk[0] || (o == bk[0] && j < tid)) ? 1 : 0;
-                        }
-                        if (r == want) cut_s = bk[0];
+                    int r = 0;  // samples ahead of this one (index breaks ties)
+                    for (int j = 0; j < nsm; ++j) {
+                        const double o = ob[j];
+                        r += (o > bk[0] || (o == bk[0] && j < tid)) ? 1 : 0;
                     }
+                    if (r == want) cut_s = bk[0];
                     __syncthreads();
                     const double cv = cut_s;
                     int mc = 0;
