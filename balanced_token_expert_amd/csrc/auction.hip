@@ -121,6 +121,11 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static bool late_ok(int64_t T, int64_t E, int64_t k);  // auction_late.h
 // the phase end's expert-major copy of its holders' scores (E <= 128, exactly when
 // its C matrix lives in LDS: ssp_c_in_lds in auction_tail.h)
+// Workgroups per expert in the phase-end setup: two when E <= 128 (128
+// experts would leave half of the 256 CUs idle), each over half of the
+// expert's holders, its C and Ct minima in a plane of its own that the
+// phase end merges when it copies C into LDS.
+__host__ __device__ static inline int64_t ssp_parts(int64_t E) { return E <= 128 ? 2 : 1; }
 static int64_t xt_floats(int64_t T, int64_t E) { return E <= 128 ? E * T : 0; }
 
 // the late-round launch's buffers, reserved only when a solve of this size
@@ -143,8 +148,8 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
     w.slot_of = (int32_t*)p; p += align256(T * 4);
     w.sown = (float*)p; p += align256(T * 4);
     w.xt = (float*)p; p += align256(xt_floats(T, E) * 4);
-    w.C = (double*)p; p += align256(E * E * 8);
-    w.Ct = (int32_t*)p; p += align256(E * E * 4);
+    w.C = (double*)p; p += align256(ssp_parts(E) * E * E * 8);
+    w.Ct = (int32_t*)p; p += align256(ssp_parts(E) * E * E * 4);
     w.stale = (unsigned long long*)p; p += align256(E * ((E + 63) / 64) * 8);
     w.bcnt = (int32_t*)p; p += align256(E * 4);
     w.bin_t = (int32_t*)p; p += align256(E * kOvfCap * 4);
@@ -159,9 +164,9 @@ static AucWs carve(void* ws, int64_t T, int64_t E) {
 
 size_t auction_ws_bytes(int64_t T, int64_t E) {
     return align256(sizeof(AucCtl)) + 2 * align256(E * 8) + align256(E * 4) +
-           6 * align256(T * 4) + 2 * align256(T * 8) + align256(E * E * 8) +
+           6 * align256(T * 4) + 2 * align256(T * 8) + align256(ssp_parts(E) * E * E * 8) +
            align256(xt_floats(T, E) * 4) +
-           align256(E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
+           align256(ssp_parts(E) * E * E * 4) + align256(E * ((E + 63) / 64) * 8) + align256(E * 4) +
            align256(E * kOvfCap * 4) + align256(E * kBinMax * 8) +
            align256(late_ws_g(T, E) * 2 * T * 4) + align256(late_ws_g(T, E) * E * kLateCapWs * 4) +
            align256(late_ws_g(T, E) * E * kLateCapWs * 8) + align256(late_ws_g(T, E) * E * 4) + 256;
@@ -855,7 +860,7 @@ static void launch_tail(const float* s, int64_t T, int64_t E, int64_t k, const A
                         AucStatsDev* st, hipStream_t stream) {
     auction_mark(4 * phase + 1, stream);
     const int sth = ssp_setup_threads(E);
-    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)E), dim3(sth),
+    hipLaunchKernelGGL(auc_ssp_setup_kernel<NCH>, dim3((unsigned)(E * ssp_parts(E))), dim3(sth),
                        (size_t)(sth / 64) * 12 * E + 4 * kSetupChunk +
                            (E <= 128 ? (size_t)(sth / 64) * 8 * E * 4 : 0), stream, s,
                        E, k, w, scan);

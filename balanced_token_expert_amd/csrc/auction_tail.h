@@ -142,17 +142,21 @@ __global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int
     const bool xtl = ssp_c_in_lds(E);  // the phase end keeps xt exactly when C is in LDS
     const AucCtl* ctl = w.ctl;
     if (ctl->abort || ctl->nbid[ctl->cur] == 0) return;
-    const int a = blockIdx.x;
+    const int parts = (int)ssp_parts(E);
+    const int a = blockIdx.x / parts, part = blockIdx.x % parts;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const Sani sn = read_sani(scan);
     const int n = w.cnt[a];
+    // this workgroup's share of a's holders: slots [p0, p1)
+    const int share = (n + parts - 1) / parts;
+    const int p0 = min(n, part * share), p1 = min(n, p0 + share);
     constexpr int U = NCH >= 16 ? 2 : 32 / NCH;
     double bv[NCH];
     int bt[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) { bv[c] = DBL_MAX; bt[c] = kNoTok; }
-    for (int c0 = 0; c0 < n; c0 += kSetupChunk) {
-        const int cn = min(kSetupChunk, n - c0);
+    for (int c0 = p0; c0 < p1; c0 += kSetupChunk) {
+        const int cn = min(kSetupChunk, p1 - c0);
         for (int i = threadIdx.x; i < cn; i += blockDim.x) {
             const int h = w.stok[(int64_t)a * k + c0 + i];
             hl[i] = h;
@@ -223,8 +227,8 @@ __global__ __launch_bounds__(1024) void auc_ssp_setup_kernel(const float* s, int
         double v = pv[e];
         int t = pt[e];
         for (int q = 1; q < nwv; ++q) argmin_merge(v, t, pv[q * E + e], pt[q * E + e]);
-        w.C[(int64_t)a * E + e] = v;
-        w.Ct[(int64_t)a * E + e] = t;
+        w.C[(int64_t)part * E * E + (int64_t)a * E + e] = v;
+        w.Ct[(int64_t)part * E * E + (int64_t)a * E + e] = t;
     }
 }
 
@@ -353,8 +357,18 @@ __global__ __launch_bounds__(kSspThreads) void auc_ssp_kernel(const float* s, in
         head[e] = -1;
     }
     if (nb > 0) {
-        if (CL)
-            for (int64_t i = tid; i < E * E; i += kSspThreads) Cl[(i / E) * cs + i % E] = Cg[i];
+        if (CL) {
+            // the setup's planes merged (one per workgroup of an expert)
+            const int parts = (int)ssp_parts(E);
+            for (int64_t i = tid; i < E * E; i += kSspThreads) {
+                double v = Cg[i];
+                int t = Ct[i];
+                for (int q = 1; q < parts; ++q) argmin_merge(v, t, Cg[q * E * E + i], Ct[q * E * E + i]);
+                Cl[(i / E) * cs + i % E] = v;
+                if (parts > 1) Ct[i] = t;
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the merged Ct in L2 before the barrier below
+        }
         for (int i = tid; i < (int)E * nw; i += kSspThreads) sput(i / nw, i % nw, 0ull);
     }
     const unsigned long long used0 = ctl->bids_total + ctl->bids_phase;
