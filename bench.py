@@ -62,7 +62,7 @@ MEASURED_TRAFFIC = {
     "ffn2": ("large_t64k_e128_d2048", GEMM_SOURCES,
              "8695e9d768e779a6446828c43f56586668b688f505037704cdcad5c56d212b0d", 2907136.1, 353352.6),
     "auction_tail": ("large_t64k_e128_d2048", AUCTION_SOURCES,
-                     "1bb42f64448caf5261a1e725ee59e40fc9eead3c8250485baa9cf115428b1056", 534.9, 823.0),
+                     "27a2f4c6a6b45d10224f920866823bc1267073d4c7b0e6d0b311ceb0199ba249", 638.0, 881.0),
 }
 
 
